@@ -1,0 +1,244 @@
+"""Oracle: paged decode attention, KV append and block copy, in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed, and where the pages fix it
+--------------------------------------------
+* KV lives in fixed-size blocks of 16 tokens held in one preallocated pool;
+  each sequence owns a block table that maps its logical block index to a
+  physical block, and blocks need not be neighbours
+  [cs2680 Lecture 10, §10.3 "PagedAttention: the KV cache as virtual memory";
+  the 16-token default is in the same section's block-size table and in
+  "The inference server" (srikanthmalla.com), PagedAttention answer].
+* A paged kernel reads, for every block, the table entry and then gathers
+  that block; the FLOPs and bytes are those of contiguous attention
+  [§10.3 "Step three"; llm-serving.xyz "KV-cache systems", paging paragraph
+  on block-table cost].
+* The attention is GQA: several query heads share one KV head, n_kv = 8 for
+  the shapes used here [llm-serving.xyz "KV-cache systems", bytes-per-token
+  equation].
+* The kernel takes a block-table pointer and a length per sequence
+  ["The inference server", fixed-shape kernel signature answer].
+
+Readings where the pages are silent (each also listed in the design notes):
+* The attention formula is standard scaled dot-product softmax attention of
+  one query token over the sequence's L cached tokens, scale given by the
+  caller; query head h reads KV head floor(h / G) with G = Hq / Hkv.
+* ``seq_lens[b]`` counts every cached token including the newest one; a
+  row with length 0 is a padded row whose output is exactly zero.
+* Pool layout (the library's interface; the pages leave it open):
+      k_pool[block, kv_head, slot, d]     token-major K tiles
+      v_pool[block, kv_head, d, slot]     dim-major V tiles
+  A token at position t of sequence b lives in block
+  ``block_tables[b, t // 16]`` at slot ``t % 16``.
+* Inputs are exact: bf16 values are widened to float64 without rounding.
+
+The arithmetic is done in float64 with a naive (two-pass) softmax over the
+whole row; nothing is blocked, fused or reordered.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen stored values to float64 exactly.
+
+    ``dtype`` names the storage format: "f32" arrays are float32; "bf16"
+    arrays hold the raw 16-bit patterns (uint16), which are the upper half of
+    the float32 with the same value, so widening is a 16-bit left shift.
+    """
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(a).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (round to nearest, ties to even).
+
+    Written from the format's definition: bfloat16 keeps the sign, the
+    8 exponent bits and the top 7 fraction bits of an IEEE binary32. The
+    value is first rounded to binary32 (numpy, RNE), then the low 16 bits
+    are rounded away with ties to even. NaN maps to a quiet NaN.
+    """
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    rounded = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(f)
+    rounded = np.where(nan, np.uint16(0x7FC0), rounded)
+    return rounded.astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Table walk and attention
+# --------------------------------------------------------------------------
+
+def gather_sequence(k_pool, v_pool, table_row, seq_len, dtype,
+                    block_size=BLOCK_SIZE):
+    """Materialise one sequence's contiguous K and V by walking its table.
+
+    Returns ``K, V`` of shape [Hkv, L, D] in float64, where token t comes
+    from physical block ``table_row[t // block_size]`` at slot
+    ``t % block_size`` [cs2680 Lecture 10, §10.3: logical block index ->
+    physical block]. Table entries at or beyond ceil(L / block_size) and
+    slots at or beyond L are never touched.
+    """
+    L = int(seq_len)
+    Hkv = k_pool.shape[1]
+    D = k_pool.shape[3]
+    if L == 0:
+        z = np.zeros((Hkv, 0, D))
+        return z, z.copy()
+    t = np.arange(L)
+    phys = np.asarray(table_row)[t // block_size].astype(np.int64)
+    slot = t % block_size
+    # k_pool[phys, :, slot, :] -> [L, Hkv, D]; v_pool[phys, :, :, slot] -> [L, Hkv, D]
+    k = k_pool[phys, :, slot, :]
+    v = v_pool[phys, :, :, slot]
+    K = as_f64(k, dtype).transpose(1, 0, 2)
+    V = as_f64(v, dtype).transpose(1, 0, 2)
+    return K, V
+
+
+def decode_contiguous(q_b, K, V, scale):
+    """Attention of one sequence's query heads over contiguous K/V.
+
+    q_b: [Hq, D] float64; K, V: [Hkv, L, D] float64. Query head h uses KV
+    head h // (Hq // Hkv). For each head: s = scale * K q, p = exp(s - max s),
+    out = (p V) / sum p. L == 0 gives zeros. This is the contiguous
+    (base + stride * t) attention that paging leaves unchanged
+    [cs2680 Lecture 10, §10.3 "Step three"].
+    """
+    Hq, D = q_b.shape
+    Hkv, L, _ = K.shape
+    G = Hq // Hkv
+    out = np.zeros((Hq, D))
+    if L == 0:
+        return out
+    for kv in range(Hkv):
+        qg = q_b[kv * G:(kv + 1) * G]              # [G, D]
+        s = scale * (qg @ K[kv].T)                 # [G, L]
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        out[kv * G:(kv + 1) * G] = (p @ V[kv]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def paged_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, dtype,
+                 rows=None, block_size=BLOCK_SIZE):
+    """Paged decode attention for a batch, in float64.
+
+    q [B, Hq, D], k_pool [NB, Hkv, 16, D], v_pool [NB, Hkv, D, 16] (storage
+    format ``dtype``), block_tables int [B, MB], seq_lens int [B]. For each
+    selected row b the sequence is gathered through its table and attended
+    contiguously; rows with length 0 are zero. ``rows`` selects a subset of
+    sequences (for sampled checks at full size); the result then has one
+    entry per selected row, in the given order.
+    """
+    B, Hq, D = q.shape
+    rows = range(B) if rows is None else list(rows)
+    out = np.zeros((len(rows), Hq, D))
+    for i, b in enumerate(rows):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        K, V = gather_sequence(k_pool, v_pool, block_tables[b], L, dtype,
+                               block_size)
+        out[i] = decode_contiguous(as_f64(q[b], dtype), K, V, scale)
+    return out
+
+
+def brute_force_decode(q, k_pool, v_pool, block_tables, seq_lens, scale,
+                       dtype, block_size=BLOCK_SIZE):
+    """Same quantity as ``paged_decode`` with scalar Python loops.
+
+    For tiny inputs only. Uses its own element-wise table walk and
+    ``math.exp``; shares nothing with ``paged_decode`` except the exact
+    widening of stored values.
+    """
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    qf = as_f64(q, dtype)
+    kf = as_f64(k_pool, dtype)
+    vf = as_f64(v_pool, dtype)
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(Hq):
+            kv = h // G
+            scores = []
+            for t in range(L):
+                blk = int(block_tables[b][t // block_size])
+                slot = t % block_size
+                acc = 0.0
+                for d in range(D):
+                    acc += float(qf[b, h, d]) * float(kf[blk, kv, slot, d])
+                scores.append(scale * acc)
+            if L == 0:
+                continue
+            mx = max(scores)
+            w = [math.exp(s - mx) for s in scores]
+            tot = sum(w)
+            for d in range(D):
+                num = 0.0
+                for t in range(L):
+                    blk = int(block_tables[b][t // block_size])
+                    num += w[t] * float(vf[blk, kv, d, t % block_size])
+                out[b][h][d] = num / tot
+    return np.array(out, dtype=np.float64).reshape(B, Hq, D)
+
+
+# --------------------------------------------------------------------------
+# Cache maintenance
+# --------------------------------------------------------------------------
+
+def write_kv(k_pool, v_pool, k_new, v_new, slot_mapping,
+             block_size=BLOCK_SIZE):
+    """Append new tokens' K/V into their slots; returns updated copies.
+
+    Token i goes to slot s = slot_mapping[i]: block s // 16, position
+    s % 16, for every KV head; a negative slot means "skip". A sequence grows
+    into the next position of its last block and takes a new block only when
+    the last one is full [cs2680 Lecture 10, §10.3 and its instructor notes
+    on growing a sequence by one token]. Pure data movement: the stored bits
+    are copied unchanged.
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    for i, s in enumerate(np.asarray(slot_mapping).tolist()):
+        if s < 0:
+            continue
+        blk, pos = divmod(int(s), block_size)
+        k_out[blk, :, pos, :] = k_new[i]
+        v_out[blk, :, :, pos] = v_new[i]
+    return k_out, v_out
+
+
+def copy_blocks(k_pool, v_pool, block_mapping):
+    """Copy-on-write block copy; returns updated copies.
+
+    For each (src, dst) pair the whole K block and the whole V block of dst
+    become bit-identical to src, for every KV head [cs2680 Lecture 10, §10.4
+    (a divergent write gets a new block); llm-serving.xyz "KV-cache systems",
+    copy-on-write paragraph].
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    for src, dst in np.asarray(block_mapping).reshape(-1, 2).tolist():
+        k_out[dst] = k_pool[src]
+        v_out[dst] = v_pool[src]
+    return k_out, v_out
