@@ -1,0 +1,145 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: paged decode attention for MI355X
+ * (gfx950), plus the two cache-maintenance calls it needs.
+ *
+ * What the calls compute
+ *   The KV cache is one preallocated pool of fixed-size blocks of 16 tokens;
+ *   every sequence has a block table mapping its logical block j to a
+ *   physical block, and a length; blocks need not be adjacent
+ *   [cs2680 Lecture 10, §10.3 "PagedAttention: the KV cache as virtual
+ *   memory"]. The attention call takes a block-table pointer and a length
+ *   per sequence, so its arguments keep a fixed shape while sequences grow
+ *   ["The inference server" (srikanthmalla.com), the answer on fixed-shape
+ *   kernel signatures and bucketed graph capture]. A paged kernel reads each
+ *   block's table entry and then gathers the block; the FLOPs and bytes are
+ *   those of contiguous attention [§10.3 "Step three"; llm-serving.xyz
+ *   "KV-cache systems", paragraph on the price of paging].
+ *
+ * Layouts (row-major, contiguous; all device memory unless noted)
+ *   q, out        [B, Hq, D]                        element type = dtype
+ *   k_pool        [NB, Hkv, 16, D]   token-major K tiles
+ *   v_pool        [NB, Hkv, D, 16]   dim-major (transposed) V tiles
+ *   block_tables  int32 [B, MB]      row b, entry j = physical block of
+ *                                    tokens 16j .. 16j+15 of sequence b
+ *   seq_lens      int32 [B]          tokens attended, newest included;
+ *                                    0 = padded row (output is exact zeros)
+ *   k_new, v_new  [T, Hkv, D]
+ *   slot_mapping  int32 [T]          slot = block * 16 + offset; < 0 = skip
+ *   block_mapping int32 [n, 2]       (src, dst) physical block pairs
+ *   Query head h reads KV head h / (Hq / Hkv).
+ *
+ * Ownership and execution
+ *   The caller allocates and owns every buffer, including the workspace.
+ *   The library allocates nothing, keeps no pointer after a call returns
+ *   and holds no state: calls are re-entrant. Each call only enqueues work
+ *   on `stream` (a hipStream_t; NULL = the default stream) and returns
+ *   without synchronising. Launch grids depend only on the pa_dims values,
+ *   never on device-resident lengths or table entries.
+ *
+ * Errors
+ *   Arguments the host can see (pointers, dims, sizes) are checked before
+ *   anything is launched; a bad one returns PA_ERR_INVALID_ARG or
+ *   PA_ERR_UNSUPPORTED and nothing runs. A launch failure reported by the
+ *   HIP runtime returns PA_ERR_LAUNCH. Device-resident values are NOT
+ *   checked (that would need a synchronisation); the caller guarantees:
+ *     0 <= seq_lens[b] <= MB * 16;
+ *     0 <= block_tables[b][j] < NB for every j < ceil(seq_lens[b] / 16);
+ *     write slots are distinct and < NB * 16;
+ *     copy pairs name blocks < NB, destinations are distinct and no
+ *     destination is also a source in the same call.
+ *   Violations give undefined results (out-of-range reads or racing
+ *   writes); the Python binding offers an opt-in host validator.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* null pointer, bad dims, workspace too small */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype, head dim, G) */
+  PA_ERR_LAUNCH = 3        /* the HIP runtime rejected a kernel launch */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Decode kernel selection. AUTO picks the matrix-core kernel for bf16 and
+ * the vector-ALU kernel for f32. */
+typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_kernel;
+
+/* Host-side dimensions; all fields are fixed for a given captured shape. */
+typedef struct {
+  int32_t num_seqs;           /* B   (>= 1) */
+  int32_t num_q_heads;        /* Hq  (multiple of Hkv, Hq / Hkv <= 16) */
+  int32_t num_kv_heads;       /* Hkv (>= 1) */
+  int32_t head_dim;           /* D   (64 or 128) */
+  int32_t block_size;         /* must be 16 */
+  int32_t max_blocks_per_seq; /* MB: row stride of block_tables (>= 1) */
+  int32_t num_blocks;         /* NB: pool capacity in blocks (>= 1) */
+  int32_t partition_tokens;   /* split-K partition length: a multiple of 16,
+                                 or 0 for one partition per sequence */
+  int32_t dtype;              /* pa_dtype of q, pools, k_new/v_new and out */
+  int32_t kernel;             /* pa_kernel */
+} pa_dims;
+
+/* Bytes of device workspace pa_decode needs for these dims: 0 when every
+ * sequence fits one partition (MB * 16 <= partition_tokens, or
+ * partition_tokens == 0), else room for fp32 partial results
+ * (max, sum, unnormalised output) of every (sequence, query head,
+ * partition). Returns 0 for invalid dims as well; pa_decode reports those. */
+size_t pa_decode_workspace_bytes(const pa_dims* dims);
+
+/* Paged decode attention: for every sequence b and query head h,
+ *   out[b,h,:] = sum_t softmax_t(scale * <q[b,h,:], K_b[t]>) V_b[t]
+ * over t < seq_lens[b], with K_b/V_b gathered through block_tables[b]
+ * (naive softmax over the whole row; computed with an online softmax per
+ * partition and a log-sum-exp merge across partitions, fp32 accumulation).
+ * Rows with seq_lens[b] == 0 get zeros. Slots at or past seq_lens[b] and
+ * table entries at or past ceil(seq_lens[b] / 16) are never read, so they
+ * may hold anything (NaN included). bf16 output is rounded to nearest even.
+ * `workspace` may be NULL when pa_decode_workspace_bytes() is 0. */
+pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    float scale, void* out, const pa_dims* dims,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* KV append: for t < num_tokens with s = slot_mapping[t] >= 0,
+ *   k_pool[s / 16, h, s % 16, :] = k_new[t, h, :]
+ *   v_pool[s / 16, h, :, s % 16] = v_new[t, h, :]   for every KV head h.
+ * A bit copy: no value is converted. Growth takes a new block only when a
+ * sequence's last block is full [cs2680 Lecture 10, §10.3 and its notes on
+ * growing a sequence by one token]. Uses num_kv_heads, head_dim,
+ * block_size, num_blocks and dtype from `dims`. num_tokens == 0 is a no-op
+ * (pointers may then be NULL). */
+pa_status pa_write_kv(const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, int32_t num_tokens,
+                      void* k_pool, void* v_pool, const pa_dims* dims,
+                      void* stream);
+
+/* Copy-on-write block copy: for each pair (src, dst) in block_mapping,
+ * the whole K block and the whole V block of dst (every KV head) become
+ * bit-identical to those of src [cs2680 Lecture 10, §10.4; llm-serving.xyz
+ * "KV-cache systems", copy-on-write paragraph]. Uses num_kv_heads,
+ * head_dim, block_size, num_blocks and dtype from `dims`.
+ * num_pairs == 0 is a no-op. */
+pa_status pa_copy_blocks(void* k_pool, void* v_pool,
+                         const int32_t* block_mapping, int32_t num_pairs,
+                         const pa_dims* dims, void* stream);
+
+/* Static description of a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Library version string, e.g. "pagedkv 0.1 gfx950". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,219 @@
+"""Python binding of libpagedkv (paged decode attention for MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI in include/pagedkv.h; the functions
+carry the C names. Tensors are PyTorch device tensors (PyTorch supplies
+device memory and the stream); every step of the computation runs in the
+HIP kernels of libpagedkv.so. The library is loaded on first use and a
+missing build is an error: there is no fallback path.
+
+    pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, ...)
+    pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool)
+    pa_copy_blocks(k_pool, v_pool, block_mapping)
+    pa_decode_workspace_bytes(dims)
+
+Layouts: q/out [B, Hq, D]; k_pool [NB, Hkv, 16, D]; v_pool [NB, Hkv, D, 16];
+block_tables int32 [B, MB]; seq_lens int32 [B]; k_new/v_new [T, Hkv, D];
+slot_mapping int32 [T]; block_mapping int32 [n, 2].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+__all__ = [
+    "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_LAUNCH",
+    "PaDims", "PagedKVError", "SYMBOLS", "load_library", "make_dims",
+    "pa_decode", "pa_decode_workspace_bytes", "pa_write_kv", "pa_copy_blocks",
+    "pa_status_string", "pa_version", "validate",
+]
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
+PA_F32, PA_BF16 = 0, 1
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+BLOCK_SIZE = 16
+
+SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_write_kv",
+           "pa_copy_blocks", "pa_status_string", "pa_version")
+
+
+class PaDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+        "max_blocks_per_seq", "num_blocks", "partition_tokens", "dtype",
+        "kernel")]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, call, status):
+        super().__init__(f"{call}: {pa_status_string(status)} (status {status})")
+        self.status = status
+
+
+_LIB = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpagedkv.so once; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_cache_55_amd.build` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(PaDims)
+    lib.pa_decode_workspace_bytes.argtypes = [D]
+    lib.pa_decode_workspace_bytes.restype = SZ
+    lib.pa_decode.argtypes = [P, P, P, P, P, F32, P, D, P, SZ, P]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_write_kv.argtypes = [P, P, P, I32, P, P, D, P]
+    lib.pa_write_kv.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def pa_version() -> str:
+    return load_library().pa_version().decode()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def make_dims(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+              num_blocks, dtype, partition_tokens=512, kernel="auto") -> PaDims:
+    return PaDims(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                  BLOCK_SIZE, int(max_blocks_per_seq), int(num_blocks),
+                  int(partition_tokens), int(dtype), KERNELS[kernel])
+
+
+def _pool_dims(k_pool, v_pool):
+    _need(k_pool.dim() == 4 and v_pool.dim() == 4, "pools must be 4-D")
+    NB, Hkv, BS, D = k_pool.shape
+    _need(BS == BLOCK_SIZE, f"k_pool block dim must be {BLOCK_SIZE}")
+    _need(tuple(v_pool.shape) == (NB, Hkv, D, BS), "v_pool must be [NB, Hkv, D, 16]")
+    _need(k_pool.dtype == v_pool.dtype, "k_pool and v_pool dtypes differ")
+    _need(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
+    _need(k_pool.is_cuda and v_pool.is_cuda, "pools must be device tensors")
+    return NB, Hkv, D
+
+
+def pa_decode_workspace_bytes(dims: PaDims) -> int:
+    return int(load_library().pa_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
+              partition_tokens=512, kernel="auto", workspace=None, stream=None):
+    """out[b, h] = softmax(scale * q[b, h] K_b^T) V_b over the paged K/V."""
+    torch = _torch()
+    NB, Hkv, D = _pool_dims(k_pool, v_pool)
+    _need(q.dim() == 3 and q.shape[2] == D, "q must be [B, Hq, D]")
+    B, Hq, _ = q.shape
+    _need(q.dtype == k_pool.dtype, "q and pools must share a dtype")
+    _need(q.is_contiguous() and q.is_cuda, "q must be a contiguous device tensor")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == B and block_tables.is_contiguous()
+          and block_tables.is_cuda, "block_tables must be int32 [B, MB] on the device")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,)
+          and seq_lens.is_contiguous() and seq_lens.is_cuda,
+          "seq_lens must be int32 [B] on the device")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
+          and out.is_cuda, "out must match q")
+    dims = make_dims(B, Hq, Hkv, D, block_tables.shape[1], NB, _dtype_code(q),
+                     partition_tokens, kernel)
+    lib = load_library()
+    need = int(lib.pa_decode_workspace_bytes(ctypes.byref(dims)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                       _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                       ctypes.byref(dims), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+                       _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_decode", st)
+    return out
+
+
+def pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, *, stream=None):
+    """k_pool/v_pool[slot] = k_new/v_new[t] for every t with slot >= 0."""
+    torch = _torch()
+    NB, Hkv, D = _pool_dims(k_pool, v_pool)
+    T = slot_mapping.shape[0]
+    _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1
+          and slot_mapping.is_contiguous() and slot_mapping.is_cuda,
+          "slot_mapping must be int32 [T] on the device")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(tuple(t.shape) == (T, Hkv, D) and t.dtype == k_pool.dtype
+              and t.is_contiguous() and t.is_cuda, f"{n} must be [T, Hkv, D] like the pools")
+    dims = make_dims(1, Hkv, Hkv, D, 1, NB, _dtype_code(k_pool))
+    st = load_library().pa_write_kv(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T,
+                                    _ptr(k_pool), _ptr(v_pool), ctypes.byref(dims),
+                                    _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_write_kv", st)
+
+
+def pa_copy_blocks(k_pool, v_pool, block_mapping, *, stream=None):
+    """Whole-block copy dst <- src for every (src, dst) row of block_mapping."""
+    torch = _torch()
+    NB, Hkv, D = _pool_dims(k_pool, v_pool)
+    _need(block_mapping.dtype == torch.int32 and block_mapping.dim() == 2
+          and block_mapping.shape[1] == 2 and block_mapping.is_contiguous()
+          and block_mapping.is_cuda, "block_mapping must be int32 [n, 2] on the device")
+    dims = make_dims(1, Hkv, Hkv, D, 1, NB, _dtype_code(k_pool))
+    st = load_library().pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(block_mapping),
+                                       block_mapping.shape[0], ctypes.byref(dims),
+                                       _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_copy_blocks", st)
+
+
+from .validate import validate  # noqa: E402

@@ -1,0 +1,171 @@
+// C ABI of libpagedkv (declared in include/pagedkv.h): argument checks,
+// kernel selection and launches. No allocation, no state, no host sync.
+#include <math.h>
+
+#include "launch.h"
+#include "pagedkv.h"
+
+using namespace pagedkv;
+
+namespace {
+
+constexpr int kMaxGroup = 16;
+constexpr int kMaxGridYZ = 65535;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Checks shared by every call: pool geometry and dtype.
+pa_status check_pool(const pa_dims* d) {
+  if (!d) return PA_ERR_INVALID_ARG;
+  if (d->block_size != kBlockTokens) return PA_ERR_INVALID_ARG;
+  if (d->num_kv_heads < 1 || d->head_dim < 1 || d->num_blocks < 1) return PA_ERR_INVALID_ARG;
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (d->num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int elem_bytes(const pa_dims* d) { return d->dtype == PA_F32 ? 4 : 2; }
+
+struct Plan {
+  int part_tokens;  // tokens per partition (multiple of 16)
+  int num_parts;    // partitions per sequence at most
+  size_t ws_bytes;  // 0 when num_parts == 1
+  size_t off_l, off_o;
+};
+
+pa_status plan_decode(const pa_dims* d, Plan* p) {
+  pa_status st = check_pool(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs < 1 || d->num_q_heads < 1 || d->max_blocks_per_seq < 1)
+    return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads / d->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs > kMaxGridYZ || d->num_q_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if (d->max_blocks_per_seq > (1 << 26)) return PA_ERR_UNSUPPORTED;
+  if (d->partition_tokens < 0 || d->partition_tokens % kBlockTokens != 0)
+    return PA_ERR_INVALID_ARG;
+  if (d->kernel != PA_KERNEL_AUTO && d->kernel != PA_KERNEL_VALU && d->kernel != PA_KERNEL_MFMA)
+    return PA_ERR_INVALID_ARG;
+  if (d->kernel == PA_KERNEL_MFMA && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  const int max_tokens = d->max_blocks_per_seq * kBlockTokens;
+  const int part = (d->partition_tokens == 0 || d->partition_tokens >= max_tokens)
+                       ? max_tokens
+                       : d->partition_tokens;
+  p->part_tokens = part;
+  p->num_parts = (max_tokens + part - 1) / part;
+  if (p->num_parts == 1) {
+    p->ws_bytes = p->off_l = p->off_o = 0;
+    return PA_OK;
+  }
+  const size_t rows = (size_t)d->num_seqs * d->num_q_heads * p->num_parts;
+  p->off_l = align_up(rows * sizeof(float));
+  p->off_o = 2 * p->off_l;
+  p->ws_bytes = p->off_o + rows * (size_t)d->head_dim * sizeof(float);
+  return PA_OK;
+}
+
+int pick_kernel(const pa_dims* d) {
+  if (d->kernel != PA_KERNEL_AUTO) return d->kernel;
+  return d->dtype == PA_BF16 ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_workspace_bytes(const pa_dims* dims) {
+  Plan p;
+  if (plan_decode(dims, &p) != PA_OK) return 0;
+  return p.ws_bytes;
+}
+
+pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                    void* out, const pa_dims* dims, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  Plan plan;
+  pa_status st = plan_decode(dims, &plan);
+  if (st != PA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return PA_ERR_INVALID_ARG;
+
+  DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  char* ws = (char*)workspace;
+  a.ws_m = plan.ws_bytes ? (float*)ws : nullptr;
+  a.ws_l = plan.ws_bytes ? (float*)(ws + plan.off_l) : nullptr;
+  a.ws_o = plan.ws_bytes ? (float*)(ws + plan.off_o) : nullptr;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = dims->num_seqs;
+  a.num_q_heads = dims->num_q_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.group = dims->num_q_heads / dims->num_kv_heads;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.part_tokens = plan.part_tokens;
+  a.num_parts = plan.num_parts;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  const int kernel = pick_kernel(dims);
+  if (kernel == PA_KERNEL_MFMA)
+    e = launch_decode_mfma(a, dims->head_dim, s);
+  else
+    e = launch_decode_valu(a, dims->dtype, dims->head_dim, s);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (plan.num_parts > 1) {
+    e = launch_decode_reduce(a, dims->dtype, dims->head_dim, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+pa_status pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                      int32_t num_tokens, void* k_pool, void* v_pool, const pa_dims* dims,
+                      void* stream) {
+  pa_status st = check_pool(dims);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool) return PA_ERR_INVALID_ARG;
+  hipError_t e = launch_write_kv(k_new, v_new, slot_mapping, num_tokens, k_pool, v_pool,
+                                 dims->num_kv_heads, dims->head_dim, elem_bytes(dims),
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping,
+                         int32_t num_pairs, const pa_dims* dims, void* stream) {
+  pa_status st = check_pool(dims);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_mapping) return PA_ERR_INVALID_ARG;
+  const size_t block_bytes =
+      (size_t)dims->num_kv_heads * kBlockTokens * dims->head_dim * elem_bytes(dims);
+  hipError_t e = launch_copy_blocks(k_pool, v_pool, block_mapping, num_pairs, block_bytes,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* pa_version(void) { return "pagedkv 0.1 gfx950"; }
+
+}  // extern "C"

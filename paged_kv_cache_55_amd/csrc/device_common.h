@@ -1,0 +1,94 @@
+// Device helpers shared by the gfx950 kernels of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pagedkv {
+
+constexpr int kBlockTokens = 16;  // tokens per KV block (fixed)
+
+// bf16 is carried as its raw 16-bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+// ---- element conversion ---------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct ElemTraits;
+
+template <> struct ElemTraits<float> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerVec = 4;  // elements per 16-byte vector
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+  __device__ static __forceinline__ void store1(float* p, float v) { *p = v; }
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
+    f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+  }
+  // zero the elements whose index (0..3) is >= nvalid
+  __device__ static __forceinline__ float zero() { return 0.f; }
+};
+
+template <> struct ElemTraits<bf16_t> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  __device__ static __forceinline__ float load1(const bf16_t* p) {
+    return __uint_as_float((uint32_t)p->bits << 16);
+  }
+  __device__ static __forceinline__ void store1(bf16_t* p, float v) { p->bits = f32_to_bf16_bits(v); }
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
+    f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+    f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+    f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
+    f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+  }
+};
+
+// ---- math ----------------------------------------------------------------
+
+// 2^x on the hardware exponential unit; 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- wave-level exchange -------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Orders this wave's LDS writes before its later LDS reads (and vice versa)
+// without a workgroup barrier: waves of one workgroup run loops of
+// different trip counts, so only the issuing wave may be synchronised.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- decode arguments ------------------------------------------------------
+
+// Everything a decode kernel needs; passed by value.
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* out;
+  float* ws_m;   // [B, Hq, NPmax] running max (log2 domain, scaled scores)
+  float* ws_l;   // [B, Hq, NPmax] sum of 2^(s - m)
+  float* ws_o;   // [B, Hq, NPmax, D] unnormalised output
+  float scale_log2;  // scale * log2(e)
+  int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, part_tokens, num_parts;
+};
+
+}  // namespace pagedkv

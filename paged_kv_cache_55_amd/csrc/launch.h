@@ -1,0 +1,22 @@
+// Host-side launchers of the libpagedkv kernels (internal; the public
+// interface is include/pagedkv.h). Each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+namespace pagedkv {
+
+// dtype: 0 = f32, 1 = bf16 (pa_dtype).
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
+
+hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,
+                           int num_tokens, void* k_pool, void* v_pool, int num_kv_heads,
+                           int head_dim, int elem_bytes, hipStream_t s);
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
+                              size_t block_bytes, hipStream_t s);
+
+}  // namespace pagedkv

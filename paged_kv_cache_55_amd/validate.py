@@ -1,0 +1,59 @@
+"""Opt-in host check of the device-value contracts of the C ABI.
+
+The library does not read device-resident lengths or table entries on the
+host (that would need a synchronisation). This validator checks, on host
+copies, the conditions the kernels rely on:
+  * 0 <= seq_lens[b] <= MB * 16;
+  * every table entry a sequence uses is a block id in [0, NB);
+  * write slots are distinct, and non-negative ones are < NB * 16;
+  * copy pairs name blocks in [0, NB), destinations are distinct, and no
+    destination is also a source in the same call.
+It raises ValueError on the first violation.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+
+def _host(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        return x.detach().cpu().numpy()
+    return np.asarray(x)
+
+
+def validate(num_blocks, block_tables=None, seq_lens=None, slot_mapping=None,
+             block_mapping=None) -> None:
+    nb = int(num_blocks)
+    if block_tables is not None or seq_lens is not None:
+        bt = _host(block_tables)
+        lens = _host(seq_lens).astype(np.int64)
+        if bt.ndim != 2 or lens.shape != (bt.shape[0],):
+            raise ValueError("block_tables must be [B, MB] and seq_lens [B]")
+        mb = bt.shape[1]
+        if (lens < 0).any() or (lens > mb * BLOCK_SIZE).any():
+            raise ValueError("seq_lens out of [0, MB * 16]")
+        for b, L in enumerate(lens.tolist()):
+            used = bt[b, :-(-L // BLOCK_SIZE)] if L else bt[b, :0]
+            if used.size and ((used < 0).any() or (used >= nb).any()):
+                raise ValueError(f"sequence {b}: table entry out of [0, {nb})")
+    if slot_mapping is not None:
+        s = _host(slot_mapping).astype(np.int64)
+        live = s[s >= 0]
+        if (live >= nb * BLOCK_SIZE).any():
+            raise ValueError("slot out of range")
+        if len(np.unique(live)) != len(live):
+            raise ValueError("duplicate write slots race")
+    if block_mapping is not None:
+        m = _host(block_mapping).astype(np.int64).reshape(-1, 2)
+        if m.size and ((m < 0).any() or (m >= nb).any()):
+            raise ValueError("copy pair names a block out of range")
+        src, dst = m[:, 0], m[:, 1]
+        if len(np.unique(dst)) != len(dst):
+            raise ValueError("duplicate copy destinations race")
+        if np.intersect1d(src, dst).size:
+            raise ValueError("a copy destination is also a source")

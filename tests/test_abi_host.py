@@ -1,0 +1,166 @@
+"""The C ABI library without a GPU: it loads, exports what the header
+declares, and rejects bad host-visible arguments before launching anything.
+
+Every call here returns before the library touches the HIP runtime, so
+these run on a machine without a GPU.
+"""
+
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_55_amd as pk
+from paged_kv_cache_55_amd import build as pkbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkbuild.LIB_PATH):
+        pkbuild.build()
+    return pk.load_library()
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(pa_[a-z_0-9]+)\s*\(",
+                            text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(pk.SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert pk.pa_status_string(pk.PA_OK) == "ok"
+    assert "invalid" in pk.pa_status_string(pk.PA_ERR_INVALID_ARG)
+    assert "unsupported" in pk.pa_status_string(pk.PA_ERR_UNSUPPORTED)
+    assert "launch" in pk.pa_status_string(pk.PA_ERR_LAUNCH)
+    assert "gfx950" in pk.pa_version()
+
+
+def dims(**kw):
+    base = dict(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                max_blocks_per_seq=256, num_blocks=9000, dtype=pk.PA_BF16,
+                partition_tokens=512, kernel="auto")
+    base.update(kw)
+    return pk.make_dims(**base)
+
+
+def test_workspace_size(lib):
+    d = dims()
+    nparts = 4096 // 512
+    rows = 64 * 32 * nparts
+    align = lambda x: (x + 255) // 256 * 256
+    assert pk.pa_decode_workspace_bytes(d) == 2 * align(rows * 4) + rows * 128 * 4
+    assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0)) == 0
+    assert pk.pa_decode_workspace_bytes(dims(partition_tokens=4096)) == 0
+    assert pk.pa_decode_workspace_bytes(dims(max_blocks_per_seq=32)) == 0
+    assert pk.pa_decode_workspace_bytes(dims(head_dim=96)) == 0  # invalid -> 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails first
+
+
+def decode_status(lib, d, q=FAKE, ws=None, wsb=0, scale=0.1):
+    return lib.pa_decode(q, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE,
+                         ctypes.byref(d), ws, ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), pk.PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=33), pk.PA_ERR_INVALID_ARG),
+    (dict(num_q_heads=8 * 17), pk.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=0), pk.PA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), pk.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), pk.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), pk.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=100), pk.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=-16), pk.PA_ERR_INVALID_ARG),
+    (dict(dtype=7), pk.PA_ERR_INVALID_ARG),
+    (dict(dtype=pk.PA_F32, kernel="mfma"), pk.PA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_dims(lib, kw, status):
+    assert decode_status(lib, dims(**kw)) == status
+
+
+def test_decode_rejects_bad_block_size(lib):
+    d = dims()
+    d.block_size = 32
+    assert decode_status(lib, d) == pk.PA_ERR_INVALID_ARG
+
+
+def test_decode_rejects_bad_kernel_code(lib):
+    d = dims()
+    d.kernel = 9
+    assert decode_status(lib, d) == pk.PA_ERR_INVALID_ARG
+
+
+def test_decode_rejects_null_and_small_workspace(lib):
+    d = dims()
+    assert decode_status(lib, d, q=None) == pk.PA_ERR_INVALID_ARG
+    assert decode_status(lib, d, ws=None) == pk.PA_ERR_INVALID_ARG
+    need = pk.pa_decode_workspace_bytes(d)
+    assert decode_status(lib, d, ws=FAKE, wsb=need - 1) == pk.PA_ERR_INVALID_ARG
+    assert decode_status(lib, d, scale=float("nan")) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
+                         None, None, 0, None) == pk.PA_ERR_INVALID_ARG
+
+
+def test_write_and_copy_reject_bad_args(lib):
+    d = dims()
+    assert lib.pa_write_kv(FAKE, FAKE, FAKE, -1, FAKE, FAKE, ctypes.byref(d), None) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(None, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(d), None) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(None, None, None, 0, None, None, ctypes.byref(d), None) == pk.PA_OK
+    assert lib.pa_copy_blocks(FAKE, FAKE, None, 2, ctypes.byref(d), None) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_copy_blocks(FAKE, FAKE, FAKE, -3, ctypes.byref(d), None) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_copy_blocks(None, None, None, 0, ctypes.byref(d), None) == pk.PA_OK
+    bad = dims(head_dim=80)
+    assert lib.pa_copy_blocks(FAKE, FAKE, FAKE, 1, ctypes.byref(bad), None) == pk.PA_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------
+# host validator
+# --------------------------------------------------------------------------
+
+def test_validator_accepts_good_inputs():
+    import workloads as wl
+    c = wl.config2()
+    pk.validate(c.num_blocks, c.block_tables, c.seq_lens, c.slot_mapping)
+    c3 = wl.config3()
+    pk.validate(c3.num_blocks, c3.block_tables, c3.seq_lens, c3.slot_mapping, c3.block_mapping)
+
+
+@pytest.mark.parametrize("case", ["len", "entry", "dup_slot", "slot_range", "dst_src", "dup_dst"])
+def test_validator_rejects(case):
+    bt = np.array([[0, 1, 2]], dtype=np.int32)
+    lens = np.array([40], dtype=np.int32)
+    kw = dict(num_blocks=4, block_tables=bt, seq_lens=lens)
+    if case == "len":
+        kw["seq_lens"] = np.array([49], dtype=np.int32)
+    elif case == "entry":
+        kw["block_tables"] = np.array([[0, 1, 9]], dtype=np.int32)
+    elif case == "dup_slot":
+        kw["slot_mapping"] = np.array([5, -1, 5], dtype=np.int32)
+    elif case == "slot_range":
+        kw["slot_mapping"] = np.array([64], dtype=np.int32)
+    elif case == "dst_src":
+        kw["block_mapping"] = np.array([[0, 1], [1, 2]], dtype=np.int32)
+    elif case == "dup_dst":
+        kw["block_mapping"] = np.array([[0, 3], [1, 3]], dtype=np.int32)
+    with pytest.raises(ValueError):
+        pk.validate(**kw)

@@ -1,0 +1,238 @@
+"""pa_decode on the GPU against the float64 oracle on the same seeded inputs.
+
+Covers the five configurations (configuration 4 and the 32-layer step at
+full size on sampled rows), small random cases that span several tiles and
+partitions with ragged tails, every supported head group and head dim, both
+decode kernels, padded rows, poisoned memory, run-to-run determinism,
+placement invariance and sharing exactness (bitwise).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_55_amd as pk
+import workloads as wl
+from workloads import to_numpy
+from parity import compare, gpu_out_f64, oracle_inputs, oracle_step, run_step, bits_equal
+
+pytestmark = pytest.mark.gpu
+
+BF16_KERNELS = ["mfma", "valu"]
+
+
+def _kernels(dtype):
+    return BF16_KERNELS if dtype == "bf16" else ["valu"]
+
+
+# --------------------------------------------------------------------------
+# configuration 1: tiny fp32
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("partition", [0, 16, 32, 512])
+def test_config1_fp32(partition):
+    c = wl.config1()
+    ref, _, _ = oracle_step(c)
+    out, _, _ = run_step(c, partition_tokens=partition)
+    compare(gpu_out_f64(out), ref, c.seq_lens.numpy(), "f32")
+
+
+def test_config1_single_token_row_is_its_value():
+    c = wl.config1()
+    out, _, _ = run_step(c)
+    blk = int(c.block_tables[0, 0])
+    o = out.cpu()
+    for h in range(4):
+        np.testing.assert_allclose(o[0, h].numpy(), c.v_pool[blk, h // 2, :, 0].numpy(),
+                                   rtol=0, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# small random cases: tiles, partitions, ragged tails
+# --------------------------------------------------------------------------
+
+CASES = []
+for dtype in ("f32", "bf16"):
+    for D in (64, 128):
+        for G in (1, 2, 4, 8, 16):
+            CASES.append((dtype, D, G))
+
+
+@pytest.mark.parametrize("dtype,D,G", CASES)
+def test_random_small(dtype, D, G):
+    Hkv = 2
+    lens = [0, 1, 15, 16, 17, 33, 100, 255, 257, 600]
+    c = wl.random_case(100 + D + G, len(lens), G * Hkv, Hkv, D, dtype, lens=lens,
+                       extra_table_cols=3)
+    ref, _, _ = oracle_step(c)
+    for kernel in _kernels(dtype):
+        for part in (0, 16, 48, 256):
+            out, _, _ = run_step(c, kernel=kernel, partition_tokens=part)
+            compare(gpu_out_f64(out), ref, lens, dtype)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_lengths_bf16(seed):
+    c = wl.random_case(200 + seed, 9, 32, 8, 128, "bf16", max_len=1100, with_write=True)
+    ref, _, _ = oracle_step(c)
+    for kernel in BF16_KERNELS:
+        out, _, _ = run_step(c, kernel=kernel, partition_tokens=512)
+        compare(gpu_out_f64(out), ref, c.seq_lens.numpy(), "bf16")
+
+
+# --------------------------------------------------------------------------
+# configuration 2: 8B-shaped layer, write then decode, full batch
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def config2_ref():
+    c = wl.config2()
+    ref, k, v = oracle_step(c)
+    return c, ref, k, v
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+@pytest.mark.parametrize("partition", [512, 256, 0])
+def test_config2_full(config2_ref, kernel, partition):
+    c, ref, k_ref, v_ref = config2_ref
+    out, k, v = run_step(c, kernel=kernel, partition_tokens=partition)
+    assert bits_equal(k, k_ref) and bits_equal(v, v_ref)
+    worst = compare(gpu_out_f64(out), ref, c.seq_lens.numpy(), "bf16")
+    print(f"config2 {kernel} part={partition} worst ratio {worst:.3f}")
+
+
+# --------------------------------------------------------------------------
+# configuration 3: copy-on-write over a shared prefix
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_config3_cow(kernel):
+    c = wl.config3()
+    ref, k_ref, v_ref = oracle_step(c)
+    out, k, v = run_step(c, kernel=kernel)
+    assert bits_equal(k, k_ref) and bits_equal(v, v_ref)
+    compare(gpu_out_f64(out), ref, c.seq_lens.numpy(), "bf16")
+    # sequence 0 and its fork differ only in the last token
+    assert not torch.equal(out[0], out[7])
+
+
+def test_config3_sharing_is_exact():
+    """Shared prefix blocks and private copies of them give identical bits."""
+    c = wl.config3()
+    out_shared, k, v = run_step(c)
+    nb = c.num_blocks
+    tables = c.block_tables.clone()
+    extra_k = torch.empty((128 * 2, *c.k_pool.shape[1:]), dtype=c.k_pool.dtype, device="cuda")
+    extra_v = torch.empty((128 * 2, *c.v_pool.shape[1:]), dtype=c.v_pool.dtype, device="cuda")
+    nxt = 0
+    for r in (1, 2):
+        for j in range(128):
+            extra_k[nxt] = k[tables[r, j]]
+            extra_v[nxt] = v[tables[r, j]]
+            tables[r, j] = nb + nxt
+            nxt += 1
+    k2 = torch.cat([k, extra_k]).contiguous()
+    v2 = torch.cat([v, extra_v]).contiguous()
+    d = c.to("cuda")
+    out_private = pk.pa_decode(d.q, k2, v2, tables.cuda(), d.seq_lens, c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_shared.view(torch.int16), out_private.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# configuration 4: 70B-shaped layer, full size, sampled rows
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_config4_full_size_sampled(kernel):
+    c = wl.config4()
+    lens = c.seq_lens.numpy()
+    order = np.argsort(lens)
+    rows = sorted(set(order[:6].tolist() + order[-6:].tolist() + list(range(0, 256, 23))))
+    ref = oracle.paged_decode(**oracle_inputs(c), rows=rows)
+    out, _, _ = run_step(c, kernel=kernel, partition_tokens=512)
+    worst = compare(gpu_out_f64(out, rows), ref, lens[rows], "bf16")
+    print(f"config4 {kernel} worst ratio {worst:.3f} over {len(rows)} rows")
+
+
+# --------------------------------------------------------------------------
+# configuration 5: bucketed step with padded rows, per-layer pools
+# --------------------------------------------------------------------------
+
+def _c5_check(bucket, layers, rows=None):
+    spec = wl.config5_spec(bucket)
+    bt = torch.from_numpy(spec.block_tables).cuda()
+    lens = torch.from_numpy(spec.seq_lens).cuda()
+    for layer in layers:
+        q, k, v = wl.config5_layer(spec, layer, "cuda")
+        out = pk.pa_decode(q, k, v, bt, lens, 1.0 / math.sqrt(128), partition_tokens=512)
+        torch.cuda.synchronize()
+        sel = list(range(bucket)) if rows is None else rows
+        # host copies of just the blocks the sampled rows reference
+        need = sorted({int(spec.block_tables[b, j]) for b in sel
+                       for j in range(math.ceil(int(spec.seq_lens[b]) / 16))} | {spec.poison_block})
+        remap = np.full(spec.num_blocks, -1, dtype=np.int64)
+        remap[need] = np.arange(len(need))
+        idx = torch.tensor(need, dtype=torch.long, device="cuda")
+        kh, vh = to_numpy(k[idx]), to_numpy(v[idx])
+        tables = np.where(spec.block_tables[sel] >= 0,
+                          remap[spec.block_tables[sel]], 0).astype(np.int32)
+        tables[tables < 0] = remap[spec.poison_block]
+        ref = oracle.paged_decode(to_numpy(q)[sel], kh, vh, tables, spec.seq_lens[sel],
+                                  1.0 / math.sqrt(128), "bf16")
+        compare(gpu_out_f64(out, sel), ref, spec.seq_lens[sel], "bf16")
+        # padded rows are exact zeros
+        pad = out[spec.n_real:]
+        assert torch.count_nonzero(pad.view(torch.int16)) == 0
+        del q, k, v
+
+
+@pytest.mark.parametrize("bucket", [1, 2, 4, 8])
+def test_config5_small_buckets_all_rows(bucket):
+    _c5_check(bucket, layers=[0, 1, 2, 31])
+
+
+@pytest.mark.parametrize("bucket", [64, 256])
+def test_config5_large_buckets_sampled(bucket):
+    spec = wl.config5_spec(bucket)
+    rng = np.random.default_rng(bucket)
+    rows = sorted(rng.choice(spec.n_real, size=12, replace=False).tolist()
+                  + [spec.n_real - 1] + ([spec.n_real] if spec.n_real < bucket else []))
+    _c5_check(bucket, layers=[0, 31], rows=rows)
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_deterministic_and_placement_invariant(kernel):
+    c = wl.random_case(300, 12, 32, 8, 128, "bf16", max_len=2000)
+    out1, _, _ = run_step(c, kernel=kernel)
+    out2, _, _ = run_step(c, kernel=kernel)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    p = wl.permute_physical(c, 3)
+    out3, _, _ = run_step(p, kernel=kernel)
+    assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
+
+
+def test_kernels_agree_within_tolerance():
+    c = wl.random_case(301, 6, 64, 8, 128, "bf16", max_len=3000)
+    ref, _, _ = oracle_step(c)
+    a, _, _ = run_step(c, kernel="mfma")
+    b, _, _ = run_step(c, kernel="valu")
+    compare(gpu_out_f64(a), ref, c.seq_lens.numpy(), "bf16")
+    compare(gpu_out_f64(b), ref, c.seq_lens.numpy(), "bf16")
+
+
+def test_abi_error_reaches_python():
+    c = wl.random_case(302, 2, 8, 2, 64, "bf16", max_len=600).to("cuda")
+    with pytest.raises(pk.PagedKVError):
+        pk.pa_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.seq_lens, c.scale,
+                     partition_tokens=16,
+                     workspace=torch.empty(8, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        pk.pa_decode(c.q.float(), c.k_pool, c.v_pool, c.block_tables, c.seq_lens, c.scale)
