@@ -1,0 +1,325 @@
+"""Paged decode attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|4|5]
+                    [--kernel auto|mfma|valu] [--partition P] [--bucket B]
+
+A step is one pass of the hot path over one batch:
+  config 2 (default; Llama-3-8B-shaped layer, B = 64, L ~ U[128, 4096]):
+      pa_write_kv of the 64 new tokens, then pa_decode over all 64 rows;
+  config 4 (Llama-3.3-70B-shaped layer, B = 256, lognormal lengths):
+      pa_decode;
+  config 5 (8B decode step, 32 layers, bucket B of padded rows):
+      pa_decode for each of the 32 layers.
+Copy-on-write block copies fire only on a divergent write to a shared block,
+which these batches do not have; pa_copy_blocks is timed separately
+(`copy_blocks_us`) on one 8B-shaped block pair per call.
+
+Inputs are seeded, synthetic and resident in HBM before timing; three
+independent copies of the inputs rotate so that no step reads data the
+previous one left in the 256 MB last-level cache (config 5 streams > 0.5 GB
+per step by itself and uses one copy).
+
+Printed: one JSON line with the achieved KV bandwidth (valid tokens' K and V
+bytes / step time), sequences per second per layer, the roofline of the
+decode kernel (algorithmic bytes per call / mean call time from HIP events on
+the launch stream), and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s per layer"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = {
+    "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h"],
+    "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 4, 5])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-K partition tokens; 0 = balanced split (default 0 for "
+                         "configs 2 and 4, 512 for the 32-layer step)")
+    ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work budget for the oracle baseline (0 = skip)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="also run a plain copy kernel of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SRC[kernel]:
+        with open(os.path.join(ROOT, "paged_kv_cache_55_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per decode call from a committed counter summary, if the
+    kernel sources still hash to what was profiled."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("TRAFFIC_JSON "):
+            rec = json.loads(line[len("TRAFFIC_JSON "):])
+            if rec.get("kernel_hash") == kernel_hash(kernel):
+                return rec.get("hbm_bytes_per_call")
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not "
+              "supported (the paged decode path shards by sequence or KV head "
+              "with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_55_amd as pk
+    import workloads as wl
+
+    if not os.path.exists(os.path.join(ROOT, "paged_kv_cache_55_amd", "libpagedkv.so")):
+        from paged_kv_cache_55_amd import build as b
+        b.build()
+    pk.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kernel = args.kernel if args.kernel != "auto" else "mfma"
+    part = (512 if args.config == 5 else 0) if args.partition is None else args.partition
+
+    # ---------------- inputs ----------------
+    if args.config in (2, 4):
+        case = wl.config2() if args.config == 2 else wl.config4()
+        copies = [case.to(dev) for _ in range(max(1, args.copies))]
+        B, Hq, Hkv, D = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
+        n_real = int((case.seq_lens > 0).sum())
+        kv_bytes = case.kv_bytes()
+        layers = 1
+        lens_host = case.seq_lens.numpy()
+        workload = ("llama3_8b_layer_b64_u128_4096" if args.config == 2
+                    else "llama33_70b_layer_b256_lognormal1024")
+        outs = [torch.empty_like(c.q) for c in copies]
+        dims = pk.make_dims(B, Hq, Hkv, D, case.max_blocks_per_seq, case.num_blocks,
+                            pk.PA_BF16, part, kernel)
+        ws_bytes = pk.pa_decode_workspace_bytes(dims)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        scale = case.scale
+
+        def decode_calls(i):
+            c = copies[i % len(copies)]
+            return [(c.q, c.k_pool, c.v_pool, c.block_tables, c.seq_lens, outs[i % len(copies)])]
+
+        def pre(i):
+            c = copies[i % len(copies)]
+            if c.slot_mapping is not None:
+                pk.pa_write_kv(c.k_new, c.v_new, c.slot_mapping, c.k_pool, c.v_pool)
+    else:
+        spec = wl.config5_spec(args.bucket)
+        B, Hq, Hkv, D = spec.bucket, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+        n_real = spec.n_real
+        layers = spec.layers
+        kv_bytes = spec.kv_bytes_per_layer() * layers
+        lens_host = spec.seq_lens
+        workload = f"llama3_8b_step_32layers_bucket{args.bucket}"
+        bt = torch.from_numpy(spec.block_tables).to(dev)
+        lens = torch.from_numpy(spec.seq_lens).to(dev)
+        layer_t = [wl.config5_layer(spec, l, dev) for l in range(layers)]
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        dims = pk.make_dims(B, Hq, Hkv, D, wl.C5_MB, spec.num_blocks, pk.PA_BF16, part, kernel)
+        ws_bytes = pk.pa_decode_workspace_bytes(dims)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        scale = 1.0 / math.sqrt(D)
+        case = None
+
+        def decode_calls(i):
+            return [(q, k, v, bt, lens, out) for (q, k, v) in layer_t]
+
+        def pre(i):
+            pass
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        pre(i)
+        for (q, k, v, tb, ln, o) in decode_calls(i):
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part, kernel=kernel,
+                         workspace=ws, stream=stream)
+            if events is not None:
+                e1.record(stream)
+                events.append((e0, e1))
+
+    # ---------------- timing ----------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-call decode durations, measured in a second pass with events
+    events = []
+    for i in range(args.steps):
+        step(i, events)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in events])
+
+    # copy-on-write block copy, one 8B-shaped block pair per call
+    copy_us = None
+    if args.config in (2, 4):
+        c = copies[0]
+        pair = torch.tensor([[int(c.block_tables[0, 0]), c.poison_block]], dtype=torch.int32,
+                            device=dev)
+        ce0 = torch.cuda.Event(enable_timing=True)
+        ce1 = torch.cuda.Event(enable_timing=True)
+        kp = c.k_pool.clone()
+        vp = c.v_pool.clone()
+        for _ in range(5):
+            pk.pa_copy_blocks(kp, vp, pair)
+        ce0.record(stream)
+        for _ in range(50):
+            pk.pa_copy_blocks(kp, vp, pair)
+        ce1.record(stream)
+        torch.cuda.synchronize()
+        copy_us = ce0.elapsed_time(ce1) / 50 * 1e3
+        del kp, vp
+
+    if args.traffic_probe:
+        n = 1 << 28
+        x = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(f"TRAFFIC_PROBE neg bytes_read={n} bytes_written={n}", file=sys.stderr)
+
+    # ---------------- figures ----------------
+    sec = ms_per_step / 1e3
+    value = kv_bytes / sec / 1e9
+    table_bytes = int(sum(math.ceil(int(L) / 16) for L in lens_host)) * 4 * (1 if layers == 1 else 1)
+    per_call_alg = (kv_bytes / layers) + 2 * B * Hq * D * 2 + table_bytes + 4 * B
+    mean_call_s = float(call_ms.mean()) / 1e3
+    achieved = per_call_alg / mean_call_s / 1e9
+    traffic = load_traffic(kernel, workload)
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(args, case, lens_host, kv_bytes / layers, workload)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block placement)",
+        "config": {
+            "workload": workload,
+            "batch": B, "real_rows": n_real, "q_heads": Hq, "kv_heads": Hkv,
+            "head_dim": D, "block_size": 16, "layers": layers,
+            "partition_tokens": part, "kernel": kernel,
+            "kv_bytes_per_step": kv_bytes,
+            "step": ("pa_write_kv(64 tokens) + pa_decode" if args.config == 2
+                     else "pa_decode" if args.config == 4 else "32 x pa_decode"),
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s_per_layer": round(n_real * layers / sec, 1) if layers == 1 else round(n_real / (sec / layers), 1),
+        "decode_call_us": {"mean": round(float(call_ms.mean()) * 1e3, 2),
+                           "p10": round(float(np.percentile(call_ms, 10)) * 1e3, 2),
+                           "p50": round(float(np.percentile(call_ms, 50)) * 1e3, 2),
+                           "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
+        "copy_blocks_us": None if copy_us is None else round(copy_us, 2),
+        "roofline": {
+            "kernel": f"pa_decode ({kernel} decode kernel + partial merge kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_call": int(per_call_alg),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, case, lens_host, kv_bytes_per_layer, workload):
+    """Time the float64 oracle on host cores over a bounded sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads as wl
+    from workloads import to_numpy
+
+    if case is None:  # config 5: one layer's sample of rows, drawn on the host
+        return None
+    a = dict(q=to_numpy(case.q), k_pool=to_numpy(case.k_pool), v_pool=to_numpy(case.v_pool),
+             block_tables=to_numpy(case.block_tables), seq_lens=to_numpy(case.seq_lens),
+             scale=case.scale, dtype=case.dtype)
+    rows_all = list(range(case.num_seqs))
+    done_bytes, done_rows, t_total = 0, 0, 0.0
+    elem = 2
+    with threadpool_limits(limits=1):
+        i = 0
+        while t_total < args.cpu_seconds and i < 4 * len(rows_all):
+            b = rows_all[i % len(rows_all)]
+            t = time.perf_counter()
+            oracle.paged_decode(**a, rows=[b])
+            t_total += time.perf_counter() - t
+            done_bytes += int(lens_host[b]) * case.num_kv_heads * case.head_dim * 2 * elem
+            done_rows += 1
+            i += 1
+    return {
+        "value": round(done_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done_rows} sequence decodes of {workload} (rows in batch order, "
+                  f"{done_bytes / 1e6:.1f} MB of K/V) in {t_total:.1f} s, float64 numpy, "
+                  "BLAS limited to 1 thread",
+        "seqs_per_s": round(done_rows / t_total, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -30,11 +30,14 @@
  *
  * Ownership and execution
  *   The caller allocates and owns every buffer, including the workspace.
- *   The library allocates nothing, keeps no pointer after a call returns
- *   and holds no state: calls are re-entrant. Each call only enqueues work
- *   on `stream` (a hipStream_t; NULL = the default stream) and returns
- *   without synchronising. Launch grids depend only on the pa_dims values,
- *   never on device-resident lengths or table entries.
+ *   The library allocates nothing and keeps no pointer after a call
+ *   returns; its only state is a per-device cache of launch geometry (CU
+ *   count and kernel occupancy), filled on first use under a lock, so calls
+ *   are re-entrant. Each call only enqueues work on `stream` (a
+ *   hipStream_t on the current device; NULL = the default stream) and
+ *   returns without synchronising. Launch grids depend only on the pa_dims
+ *   values and the device, never on device-resident lengths or table
+ *   entries.
  *
  * Errors
  *   Arguments the host can see (pointers, dims, sizes) are checked before
@@ -75,7 +78,7 @@ typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_k
 
 /* Host-side dimensions; all fields are fixed for a given captured shape. */
 typedef struct {
-  int32_t num_seqs;           /* B   (>= 1) */
+  int32_t num_seqs;           /* B   (1 .. 4096) */
   int32_t num_q_heads;        /* Hq  (multiple of Hkv, Hq / Hkv <= 16) */
   int32_t num_kv_heads;       /* Hkv (>= 1) */
   int32_t head_dim;           /* D   (64 or 128) */

@@ -2,8 +2,13 @@
 // kernel selection and launches. No allocation, no state, no host sync.
 #include <math.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "launch.h"
 #include "pagedkv.h"
+#include "worklist.h"
 
 using namespace pagedkv;
 
@@ -28,10 +33,22 @@ pa_status check_pool(const pa_dims* d) {
 
 int elem_bytes(const pa_dims* d) { return d->dtype == PA_F32 ? 4 : 2; }
 
+int pick_kernel(const pa_dims* d) {
+  if (d->kernel != PA_KERNEL_AUTO) return d->kernel;
+  return d->dtype == PA_BF16 ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
+}
+
+// Balanced split: at most this many decode workgroups (4 waves each); the
+// workspace holds two partial slots per wave.
+constexpr int kMaxBalancedGrid = 1024;
+constexpr int kMinSegBlocks = 16;
+
 struct Plan {
-  int part_tokens;  // tokens per partition (multiple of 16)
-  int num_parts;    // partitions per sequence at most
-  size_t ws_bytes;  // 0 when num_parts == 1
+  int kernel;       // PA_KERNEL_VALU or PA_KERNEL_MFMA
+  bool balanced;    // balanced split (MFMA, partition_tokens == 0)
+  int part_tokens;  // fixed split: tokens per partition (multiple of 16)
+  int num_parts;    // fixed split: partitions per sequence at most
+  size_t ws_bytes;  // 0 when nothing is ever merged
   size_t off_l, off_o;
 };
 
@@ -42,14 +59,26 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
     return PA_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (d->num_q_heads / d->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
-  if (d->num_seqs > kMaxGridYZ || d->num_q_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs > kMaxSeqs || d->num_q_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   if (d->max_blocks_per_seq > (1 << 26)) return PA_ERR_UNSUPPORTED;
   if (d->partition_tokens < 0 || d->partition_tokens % kBlockTokens != 0)
     return PA_ERR_INVALID_ARG;
   if (d->kernel != PA_KERNEL_AUTO && d->kernel != PA_KERNEL_VALU && d->kernel != PA_KERNEL_MFMA)
     return PA_ERR_INVALID_ARG;
   if (d->kernel == PA_KERNEL_MFMA && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  p->kernel = pick_kernel(d);
+  const int G = d->num_q_heads / d->num_kv_heads;
   const int max_tokens = d->max_blocks_per_seq * kBlockTokens;
+  p->balanced = p->kernel == PA_KERNEL_MFMA && d->partition_tokens == 0;
+  if (p->balanced) {
+    p->part_tokens = max_tokens;
+    p->num_parts = 1;
+    const size_t rows = (size_t)2 * 4 * kMaxBalancedGrid * G;
+    p->off_l = align_up(rows * sizeof(float));
+    p->off_o = 2 * p->off_l;
+    p->ws_bytes = p->off_o + rows * (size_t)d->head_dim * sizeof(float);
+    return PA_OK;
+  }
   const int part = (d->partition_tokens == 0 || d->partition_tokens >= max_tokens)
                        ? max_tokens
                        : d->partition_tokens;
@@ -66,9 +95,30 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
   return PA_OK;
 }
 
-int pick_kernel(const pa_dims* d) {
-  if (d->kernel != PA_KERNEL_AUTO) return d->kernel;
-  return d->dtype == PA_BF16 ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
+// Workgroups of `fn` (256 threads, `smem` dynamic LDS bytes) the current
+// device holds at once: CU count x occupancy. Cached per (device, kernel,
+// LDS size rounded up to 1 KiB); the only state the library keeps.
+hipError_t resident_workgroups(const void* fn, size_t smem, int* out) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  smem = (smem + 1023) / 1024 * 1024;
+  const auto key = std::make_tuple(dev, fn, smem);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  int ncu = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, smem);
+  if (e != hipSuccess) return e;
+  *out = cache[key] = (ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -112,14 +162,36 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.max_blocks = dims->max_blocks_per_seq;
   a.part_tokens = plan.part_tokens;
   a.num_parts = plan.num_parts;
+  a.split_waves = 0;
+  a.min_seg_blocks = 0;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  const int kernel = pick_kernel(dims);
-  if (kernel == PA_KERNEL_MFMA)
-    e = launch_decode_mfma(a, dims->head_dim, s);
+  const void* fn = plan.kernel == PA_KERNEL_MFMA
+                       ? decode_mfma_fn(dims->head_dim, plan.balanced)
+                       : decode_valu_fn(dims->dtype, dims->head_dim, a.group);
+  const size_t smem = (size_t)(dims->num_seqs + 1) * sizeof(int);
+  int resident = 0;
+  hipError_t e = resident_workgroups(fn, smem, &resident);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (plan.balanced) {
+    const int grid = resident < kMaxBalancedGrid ? resident : kMaxBalancedGrid;
+    a.split_waves = 4 * grid;
+    a.min_seg_blocks = kMinSegBlocks;
+    e = launch_decode_mfma(a, dims->head_dim, true, grid, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+    const long long pairs = (long long)dims->num_seqs * dims->num_kv_heads;
+    e = launch_decode_balanced_reduce(a, dims->head_dim,
+                                      (int)(pairs < kMaxBalancedGrid ? pairs : kMaxBalancedGrid),
+                                      s);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  }
+  // never more workgroups than items can exist
+  const long long max_items = (long long)dims->num_seqs * dims->num_kv_heads * plan.num_parts;
+  const int grid = (int)(max_items < resident ? max_items : resident);
+  if (plan.kernel == PA_KERNEL_MFMA)
+    e = launch_decode_mfma(a, dims->head_dim, false, grid, s);
   else
-    e = launch_decode_valu(a, dims->dtype, dims->head_dim, s);
+    e = launch_decode_valu(a, dims->dtype, dims->head_dim, grid, s);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
   if (plan.num_parts > 1) {
     e = launch_decode_reduce(a, dims->dtype, dims->head_dim, s);

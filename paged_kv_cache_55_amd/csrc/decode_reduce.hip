@@ -12,24 +12,30 @@ namespace pagedkv {
 
 namespace {
 
+// One workgroup per (KV head, sequence): its G query heads x D outputs.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
   const int L = a.seq_lens[b];
   const int np = (L + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
-  const size_t r0 = ((size_t)b * a.num_q_heads + h) * a.num_parts;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[r0 + p]);
-  float lsum = 0.f, o = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float f = fast_exp2(a.ws_m[r0 + p] - M);
-    lsum = fmaf(a.ws_l[r0 + p], f, lsum);
-    o = fmaf(a.ws_o[(r0 + p) * D + d], f, o);
+  const int G = a.group;
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    const int h = kvh * G + g;
+    const size_t r0 = ((size_t)b * a.num_q_heads + h) * a.num_parts;
+    float M = -INFINITY;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[r0 + p]);
+    float lsum = 0.f, o = 0.f;
+    for (int p = 0; p < np; ++p) {
+      const float f = fast_exp2(a.ws_m[r0 + p] - M);
+      lsum = fmaf(a.ws_l[r0 + p], f, lsum);
+      o = fmaf(a.ws_o[(r0 + p) * D + d], f, o);
+    }
+    ElemTraits<T>::store1((T*)a.out + ((size_t)b * a.num_q_heads + h) * D + d, o / lsum);
   }
-  ElemTraits<T>::store1((T*)a.out + ((size_t)b * a.num_q_heads + h) * D + d, o / lsum);
 }
 
 template <typename T, int D>
@@ -37,7 +43,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   DecodeArgs arg = a;
   void* args[] = {&arg};
   return hipLaunchKernel((const void*)&decode_reduce_kernel<T, D>,
-                         dim3(a.num_q_heads, a.num_seqs), dim3(D), args, 0, s);
+                         dim3(a.num_kv_heads, a.num_seqs), dim3(256), args, 0, s);
 }
 
 }  // namespace

@@ -1,9 +1,10 @@
 // Paged decode attention on the vector ALUs (f32 and bf16, D = 64 or 128).
 //
-// One workgroup (4 waves) per (partition, KV head, sequence): grid
-// (NPmax, Hkv, B). A partition is `part_tokens` consecutive tokens
-// (a multiple of 16); waves take the partition's 16-token blocks round
-// robin. For each block the wave
+// A persistent grid of 4-wave workgroups walks the work list of
+// (sequence, partition, KV head) items (worklist.h). A partition is
+// `part_tokens` consecutive tokens (a multiple of 16); the waves of a
+// workgroup take the partition's 16-token blocks round robin. For each
+// block the wave
 //   1. reads the block's physical id from the table (wave-uniform load),
 //   2. loads the 16 x D K tile (16-byte loads, 4 lanes per token row),
 //   3. forms the G scores of each token (q held in LDS, fp32 FMA), reduces
@@ -21,6 +22,7 @@
 // three": per block, a table read then a gather) and llm-serving.xyz
 // "KV-cache systems" (the table read sits in front of the gather).
 #include "launch.h"
+#include "worklist.h"
 
 namespace pagedkv {
 
@@ -29,16 +31,24 @@ namespace {
 constexpr int kWaves = 4;
 
 template <typename T, int D, int GP>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+struct ValuSmem {
+  float qs[GP][D];
+  float pbuf[kWaves][kBlockTokens][GP];
+  float red_m[kWaves][GP];
+  float red_l[kWaves][GP];
+  float red_o[kWaves][GP][D];
+};
+
+// One work item: partition `part` of sequence b against KV head kvh.
+template <typename T, int D, int GP>
+__device__ __forceinline__ void valu_item(const DecodeArgs& a, int b, int kvh, int part, int L,
+                                          ValuSmem<T, D, GP>& sm) {
   using Tr = ElemTraits<T>;
   constexpr int E = Tr::kPerVec;           // elements per 16-byte load
   constexpr int NCH = D / (4 * E);         // 16-byte chunks per lane per K row
   constexpr int DPL = D / 64;              // V dims owned by each lane
   static_assert(NCH >= 1 && DPL >= 1, "unsupported head dim");
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -47,24 +57,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int h0 = kvh * G;
   T* out = (T*)a.out;
 
-  const int L = a.seq_lens[b];
-  if (L <= 0) {  // padded row: exact zeros, no K/V or table reads
-    if (part == 0)
-      for (int i = tid; i < G * D; i += blockDim.x)
-        Tr::store1(out + ((size_t)b * Hq + h0) * D + i, 0.f);
-    return;
-  }
   const int tok0 = part * a.part_tokens;
-  if (tok0 >= L) return;
   const int tok_end = min(L, tok0 + a.part_tokens);
   const int nblk = (tok_end - tok0 + kBlockTokens - 1) / kBlockTokens;
   const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-
-  __shared__ float qs[GP][D];
-  __shared__ float pbuf[kWaves][kBlockTokens][GP];
-  __shared__ float red_m[kWaves][GP];
-  __shared__ float red_l[kWaves][GP];
-  __shared__ float red_o[kWaves][GP][D];
+  auto& qs = sm.qs;
+  auto& pbuf = sm.pbuf;
+  auto& red_m = sm.red_m;
+  auto& red_l = sm.red_l;
+  auto& red_o = sm.red_o;
 
   const T* qp = (const T*)a.q + ((size_t)b * Hq + h0) * D;
   for (int i = tid; i < GP * D; i += blockDim.x) {
@@ -204,28 +205,59 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       }
     }
   }
+  __syncthreads();  // q and the merge buffers are reused by the next item
+}
+
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+  extern __shared__ int prefix[];  // [B + 1]
+  __shared__ int scan_scratch[kWaves];
+  __shared__ ValuSmem<T, D, GP> sm;
+
+  const int B = a.num_seqs;
+  build_partition_prefix(a.seq_lens, B, a.part_tokens, prefix, scan_scratch);
+
+  // padded rows (L <= 0): exact zeros, no K/V or table reads
+  const int row_elems = a.num_q_heads * D;
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    if (prefix[b + 1] != prefix[b]) continue;
+    T* o = (T*)a.out + (size_t)b * row_elems;
+    for (int i = threadIdx.x; i < row_elems; i += blockDim.x) ElemTraits<T>::store1(o + i, 0.f);
+  }
+
+  const int Hkv = a.num_kv_heads;
+  const int nitems = prefix[B] * Hkv;
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int j = item / Hkv;
+    const int kvh = item - j * Hkv;
+    const int b = find_sequence(prefix, B, j);
+    const int part = j - prefix[b];
+    valu_item<T, D, GP>(a, b, kvh, part, a.seq_lens[b], sm);
+  }
 }
 
 template <typename T, int D>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs), block(256);
-  DecodeArgs arg = a;
-  void* args[] = {&arg};
-  const int G = a.group;
-  const void* fn;
-  if (G <= 1) fn = (const void*)&decode_valu_kernel<T, D, 1>;
-  else if (G <= 2) fn = (const void*)&decode_valu_kernel<T, D, 2>;
-  else if (G <= 4) fn = (const void*)&decode_valu_kernel<T, D, 4>;
-  else if (G <= 8) fn = (const void*)&decode_valu_kernel<T, D, 8>;
-  else fn = (const void*)&decode_valu_kernel<T, D, 16>;
-  return hipLaunchKernel(fn, grid, block, args, 0, s);
+const void* pick_fn(int G) {
+  if (G <= 1) return (const void*)&decode_valu_kernel<T, D, 1>;
+  if (G <= 2) return (const void*)&decode_valu_kernel<T, D, 2>;
+  if (G <= 4) return (const void*)&decode_valu_kernel<T, D, 4>;
+  if (G <= 8) return (const void*)&decode_valu_kernel<T, D, 8>;
+  return (const void*)&decode_valu_kernel<T, D, 16>;
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s) {
-  if (dtype == 0) return head_dim == 64 ? launch_t<float, 64>(a, s) : launch_t<float, 128>(a, s);
-  return head_dim == 64 ? launch_t<bf16_t, 64>(a, s) : launch_t<bf16_t, 128>(a, s);
+const void* decode_valu_fn(int dtype, int head_dim, int group) {
+  if (dtype == 0) return head_dim == 64 ? pick_fn<float, 64>(group) : pick_fn<float, 128>(group);
+  return head_dim == 64 ? pick_fn<bf16_t, 64>(group) : pick_fn<bf16_t, 128>(group);
+}
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int grid,
+                              hipStream_t s) {
+  DecodeArgs arg = a;
+  void* args[] = {&arg};
+  return hipLaunchKernel(decode_valu_fn(dtype, head_dim, a.group), dim3(grid), dim3(256), args,
+                         (size_t)(a.num_seqs + 1) * sizeof(int), s);
 }
 
 }  // namespace pagedkv

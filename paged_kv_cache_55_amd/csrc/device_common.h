@@ -84,11 +84,16 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
-  float* ws_m;   // [B, Hq, NPmax] running max (log2 domain, scaled scores)
-  float* ws_l;   // [B, Hq, NPmax] sum of 2^(s - m)
-  float* ws_o;   // [B, Hq, NPmax, D] unnormalised output
+  // fp32 partials (log2-domain max m, sum of 2^(s - m), unnormalised output):
+  //   fixed split     row (b * Hq + h) * NPmax + partition
+  //   balanced split  row (2 * wave + piece) * G + g
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;   // [rows, D]
   float scale_log2;  // scale * log2(e)
   int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, part_tokens, num_parts;
+  int split_waves;     // balanced split: waves of the decode grid (4 per workgroup)
+  int min_seg_blocks;  // balanced split: least blocks per wave range
 };
 
 }  // namespace pagedkv

@@ -9,8 +9,16 @@
 namespace pagedkv {
 
 // dtype: 0 = f32, 1 = bf16 (pa_dtype).
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s);
+// Persistent decode kernels: `grid` workgroups of 256 threads, dynamic LDS
+// of (num_seqs + 1) ints for the work list.
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int grid,
+                              hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, int grid,
+                              hipStream_t s);
+hipError_t launch_decode_balanced_reduce(const DecodeArgs& a, int head_dim, int grid,
+                                         hipStream_t s);
+const void* decode_valu_fn(int dtype, int head_dim, int group);
+const void* decode_mfma_fn(int head_dim, bool balanced);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,

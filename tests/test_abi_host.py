@@ -67,7 +67,11 @@ def test_workspace_size(lib):
     rows = 64 * 32 * nparts
     align = lambda x: (x + 255) // 256 * 256
     assert pk.pa_decode_workspace_bytes(d) == 2 * align(rows * 4) + rows * 128 * 4
-    assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0)) == 0
+    # balanced split (matrix-core kernel, partition_tokens = 0): two fp32
+    # partial slots per wave of at most 1024 four-wave workgroups
+    slots = 2 * 4 * 1024 * 4
+    assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0)) == 2 * align(slots * 4) + slots * 128 * 4
+    assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0, kernel="valu")) == 0
     assert pk.pa_decode_workspace_bytes(dims(partition_tokens=4096)) == 0
     assert pk.pa_decode_workspace_bytes(dims(max_blocks_per_seq=32)) == 0
     assert pk.pa_decode_workspace_bytes(dims(head_dim=96)) == 0  # invalid -> 0
@@ -86,6 +90,7 @@ def decode_status(lib, d, q=FAKE, ws=None, wsb=0, scale=0.1):
     (dict(num_q_heads=33), pk.PA_ERR_INVALID_ARG),
     (dict(num_q_heads=8 * 17), pk.PA_ERR_UNSUPPORTED),
     (dict(num_seqs=0), pk.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=4097), pk.PA_ERR_UNSUPPORTED),
     (dict(num_kv_heads=0), pk.PA_ERR_INVALID_ARG),
     (dict(max_blocks_per_seq=0), pk.PA_ERR_INVALID_ARG),
     (dict(num_blocks=0), pk.PA_ERR_INVALID_ARG),

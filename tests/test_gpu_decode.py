@@ -146,29 +146,48 @@ def test_config3_sharing_is_exact():
 # configuration 4: 70B-shaped layer, full size, sampled rows
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_config4_full_size_sampled(kernel):
+@pytest.fixture(scope="module")
+def config4_ref():
     c = wl.config4()
     lens = c.seq_lens.numpy()
     order = np.argsort(lens)
     rows = sorted(set(order[:6].tolist() + order[-6:].tolist() + list(range(0, 256, 23))))
-    ref = oracle.paged_decode(**oracle_inputs(c), rows=rows)
-    out, _, _ = run_step(c, kernel=kernel, partition_tokens=512)
-    worst = compare(gpu_out_f64(out, rows), ref, lens[rows], "bf16")
-    print(f"config4 {kernel} worst ratio {worst:.3f} over {len(rows)} rows")
+    return c, rows, oracle.paged_decode(**oracle_inputs(c), rows=rows)
+
+
+@pytest.mark.parametrize("kernel,partition", [("mfma", 512), ("mfma", 0), ("valu", 512)])
+def test_config4_full_size_sampled(config4_ref, kernel, partition):
+    c, rows, ref = config4_ref
+    out, _, _ = run_step(c, kernel=kernel, partition_tokens=partition)
+    worst = compare(gpu_out_f64(out, rows), ref, c.seq_lens.numpy()[rows], "bf16")
+    print(f"config4 {kernel} part={partition} worst ratio {worst:.3f} over {len(rows)} rows")
+
+
+@pytest.mark.parametrize("lens", [
+    [8000],                                     # one pair cut into many pieces
+    [0, 5, 0, 0, 17, 1, 0, 300, 16, 0],         # tiny pairs, padded rows between
+    [4096, 1, 1, 1, 2000, 33, 0, 8192, 15],     # mixed
+    [1] * 64,                                   # one block per pair
+])
+def test_balanced_split_edges(lens):
+    c = wl.random_case(400 + len(lens), len(lens), 32, 8, 128, "bf16", lens=lens)
+    ref, _, _ = oracle_step(c)
+    for part in (0, 512):
+        out, _, _ = run_step(c, kernel="mfma", partition_tokens=part)
+        compare(gpu_out_f64(out), ref, lens, "bf16")
 
 
 # --------------------------------------------------------------------------
 # configuration 5: bucketed step with padded rows, per-layer pools
 # --------------------------------------------------------------------------
 
-def _c5_check(bucket, layers, rows=None):
+def _c5_check(bucket, layers, rows=None, partition=512):
     spec = wl.config5_spec(bucket)
     bt = torch.from_numpy(spec.block_tables).cuda()
     lens = torch.from_numpy(spec.seq_lens).cuda()
     for layer in layers:
         q, k, v = wl.config5_layer(spec, layer, "cuda")
-        out = pk.pa_decode(q, k, v, bt, lens, 1.0 / math.sqrt(128), partition_tokens=512)
+        out = pk.pa_decode(q, k, v, bt, lens, 1.0 / math.sqrt(128), partition_tokens=partition)
         torch.cuda.synchronize()
         sel = list(range(bucket)) if rows is None else rows
         # host copies of just the blocks the sampled rows reference
@@ -190,32 +209,34 @@ def _c5_check(bucket, layers, rows=None):
         del q, k, v
 
 
+@pytest.mark.parametrize("partition", [512, 0])
 @pytest.mark.parametrize("bucket", [1, 2, 4, 8])
-def test_config5_small_buckets_all_rows(bucket):
-    _c5_check(bucket, layers=[0, 1, 2, 31])
+def test_config5_small_buckets_all_rows(bucket, partition):
+    _c5_check(bucket, layers=[0, 1, 2, 31], partition=partition)
 
 
+@pytest.mark.parametrize("partition", [512, 0])
 @pytest.mark.parametrize("bucket", [64, 256])
-def test_config5_large_buckets_sampled(bucket):
+def test_config5_large_buckets_sampled(bucket, partition):
     spec = wl.config5_spec(bucket)
     rng = np.random.default_rng(bucket)
     rows = sorted(rng.choice(spec.n_real, size=12, replace=False).tolist()
                   + [spec.n_real - 1] + ([spec.n_real] if spec.n_real < bucket else []))
-    _c5_check(bucket, layers=[0, 31], rows=rows)
+    _c5_check(bucket, layers=[0, 31], rows=rows, partition=partition)
 
 
 # --------------------------------------------------------------------------
 # invariants
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_deterministic_and_placement_invariant(kernel):
+@pytest.mark.parametrize("kernel,partition", [("mfma", 512), ("mfma", 0), ("valu", 512)])
+def test_deterministic_and_placement_invariant(kernel, partition):
     c = wl.random_case(300, 12, 32, 8, 128, "bf16", max_len=2000)
-    out1, _, _ = run_step(c, kernel=kernel)
-    out2, _, _ = run_step(c, kernel=kernel)
+    out1, _, _ = run_step(c, kernel=kernel, partition_tokens=partition)
+    out2, _, _ = run_step(c, kernel=kernel, partition_tokens=partition)
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     p = wl.permute_physical(c, 3)
-    out3, _, _ = run_step(p, kernel=kernel)
+    out3, _, _ = run_step(p, kernel=kernel, partition_tokens=partition)
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
 
 
