@@ -42,8 +42,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s per layer"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
-    "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h"],
-    "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h"],
+    "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h", "worklist.h"],
+    "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h", "worklist.h"],
 }
 
 
@@ -125,7 +125,7 @@ def main():
         dims = pk.make_dims(B, Hq, Hkv, D, case.max_blocks_per_seq, case.num_blocks,
                             pk.PA_BF16, part, kernel)
         ws_bytes = pk.pa_decode_workspace_bytes(dims)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         scale = case.scale
 
         def decode_calls(i):
@@ -150,7 +150,7 @@ def main():
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
         dims = pk.make_dims(B, Hq, Hkv, D, wl.C5_MB, spec.num_blocks, pk.PA_BF16, part, kernel)
         ws_bytes = pk.pa_decode_workspace_bytes(dims)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         scale = 1.0 / math.sqrt(D)
         case = None
 

@@ -91,18 +91,29 @@ typedef struct {
   int32_t kernel;             /* pa_kernel */
 } pa_dims;
 
-/* Bytes of device workspace pa_decode needs for these dims: 0 when every
- * sequence fits one partition (MB * 16 <= partition_tokens, or
- * partition_tokens == 0), else room for fp32 partial results
- * (max, sum, unnormalised output) of every (sequence, query head,
- * partition). Returns 0 for invalid dims as well; pa_decode reports those. */
+/* Bytes of device workspace pa_decode needs for these dims.
+ *   Fixed split (partition_tokens > 0, or the vector-ALU kernel): 0 when
+ *   every sequence fits one partition, else fp32 partial results (max, sum,
+ *   unnormalised output) of every (sequence, query head, partition).
+ *   Balanced split (matrix-core kernel, partition_tokens == 0): int32 piece
+ *   counters for every (sequence, KV head), then fp32 partials for two
+ *   pieces per wave of the decode grid (at most 4096 waves).
+ * The workspace must be zero-filled before its first use; every pa_decode
+ * call leaves it zero where it must be (the counters), so it can be reused
+ * without clearing. Calls that may overlap in time need separate
+ * workspaces. Returns 0 for invalid dims as well; pa_decode reports those. */
 size_t pa_decode_workspace_bytes(const pa_dims* dims);
 
 /* Paged decode attention: for every sequence b and query head h,
  *   out[b,h,:] = sum_t softmax_t(scale * <q[b,h,:], K_b[t]>) V_b[t]
  * over t < seq_lens[b], with K_b/V_b gathered through block_tables[b]
  * (naive softmax over the whole row; computed with an online softmax per
- * partition and a log-sum-exp merge across partitions, fp32 accumulation).
+ * piece of the sequence and a log-sum-exp merge across pieces, fp32
+ * accumulation). Pieces are fixed partitions of partition_tokens tokens,
+ * or, with partition_tokens == 0 and the matrix-core kernel, the balanced
+ * split: every wave of a persistent grid streams an equal share of all
+ * blocks and the last wave to finish a cut sequence merges its pieces.
+ * Results do not depend on timing: pieces merge in a fixed order.
  * Rows with seq_lens[b] == 0 get zeros. Slots at or past seq_lens[b] and
  * table entries at or past ceil(seq_lens[b] / 16) are never read, so they
  * may hold anything (NaN included). bf16 output is rounded to nearest even.

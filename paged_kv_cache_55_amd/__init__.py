@@ -149,7 +149,16 @@ def pa_decode_workspace_bytes(dims: PaDims) -> int:
 
 def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
               partition_tokens=512, kernel="auto", workspace=None, stream=None):
-    """out[b, h] = softmax(scale * q[b, h] K_b^T) V_b over the paged K/V."""
+    """out[b, h] = softmax(scale * q[b, h] K_b^T) V_b over the paged K/V.
+
+    ``partition_tokens`` > 0 splits each sequence into partitions of that
+    many tokens; 0 asks for the balanced split (matrix-core kernel) or one
+    partition per sequence (vector-ALU kernel). A caller-provided
+    ``workspace`` (uint8 device tensor of at least
+    pa_decode_workspace_bytes bytes) must be zero-filled before its first
+    use; calls leave it reusable. One workspace must not serve two calls that
+    can run at the same time.
+    """
     torch = _torch()
     NB, Hkv, D = _pool_dims(k_pool, v_pool)
     _need(q.dim() == 3 and q.shape[2] == D, "q must be [B, Hq, D]")
@@ -171,7 +180,8 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
     lib = load_library()
     need = int(lib.pa_decode_workspace_bytes(ctypes.byref(dims)))
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled once; pa_decode leaves it reusable
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
                        _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),

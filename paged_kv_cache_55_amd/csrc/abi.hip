@@ -49,7 +49,8 @@ struct Plan {
   int part_tokens;  // fixed split: tokens per partition (multiple of 16)
   int num_parts;    // fixed split: partitions per sequence at most
   size_t ws_bytes;  // 0 when nothing is ever merged
-  size_t off_l, off_o;
+  size_t off_m, off_l, off_o;  // fp32 partials
+  size_t off_cnt;              // balanced split: int32 piece counters [B, Hkv]
 };
 
 pa_status plan_decode(const pa_dims* d, Plan* p) {
@@ -74,8 +75,10 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
     p->part_tokens = max_tokens;
     p->num_parts = 1;
     const size_t rows = (size_t)2 * 4 * kMaxBalancedGrid * G;
-    p->off_l = align_up(rows * sizeof(float));
-    p->off_o = 2 * p->off_l;
+    p->off_cnt = 0;
+    p->off_m = align_up((size_t)d->num_seqs * d->num_kv_heads * sizeof(int));
+    p->off_l = p->off_m + align_up(rows * sizeof(float));
+    p->off_o = p->off_l + align_up(rows * sizeof(float));
     p->ws_bytes = p->off_o + rows * (size_t)d->head_dim * sizeof(float);
     return PA_OK;
   }
@@ -84,11 +87,13 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
                        : d->partition_tokens;
   p->part_tokens = part;
   p->num_parts = (max_tokens + part - 1) / part;
+  p->off_cnt = 0;
   if (p->num_parts == 1) {
-    p->ws_bytes = p->off_l = p->off_o = 0;
+    p->ws_bytes = p->off_m = p->off_l = p->off_o = 0;
     return PA_OK;
   }
   const size_t rows = (size_t)d->num_seqs * d->num_q_heads * p->num_parts;
+  p->off_m = 0;
   p->off_l = align_up(rows * sizeof(float));
   p->off_o = 2 * p->off_l;
   p->ws_bytes = p->off_o + rows * (size_t)d->head_dim * sizeof(float);
@@ -151,9 +156,10 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.seq_lens = seq_lens;
   a.out = out;
   char* ws = (char*)workspace;
-  a.ws_m = plan.ws_bytes ? (float*)ws : nullptr;
+  a.ws_m = plan.ws_bytes ? (float*)(ws + plan.off_m) : nullptr;
   a.ws_l = plan.ws_bytes ? (float*)(ws + plan.off_l) : nullptr;
   a.ws_o = plan.ws_bytes ? (float*)(ws + plan.off_o) : nullptr;
+  a.ws_cnt = plan.balanced ? (int*)(ws + plan.off_cnt) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = dims->num_seqs;
   a.num_q_heads = dims->num_q_heads;
@@ -178,11 +184,6 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
     a.split_waves = 4 * grid;
     a.min_seg_blocks = kMinSegBlocks;
     e = launch_decode_mfma(a, dims->head_dim, true, grid, s);
-    if (e != hipSuccess) return PA_ERR_LAUNCH;
-    const long long pairs = (long long)dims->num_seqs * dims->num_kv_heads;
-    e = launch_decode_balanced_reduce(a, dims->head_dim,
-                                      (int)(pairs < kMaxBalancedGrid ? pairs : kMaxBalancedGrid),
-                                      s);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   }
   // never more workgroups than items can exist

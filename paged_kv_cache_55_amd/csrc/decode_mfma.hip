@@ -35,7 +35,9 @@
 //             contiguous range of them, prefetching across pair boundaries.
 //             A pair whose blocks lie inside one wave's range is finished
 //             in place; a pair cut by range boundaries leaves one fp32
-//             partial per piece, merged by decode_balanced_reduce.
+//             partial per piece, and the wave that completes the last piece
+//             (an atomic count per pair) merges them: one kernel, no reduce
+//             pass.
 #include "launch.h"
 #include "worklist.h"
 
@@ -356,35 +358,146 @@ __device__ __forceinline__ long long balanced_chunk(long long total, int waves, 
   return even > min_blocks ? even : (long long)min_blocks;
 }
 
+// Pieces of the pair starting at flat index s with nb blocks: waves
+// v0 = s / chunk .. v1 = (s + nb - 1) / chunk. The first piece is wave v0's
+// slot 1 when that wave's range began before s, else its slot 0; every later
+// piece is the first segment (slot 0) of its wave.
+struct Pieces {
+  int v0, v1, first_slot;
+  __device__ __forceinline__ Pieces(long long s, int nb, long long chunk) {
+    v0 = (int)(s / chunk);
+    v1 = (int)((s + nb - 1) / chunk);
+    first_slot = 2 * v0 + ((long long)v0 * chunk < s ? 1 : 0);
+  }
+  __device__ __forceinline__ int slot(int v) const { return v == v0 ? first_slot : 2 * v; }
+};
+
+// Partials cross workgroups on different XCDs, whose L2 caches are not
+// coherent with each other. They are written and read with agent-scope
+// relaxed atomic accesses (coherent at the device level without flushing or
+// invalidating the whole L2), and the writer waits for its stores to
+// complete before it counts its piece.
+__device__ __forceinline__ void put_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_complete() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// One wave merges every piece of pair (b, kvh), in piece order, and writes
+// the bf16 output. Lane work unit: 4 consecutive dims of one head. The loads
+// of up to kBatch pieces are issued together so a merge costs one or two
+// memory round trips instead of one per piece.
+template <int D>
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int b, int kvh,
+                                             const Pieces& pc, int lane) {
+  constexpr int kBatch = 8;
+  const int G = a.group;
+  const int n = pc.v1 - pc.v0 + 1;
+  bf16_t* out = (bf16_t*)a.out + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * D;
+  for (int c = lane; c < G * D / 4; c += 64) {
+    const int g = c * 4 / D;
+    const int d0 = c * 4 - g * D;
+    float M = -INFINITY;
+    if (n > kBatch) {  // long pairs: find the max first
+      for (int p0 = 0; p0 < n; p0 += kBatch) {
+        float mb[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          mb[i] = p0 + i < n ? get_coherent(a.ws_m + (size_t)pc.slot(pc.v0 + p0 + i) * G + g)
+                             : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) M = fmaxf(M, mb[i]);
+      }
+    }
+    float lsum = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < n; p0 += kBatch) {
+      float mb[kBatch], lb[kBatch], ob[kBatch][4];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (p0 + i < n) {
+          const size_t r = (size_t)pc.slot(pc.v0 + p0 + i) * G + g;
+          mb[i] = get_coherent(a.ws_m + r);
+          lb[i] = get_coherent(a.ws_l + r);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ob[i][e] = get_coherent(a.ws_o + r * D + d0 + e);
+        } else {
+          mb[i] = -INFINITY;
+          lb[i] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ob[i][e] = 0.f;
+        }
+      }
+      if (n <= kBatch) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) M = fmaxf(M, mb[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const float f = fast_exp2(mb[i] - M);  // absent pieces: 2^-inf = 0
+        lsum = fmaf(lb[i], f, lsum);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(ob[i][e], f, o[e]);
+      }
+    }
+    const float inv = 1.f / lsum;
+    *(uint2*)(out + (size_t)g * D + d0) =
+        make_uint2(pack_bf16x2(f32_to_bf16_bits(o[0] * inv), f32_to_bf16_bits(o[1] * inv)),
+                   pack_bf16x2(f32_to_bf16_bits(o[2] * inv), f32_to_bf16_bits(o[3] * inv)));
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void finish_segment(const DecodeArgs& a, const Segment& s,
-                                               WaveState<D>& st, long long f0, int wave_id,
-                                               int row, int kg) {
+                                               WaveState<D>& st, long long f0, long long chunk,
+                                               int wave_id, int lane, int row, int kg) {
   constexpr int NDT = Tile<D>::kDimTiles;
   const float l = st.total_l();
-  if (row >= a.group) return;
   const bool complete = s.fs == s.ps && s.fe == s.ps + s.nb;
   if (complete) {
-    const float inv = 1.f / l;
-    bf16_t* o = (bf16_t*)a.out +
-                ((size_t)s.b * a.num_q_heads + (size_t)s.kvh * a.group + row) * D + kg * 4;
+    if (row < a.group) {
+      const float inv = 1.f / l;
+      bf16_t* o = (bf16_t*)a.out +
+                  ((size_t)s.b * a.num_q_heads + (size_t)s.kvh * a.group + row) * D + kg * 4;
 #pragma unroll
-    for (int n = 0; n < NDT; ++n) {
-      const uint2 v = make_uint2(
-          pack_bf16x2(f32_to_bf16_bits(st.acc[n][0] * inv), f32_to_bf16_bits(st.acc[n][1] * inv)),
-          pack_bf16x2(f32_to_bf16_bits(st.acc[n][2] * inv), f32_to_bf16_bits(st.acc[n][3] * inv)));
-      *(uint2*)(o + n * kTile) = v;
+      for (int n = 0; n < NDT; ++n) {
+        const uint2 v = make_uint2(pack_bf16x2(f32_to_bf16_bits(st.acc[n][0] * inv),
+                                               f32_to_bf16_bits(st.acc[n][1] * inv)),
+                                   pack_bf16x2(f32_to_bf16_bits(st.acc[n][2] * inv),
+                                               f32_to_bf16_bits(st.acc[n][3] * inv)));
+        *(uint2*)(o + n * kTile) = v;
+      }
     }
-  } else {
-    const int slot = 2 * wave_id + (s.fs == f0 ? 0 : 1);
+    return;
+  }
+  const int slot = 2 * wave_id + (s.fs == f0 ? 0 : 1);
+  if (row < a.group) {
     const size_t r = (size_t)slot * a.group + row;
     float* o = a.ws_o + r * D + kg * 4;
 #pragma unroll
-    for (int n = 0; n < NDT; ++n) *(float4_t*)(o + n * kTile) = st.acc[n];
+    for (int n = 0; n < NDT; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) put_coherent(o + n * kTile + e, st.acc[n][e]);
     if (kg == 0) {
-      a.ws_m[r] = st.m;
-      a.ws_l[r] = l;
+      put_coherent(a.ws_m + r, st.m);
+      put_coherent(a.ws_l + r, l);
     }
+  }
+  // Publish the piece, then count it; the wave that brings the count to the
+  // number of pieces merges them all and rearms the counter for the next
+  // call. No wave ever waits for another.
+  wait_stores_complete();
+  const Pieces pc(s.ps, s.nb, chunk);
+  int* cnt = a.ws_cnt + (size_t)s.b * a.num_kv_heads + s.kvh;
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, 64);
+  if (old == pc.v1 - pc.v0) {
+    merge_pieces<D>(a, s.b, s.kvh, pc, lane);
+    if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -442,7 +555,7 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
     }
     st.block(tc, qb, min(kBlockTokens, cur.L - cur.j * kBlockTokens), a.scale_log2, kg);
     if (seg_end) {
-      finish_segment<D>(a, cur, st, f0, wave_id, row, kg);
+      finish_segment<D>(a, cur, st, f0, chunk, wave_id, lane, row, kg);
       st.reset();
 #pragma unroll
       for (int c = 0; c < Tile<D>::kQkSteps; ++c) qb[c] = qn[c];
@@ -450,53 +563,6 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
     if (!more) break;
     cur = nx;
     tc = tn;
-  }
-}
-
-// Merges the pieces of every (sequence, KV head) pair that the balanced
-// split cut: piece k of a pair starting at flat index s and ending at e came
-// from wave s / chunk + k; the first piece sits in that wave's slot 1 when
-// the wave's range began before s, else slot 0; later pieces are the first
-// segment (slot 0) of their wave. Pieces are merged in order.
-template <int D>
-__global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(DecodeArgs a) {
-  extern __shared__ int prefix[];
-  __shared__ int scan_scratch[kWaves];
-  const int B = a.num_seqs;
-  const int Hkv = a.num_kv_heads;
-  const int G = a.group;
-  build_partition_prefix(a.seq_lens, B, kBlockTokens, prefix, scan_scratch);
-  const long long total = (long long)Hkv * prefix[B];
-  const long long chunk = balanced_chunk(total, a.split_waves, a.min_seg_blocks);
-  for (int pi = blockIdx.x; pi < B * Hkv; pi += gridDim.x) {
-    const int b = pi / Hkv;
-    const int kvh = pi - b * Hkv;
-    const int nb = prefix[b + 1] - prefix[b];
-    if (nb == 0) continue;
-    const long long s = (long long)Hkv * prefix[b] + (long long)kvh * nb;
-    const long long e = s + nb;
-    const int v0 = (int)(s / chunk);
-    const int v1 = (int)((e - 1) / chunk);
-    if (v0 == v1) continue;  // finished in place
-    const int first_slot = 2 * v0 + ((long long)v0 * chunk < s ? 1 : 0);
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-      const int g = idx / D;
-      const int d = idx - g * D;
-      float M = -INFINITY;
-      for (int v = v0; v <= v1; ++v) {
-        const int slot = v == v0 ? first_slot : 2 * v;
-        M = fmaxf(M, a.ws_m[(size_t)slot * G + g]);
-      }
-      float lsum = 0.f, o = 0.f;
-      for (int v = v0; v <= v1; ++v) {
-        const size_t r = (size_t)(v == v0 ? first_slot : 2 * v) * G + g;
-        const float f = fast_exp2(a.ws_m[r] - M);
-        lsum = fmaf(a.ws_l[r], f, lsum);
-        o = fmaf(a.ws_o[r * D + d], f, o);
-      }
-      ((bf16_t*)a.out)[((size_t)b * a.num_q_heads + (size_t)kvh * G + g) * D + d].bits =
-          f32_to_bf16_bits(o / lsum);
-    }
   }
 }
 
@@ -516,16 +582,6 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, 
   void* args[] = {&arg};
   return hipLaunchKernel(decode_mfma_fn(head_dim, balanced), dim3(grid), dim3(256), args,
                          (size_t)(a.num_seqs + 1) * sizeof(int), s);
-}
-
-hipError_t launch_decode_balanced_reduce(const DecodeArgs& a, int head_dim, int grid,
-                                         hipStream_t s) {
-  DecodeArgs arg = a;
-  void* args[] = {&arg};
-  const void* fn = head_dim == 64 ? (const void*)&decode_balanced_reduce_kernel<64>
-                                  : (const void*)&decode_balanced_reduce_kernel<128>;
-  return hipLaunchKernel(fn, dim3(grid), dim3(256), args, (size_t)(a.num_seqs + 1) * sizeof(int),
-                         s);
 }
 
 }  // namespace pagedkv

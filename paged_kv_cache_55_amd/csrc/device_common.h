@@ -90,6 +90,7 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   float* ws_o;   // [rows, D]
+  int* ws_cnt;   // balanced split: pieces finished per (b, kvh); zero between calls
   float scale_log2;  // scale * log2(e)
   int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, part_tokens, num_parts;
   int split_waves;     // balanced split: waves of the decode grid (4 per workgroup)

@@ -15,8 +15,6 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int 
                               hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, int grid,
                               hipStream_t s);
-hipError_t launch_decode_balanced_reduce(const DecodeArgs& a, int head_dim, int grid,
-                                         hipStream_t s);
 const void* decode_valu_fn(int dtype, int head_dim, int group);
 const void* decode_mfma_fn(int head_dim, bool balanced);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);

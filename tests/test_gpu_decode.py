@@ -249,6 +249,23 @@ def test_kernels_agree_within_tolerance():
     compare(gpu_out_f64(b), ref, c.seq_lens.numpy(), "bf16")
 
 
+def test_workspace_reuse_across_calls():
+    """The balanced split's counters return to zero: one workspace serves a
+    sequence of different batches."""
+    cases = [wl.random_case(500 + i, 7, 32, 8, 128, "bf16", max_len=3000) for i in range(3)]
+    refs = [oracle_step(c)[0] for c in cases]
+    dims = pk.make_dims(7, 32, 8, 128, max(c.max_blocks_per_seq for c in cases),
+                        max(c.num_blocks for c in cases), pk.PA_BF16, 0, "mfma")
+    ws = torch.zeros(pk.pa_decode_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        for c, ref in zip(cases, refs):
+            d = c.to("cuda")
+            out = pk.pa_decode(d.q, d.k_pool, d.v_pool, d.block_tables, d.seq_lens, c.scale,
+                               partition_tokens=0, kernel="mfma", workspace=ws)
+            torch.cuda.synchronize()
+            compare(gpu_out_f64(out), ref, c.seq_lens.numpy(), "bf16")
+
+
 def test_abi_error_reaches_python():
     c = wl.random_case(302, 2, 8, 2, 64, "bf16", max_len=600).to("cuda")
     with pytest.raises(pk.PagedKVError):
