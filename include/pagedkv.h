@@ -97,7 +97,7 @@ typedef struct {
  *   unnormalised output) of every (sequence, query head, partition).
  *   Balanced split (matrix-core kernel, partition_tokens == 0): int32 piece
  *   counters for every (sequence, KV head), then fp32 partials for two
- *   pieces per wave of the decode grid (at most 4096 waves).
+ *   pieces per wave of the decode grid (at most 1024 waves).
  * The workspace must be zero-filled before its first use; every pa_decode
  * call leaves it zero where it must be (the counters), so it can be reused
  * without clearing. Calls that may overlap in time need separate
@@ -114,9 +114,10 @@ size_t pa_decode_workspace_bytes(const pa_dims* dims);
  * split: every wave of a persistent grid streams an equal share of all
  * blocks and the last wave to finish a cut sequence merges its pieces.
  * Results do not depend on timing: pieces merge in a fixed order.
- * Rows with seq_lens[b] == 0 get zeros. Slots at or past seq_lens[b] and
- * table entries at or past ceil(seq_lens[b] / 16) are never read, so they
- * may hold anything (NaN included). bf16 output is rounded to nearest even.
+ * Rows with seq_lens[b] == 0 get zeros. Slots at or past seq_lens[b] never
+ * reach the result (they are masked, so they may hold anything, NaN
+ * included), and table entries at or past ceil(seq_lens[b] / 16) are never
+ * read. bf16 output is rounded to nearest even.
  * `workspace` may be NULL when pa_decode_workspace_bytes() is 0. */
 pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, const int32_t* seq_lens,

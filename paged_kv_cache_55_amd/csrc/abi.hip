@@ -39,8 +39,11 @@ int pick_kernel(const pa_dims* d) {
 }
 
 // Balanced split: at most this many decode workgroups (4 waves each); the
-// workspace holds two partial slots per wave.
-constexpr int kMaxBalancedGrid = 1024;
+// workspace holds two partial slots per wave. One workgroup per compute unit
+// (256 on MI355X) streams faster than two: each wave's range is twice as
+// long, so fewer pairs are cut, and the wave's own two-tile prefetch already
+// keeps enough loads in flight.
+constexpr int kMaxBalancedGrid = 256;
 constexpr int kMinSegBlocks = 16;
 
 struct Plan {
@@ -74,12 +77,12 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
   if (p->balanced) {
     p->part_tokens = max_tokens;
     p->num_parts = 1;
-    const size_t rows = (size_t)2 * 4 * kMaxBalancedGrid * G;
+    // counters, then one record per piece slot (two per wave): O^T, m, l
+    const size_t slots = (size_t)2 * 4 * kMaxBalancedGrid;
     p->off_cnt = 0;
-    p->off_m = align_up((size_t)d->num_seqs * d->num_kv_heads * sizeof(int));
-    p->off_l = p->off_m + align_up(rows * sizeof(float));
-    p->off_o = p->off_l + align_up(rows * sizeof(float));
-    p->ws_bytes = p->off_o + rows * (size_t)d->head_dim * sizeof(float);
+    p->off_o = align_up((size_t)d->num_seqs * d->num_kv_heads * sizeof(int));
+    p->off_m = p->off_l = 0;
+    p->ws_bytes = p->off_o + slots * G * (size_t)(d->head_dim + 2) * sizeof(float);
     return PA_OK;
   }
   const int part = (d->partition_tokens == 0 || d->partition_tokens >= max_tokens)
@@ -156,8 +159,8 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.seq_lens = seq_lens;
   a.out = out;
   char* ws = (char*)workspace;
-  a.ws_m = plan.ws_bytes ? (float*)(ws + plan.off_m) : nullptr;
-  a.ws_l = plan.ws_bytes ? (float*)(ws + plan.off_l) : nullptr;
+  a.ws_m = plan.ws_bytes && !plan.balanced ? (float*)(ws + plan.off_m) : nullptr;
+  a.ws_l = plan.ws_bytes && !plan.balanced ? (float*)(ws + plan.off_l) : nullptr;
   a.ws_o = plan.ws_bytes ? (float*)(ws + plan.off_o) : nullptr;
   a.ws_cnt = plan.balanced ? (int*)(ws + plan.off_cnt) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -175,7 +178,9 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   const void* fn = plan.kernel == PA_KERNEL_MFMA
                        ? decode_mfma_fn(dims->head_dim, plan.balanced)
                        : decode_valu_fn(dims->dtype, dims->head_dim, a.group);
-  const size_t smem = (size_t)(dims->num_seqs + 1) * sizeof(int);
+  const size_t smem = plan.kernel == PA_KERNEL_MFMA
+                          ? decode_mfma_smem(dims->num_seqs, a.group, dims->head_dim, plan.balanced)
+                          : (size_t)(dims->num_seqs + 1) * sizeof(int);
   int resident = 0;
   hipError_t e = resident_workgroups(fn, smem, &resident);
   if (e != hipSuccess) return PA_ERR_LAUNCH;

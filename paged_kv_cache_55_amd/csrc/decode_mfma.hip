@@ -35,8 +35,9 @@
 //             contiguous range of them, prefetching across pair boundaries.
 //             A pair whose blocks lie inside one wave's range is finished
 //             in place; a pair cut by range boundaries leaves one fp32
-//             partial per piece, and the wave that completes the last piece
-//             (an atomic count per pair) merges them: one kernel, no reduce
+//             partial per piece. After its stream a wave counts its (at most
+//             two) pieces, and the wave that completes a pair's count (an
+//             atomic per pair) merges its pieces: one kernel, no reduce
 //             pass.
 #include "launch.h"
 #include "worklist.h"
@@ -69,15 +70,58 @@ struct Tile {
   short4_t v[kDimTiles];                    // this lane's 4-token V pieces
 };
 
+// Buffer resource of one wave-uniform memory range: the base sits in
+// scalar registers and every lane addresses it through a fixed 32-bit byte
+// offset, so a new tile costs a few scalar instructions and no per-lane
+// 64-bit address arithmetic. Reads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int bytes) {
+  constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, raw (unswizzled) access
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+// Per-lane byte offsets of the tile operands, fixed for a kernel.
+template <int D>
+struct LaneOffsets {
+  int k;  // K tile: token row, 8 dims at kg * 8 (+ 64 bytes per 32-dim step)
+  int v;  // V^T tile: dim row, 4 tokens at kg * 4 (+ 512 bytes per 16-dim tile)
+  __device__ __forceinline__ LaneOffsets(int row, int kg)
+      : k((row * D + kg * 8) * 2), v((row * kBlockTokens + kg * 4) * 2) {}
+};
+
 template <int D>
 __device__ __forceinline__ void load_tile(Tile<D>& tl, const bf16_t* kt, const bf16_t* vt,
-                                          int row, int kg) {
+                                          const LaneOffsets<D>& lo) {
+  constexpr int kTileBytes = kBlockTokens * D * 2;
+  const __amdgpu_buffer_rsrc_t kr = range_rsrc(kt, kTileBytes);
+  const __amdgpu_buffer_rsrc_t vr = range_rsrc(vt, kTileBytes);
 #pragma unroll
   for (int c = 0; c < Tile<D>::kQkSteps; ++c)
-    tl.k[c] = *(const bf16x8_t*)(kt + row * D + c * 32 + kg * 8);
+    tl.k[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kr, lo.k + c * 64, 0, 0));
 #pragma unroll
   for (int n = 0; n < Tile<D>::kDimTiles; ++n)
-    tl.v[n] = *(const short4_t*)(vt + (n * kTile + row) * kBlockTokens + kg * 4);
+    tl.v[n] = __builtin_bit_cast(short4_t, __builtin_amdgcn_raw_buffer_load_b64(vr, lo.v + n * kTile * kBlockTokens * 2, 0, 0));
+}
+
+// Q^T operand of one (sequence, KV head), branch-free: column g = row for
+// g < G; the padded columns g >= G repeat head G - 1. Their scores and
+// outputs land in MFMA columns that are never written out, so they only
+// need to be finite.
+template <int D>
+__device__ __forceinline__ void load_q_clamped(bf16x8_t (&qb)[Tile<D>::kQkSteps],
+                                               const DecodeArgs& a, int b, int kvh, int qoff) {
+  const bf16_t* qp =
+      (const bf16_t*)a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * a.group) * D;
+  const __amdgpu_buffer_rsrc_t qr = range_rsrc(qp, a.group * D * 2);
+#pragma unroll
+  for (int c = 0; c < Tile<D>::kQkSteps; ++c)
+    qb[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + c * 64, 0, 0));
+}
+
+// Byte offset of this lane's Q^T elements within its pair's G heads.
+template <int D>
+__device__ __forceinline__ int q_lane_offset(int group, int row, int kg) {
+  const int g = row < group ? row : group - 1;
+  return (g * D + kg * 8) * 2;
 }
 
 // Q^T operand of one (sequence, KV head): column g = row, zero for g >= G.
@@ -216,25 +260,34 @@ __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, 
 
   const bf16_t* kbase = (const bf16_t*)a.k_pool;
   const bf16_t* vbase = (const bf16_t*)a.v_pool;
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + tok0 / kBlockTokens;
+  const size_t bt_row = (size_t)b * a.max_blocks + tok0 / kBlockTokens;
   const size_t tile_elems = (size_t)kBlockTokens * D;
   const size_t block_stride = (size_t)a.num_kv_heads * tile_elems;
   const size_t head_off = (size_t)kvh * tile_elems;
 
-  Tile<D> cur, nxt;
+  // ping-pong over two register tiles: the loads of block i + 4 are in
+  // flight while block i is computed
+  const LaneOffsets<D> lo(row, kg);
+  Tile<D> ta, tb;
   int i = w;
   if (i < nblk) {
-    const size_t base = (size_t)bt[i] * block_stride + head_off;
-    load_tile<D>(cur, kbase + base, vbase + base, row, kg);
+    const size_t base = (size_t)uniform_load(a.block_tables, bt_row + i) * block_stride + head_off;
+    load_tile<D>(ta, kbase + base, vbase + base, lo);
   }
-  for (; i < nblk; i += kWaves) {
+  auto step = [&](Tile<D>& cur, Tile<D>& nxt) {
     const int inext = i + kWaves;
     if (inext < nblk) {
-      const size_t base = (size_t)bt[inext] * block_stride + head_off;
-      load_tile<D>(nxt, kbase + base, vbase + base, row, kg);
+      const size_t base =
+          (size_t)uniform_load(a.block_tables, bt_row + inext) * block_stride + head_off;
+      load_tile<D>(nxt, kbase + base, vbase + base, lo);
     }
     st.block(cur, qb, min(kBlockTokens, tok_end - (tok0 + i * kBlockTokens)), a.scale_log2, kg);
-    cur = nxt;
+    i = inext;
+  };
+  while (i < nblk) {
+    step(ta, tb);
+    if (i >= nblk) break;
+    step(tb, ta);
   }
 
   // merge the 4 waves through LDS
@@ -294,7 +347,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int j = item / Hkv;
     const int kvh = item - j * Hkv;
     const int b = find_sequence(prefix, B, j);
-    fixed_item<D>(a, b, kvh, j - prefix[b], a.seq_lens[b], red_m, red_l, red_o);
+    const int bu = __builtin_amdgcn_readfirstlane(b);
+    fixed_item<D>(a, bu, kvh, j - prefix[bu], uniform_load(a.seq_lens, bu), red_m, red_l, red_o);
   }
 }
 
@@ -321,7 +375,7 @@ __device__ __forceinline__ Segment locate(const int* prefix, const int32_t* seq_
   s.b = __builtin_amdgcn_readfirstlane(find_sequence(prefix, B, (int)(f / Hkv)));
   const long long base = (long long)Hkv * prefix[s.b];
   s.nb = __builtin_amdgcn_readfirstlane(prefix[s.b + 1] - prefix[s.b]);
-  s.L = seq_lens[s.b];
+  s.L = uniform_load(seq_lens, s.b);
   const long long r = f - base;
   s.kvh = __builtin_amdgcn_readfirstlane((int)(r / s.nb));
   s.j = __builtin_amdgcn_readfirstlane((int)(r - (long long)s.kvh * s.nb));
@@ -344,7 +398,7 @@ __device__ __forceinline__ Segment next_segment(const Segment& c, const int* pre
     s.b = __builtin_amdgcn_readfirstlane(b);
     s.kvh = 0;
     s.nb = __builtin_amdgcn_readfirstlane(prefix[s.b + 1] - prefix[s.b]);
-    s.L = seq_lens[b];
+    s.L = uniform_load(seq_lens, s.b);
   }
   s.j = 0;
   s.ps = c.fe;
@@ -387,73 +441,126 @@ __device__ __forceinline__ void wait_stores_complete() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+}  // namespace
+
+// LDS floats per wave of the balanced kernel: two parked pieces.
+__host__ __device__ int balanced_wave_floats(int group, int head_dim) {
+  return 2 * group * (head_dim + 2);
+}
+
+namespace {
+
+// Workspace record of one piece: O^T in accumulator order (element
+// (t = 4 n + r, kg, g) at (4 t + kg) G + g), then m[G], then l[G].
+template <int D>
+__device__ __forceinline__ size_t piece_record(int slot, int G) {
+  return (size_t)slot * G * (D + 2);
+}
+
 // One wave merges every piece of pair (b, kvh), in piece order, and writes
-// the bf16 output. Lane work unit: 4 consecutive dims of one head. The loads
-// of up to kBatch pieces are issued together so a merge costs one or two
-// memory round trips instead of one per piece.
+// the bf16 output; it runs after the wave's own stream, when the tile
+// registers are free. Work unit: 4 consecutive dims d = 16 n + 4 kg + r of
+// one head. For kUnits units per lane and kBatch pieces at a time, the
+// pieces' (m, l) and outputs are loaded in one round and folded into a
+// running (M, L, O) with the same rescaling as the online softmax, so a
+// merge of up to kBatch pieces costs one memory round trip.
 template <int D>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int b, int kvh,
                                              const Pieces& pc, int lane) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 4;
+  constexpr int kUnits = 2;
   const int G = a.group;
   const int n = pc.v1 - pc.v0 + 1;
+  const float* rec = a.ws_o;
   bf16_t* out = (bf16_t*)a.out + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * D;
-  for (int c = lane; c < G * D / 4; c += 64) {
-    const int g = c * 4 / D;
-    const int d0 = c * 4 - g * D;
-    float M = -INFINITY;
-    if (n > kBatch) {  // long pairs: find the max first
-      for (int p0 = 0; p0 < n; p0 += kBatch) {
-        float mb[kBatch];
+  const int units = G * D / 4;
+  for (int u0 = lane; u0 < units; u0 += 64 * kUnits) {
+    int g[kUnits], n16[kUnits], kq[kUnits];
+    float M[kUnits], L[kUnits], O[kUnits][4];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-          mb[i] = p0 + i < n ? get_coherent(a.ws_m + (size_t)pc.slot(pc.v0 + p0 + i) * G + g)
-                             : -INFINITY;
+    for (int h = 0; h < kUnits; ++h) {
+      const int u = min(u0 + 64 * h, units - 1);
+      g[h] = u / (D / 4);
+      const int q = u - g[h] * (D / 4);  // 4-dim quad of the head: d = 4 q
+      n16[h] = q >> 2;
+      kq[h] = q & 3;
+      M[h] = -INFINITY;
+      L[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) M = fmaxf(M, mb[i]);
-      }
+      for (int r = 0; r < 4; ++r) O[h][r] = 0.f;
     }
-    float lsum = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
     for (int p0 = 0; p0 < n; p0 += kBatch) {
-      float mb[kBatch], lb[kBatch], ob[kBatch][4];
+      float mb[kUnits][kBatch], lb[kUnits][kBatch], ob[kUnits][kBatch][4];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        if (p0 + i < n) {
-          const size_t r = (size_t)pc.slot(pc.v0 + p0 + i) * G + g;
-          mb[i] = get_coherent(a.ws_m + r);
-          lb[i] = get_coherent(a.ws_l + r);
+        const float* pr = rec + piece_record<D>(pc.slot(pc.v0 + min(p0 + i, n - 1)), G);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ob[i][e] = get_coherent(a.ws_o + r * D + d0 + e);
-        } else {
-          mb[i] = -INFINITY;
-          lb[i] = 0.f;
+        for (int h = 0; h < kUnits; ++h) {
+          mb[h][i] = p0 + i < n ? get_coherent(pr + G * D + g[h]) : -INFINITY;
+          lb[h][i] = get_coherent(pr + G * D + G + g[h]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ob[i][e] = 0.f;
+          for (int r = 0; r < 4; ++r)
+            ob[h][i][r] = get_coherent(pr + ((size_t)(n16[h] * 4 + r) * 4 + kq[h]) * G + g[h]);
         }
       }
-      if (n <= kBatch) {
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) M = fmaxf(M, mb[i]);
-      }
+      for (int h = 0; h < kUnits; ++h) {
+        float Mn = M[h];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const float f = fast_exp2(mb[i] - M);  // absent pieces: 2^-inf = 0
-        lsum = fmaf(lb[i], f, lsum);
+        for (int i = 0; i < kBatch; ++i) Mn = fmaxf(Mn, mb[h][i]);
+        const float alpha = fast_exp2(M[h] - Mn);  // 0 before the first batch
+        L[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = fmaf(ob[i][e], f, o[e]);
+        for (int r = 0; r < 4; ++r) O[h][r] *= alpha;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const float f = fast_exp2(mb[h][i] - Mn);  // absent pieces: 2^-inf = 0
+          L[h] = fmaf(lb[h][i], f, L[h]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[h][r] = fmaf(ob[h][i][r], f, O[h][r]);
+        }
+        M[h] = Mn;
       }
     }
-    const float inv = 1.f / lsum;
-    *(uint2*)(out + (size_t)g * D + d0) =
-        make_uint2(pack_bf16x2(f32_to_bf16_bits(o[0] * inv), f32_to_bf16_bits(o[1] * inv)),
-                   pack_bf16x2(f32_to_bf16_bits(o[2] * inv), f32_to_bf16_bits(o[3] * inv)));
+#pragma unroll
+    for (int h = 0; h < kUnits; ++h) {
+      if (u0 + 64 * h >= units) continue;
+      const float inv = 1.f / L[h];
+      *(uint2*)(out + (size_t)g[h] * D + n16[h] * 16 + kq[h] * 4) =
+          make_uint2(pack_bf16x2(f32_to_bf16_bits(O[h][0] * inv), f32_to_bf16_bits(O[h][1] * inv)),
+                     pack_bf16x2(f32_to_bf16_bits(O[h][2] * inv), f32_to_bf16_bits(O[h][3] * inv)));
+    }
   }
 }
 
+// Partial of one piece in accumulator order: element (t = 4 n + r, kg, g)
+// of O^T at ((t * 4) + kg) * G + g, then m[G], then l[G]. During the stream
+// pieces are parked in the wave's LDS area and copied to the workspace only
+// after it: vector memory operations retire in order, so a store issued
+// mid-stream would hold up the wait for the next prefetched tile until the
+// store had reached memory.
 template <int D>
-__device__ __forceinline__ void finish_segment(const DecodeArgs& a, const Segment& s,
-                                               WaveState<D>& st, long long f0, long long chunk,
-                                               int wave_id, int lane, int row, int kg) {
+__device__ __forceinline__ void park_piece(float* dst, const WaveState<D>& st, float l, int G,
+                                           int row, int kg) {
+  constexpr int NDT = Tile<D>::kDimTiles;
+  if (row >= G) return;
+#pragma unroll
+  for (int n = 0; n < NDT; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[((n * 4 + r) * 4 + kg) * G + row] = st.acc[n][r];
+  if (kg == 0) {
+    dst[G * D + row] = st.m;
+    dst[G * D + G + row] = l;
+  }
+}
+
+// A finished segment: a pair that lies wholly in the wave's range is
+// normalised and written; a piece of a cut pair is parked in LDS as an fp32
+// partial and reported for publishing after the stream.
+template <int D>
+__device__ __forceinline__ bool finish_segment(const DecodeArgs& a, const Segment& s,
+                                               WaveState<D>& st, long long f0, float* park,
+                                               int row, int kg) {
   constexpr int NDT = Tile<D>::kDimTiles;
   const float l = st.total_l();
   const bool complete = s.fs == s.ps && s.fe == s.ps + s.nb;
@@ -471,39 +578,56 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, const Segmen
         *(uint2*)(o + n * kTile) = v;
       }
     }
-    return;
+    return false;
   }
-  const int slot = 2 * wave_id + (s.fs == f0 ? 0 : 1);
-  if (row < a.group) {
-    const size_t r = (size_t)slot * a.group + row;
-    float* o = a.ws_o + r * D + kg * 4;
-#pragma unroll
-    for (int n = 0; n < NDT; ++n)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) put_coherent(o + n * kTile + e, st.acc[n][e]);
-    if (kg == 0) {
-      put_coherent(a.ws_m + r, st.m);
-      put_coherent(a.ws_l + r, l);
-    }
+  // park slot 0: the wave's first segment; slot 1: its last
+  park_piece<D>(park + (s.fs == f0 ? 0 : a.group * (D + 2)), st, l, a.group, row, kg);
+  return true;
+}
+
+// A piece written during the stream, published after it.
+struct PendingPiece {
+  int b, kvh, nb;
+  long long ps;
+};
+
+// After the stream: copy the parked pieces to their workspace records
+// (slot 2 wave + k for the wave's k-th park slot), wait for the stores to
+// complete, then count the wave's pieces; the wave that brings a pair's
+// count to its number of pieces merges it and rearms the counter for the
+// next call. No wave ever waits for another.
+template <int D>
+__device__ __forceinline__ void publish_pieces(const DecodeArgs& a, const PendingPiece& p0,
+                                               const PendingPiece& p1, int npend,
+                                               unsigned parked, long long chunk, int wave_id,
+                                               int lane, float* lds) {
+  const int nf = a.group * (D + 2);
+  for (int k = 0; k < 2; ++k) {
+    if (!(parked & (1u << k))) continue;
+    float* dst = a.ws_o + piece_record<D>(2 * wave_id + k, a.group);
+    const float* src = lds + k * nf;
+    for (int i = lane; i < nf; i += 64) put_coherent(dst + i, src[i]);
   }
-  // Publish the piece, then count it; the wave that brings the count to the
-  // number of pieces merges them all and rearms the counter for the next
-  // call. No wave ever waits for another.
   wait_stores_complete();
-  const Pieces pc(s.ps, s.nb, chunk);
-  int* cnt = a.ws_cnt + (size_t)s.b * a.num_kv_heads + s.kvh;
-  int old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0, 64);
-  if (old == pc.v1 - pc.v0) {
-    merge_pieces<D>(a, s.b, s.kvh, pc, lane);
-    if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int k = 0; k < npend; ++k) {
+    const PendingPiece& pp = k == 0 ? p0 : p1;
+    const Pieces pc(pp.ps, pp.nb, chunk);
+    int* cnt = a.ws_cnt + (size_t)pp.b * a.num_kv_heads + pp.kvh;
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old == pc.v1 - pc.v0) {
+      merge_pieces<D>(a, pp.b, pp.kvh, pc, lane);
+      if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a) {
-  extern __shared__ int prefix[];  // [B + 1]: exclusive prefix of blocks per sequence
+  // dynamic LDS: prefix [B + 1] ints, then per wave an area of
+  // balanced_wave_floats(G, D) floats for two parked pieces
+  extern __shared__ int prefix[];
   __shared__ int scan_scratch[kWaves];
 
   const int B = a.num_seqs;
@@ -527,43 +651,78 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   const size_t block_stride = (size_t)Hkv * tile_elems;
 
   Segment cur = locate(prefix, a.seq_lens, B, Hkv, f0, f1);
-  bf16x8_t qb[Tile<D>::kQkSteps], qn[Tile<D>::kQkSteps];
-  load_q<D>(qb, a, cur.b, cur.kvh, row, kg);
-  Tile<D> tc, tn;
+  auto tile_base = [&](const Segment& sg) {
+    const int32_t phys = uniform_load(a.block_tables, (size_t)sg.b * a.max_blocks + sg.j);
+    return (size_t)phys * block_stride + (size_t)sg.kvh * tile_elems;
+  };
+  // A step's loads: the K and V tiles of a block and the Q^T operand of its
+  // (sequence, KV head) pair (a cache hit except at pair changes). All are
+  // unconditional and branch-free, so the compiler's wait counts can leave
+  // the prefetch in flight.
+  const LaneOffsets<D> lo(row, kg);
+  const int qoff = q_lane_offset<D>(a.group, row, kg);
+  Tile<D> ta, tb;
+  bf16x8_t qa[Tile<D>::kQkSteps], qz[Tile<D>::kQkSteps];
   {
-    const int32_t phys = a.block_tables[(size_t)cur.b * a.max_blocks + cur.j];
-    const size_t base = (size_t)phys * block_stride + (size_t)cur.kvh * tile_elems;
-    load_tile<D>(tc, kbase + base, vbase + base, row, kg);
+    const size_t base = tile_base(cur);
+    load_tile<D>(ta, kbase + base, vbase + base, lo);
+    load_q_clamped<D>(qa, a, cur.b, cur.kvh, qoff);
   }
   WaveState<D> st;
   st.reset();
+  PendingPiece pend0{0, 0, 1, 0}, pend1{0, 0, 1, 0};  // at most two cut pieces per wave
+  int npend = 0;
+  unsigned parked = 0;
+  float* park = (float*)(prefix + ((B + 4) & ~3)) +
+                (size_t)(threadIdx.x >> 6) * balanced_wave_floats(a.group, D);
 
-  for (long long f = f0;; ++f) {
-    const bool more = f + 1 < f1;
-    const bool seg_end = f + 1 == cur.fe;
-    Segment nx = cur;
-    if (more) {
-      if (seg_end) {
-        nx = next_segment(cur, prefix, a.seq_lens, Hkv, f1);
-        load_q<D>(qn, a, nx.b, nx.kvh, row, kg);
-      } else {
-        nx.j = cur.j + 1;
+  // Two register tiles alternate: the loads of block f + 1 are issued before
+  // block f is folded in. After the last block the current block is
+  // requested again (a cache hit that is never used), which keeps the loads
+  // unconditional.
+  long long f = f0;
+  Segment nx = cur;
+  auto prefetch = [&](Tile<D>& dst, bf16x8_t (&qdst)[Tile<D>::kQkSteps], bool more) {
+    if (!more) {
+      nx = cur;
+    } else if (f + 1 == cur.fe) {
+      nx = next_segment(cur, prefix, a.seq_lens, Hkv, f1);
+    } else {
+      nx = cur;
+      nx.j = cur.j + 1;
+    }
+    const size_t base = tile_base(nx);
+    load_tile<D>(dst, kbase + base, vbase + base, lo);
+    load_q_clamped<D>(qdst, a, nx.b, nx.kvh, qoff);
+    // keep the scheduler from sinking these loads below the math on the
+    // current block (it would then reuse the current block's registers)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto fold = [&](Tile<D>& t, const bf16x8_t (&q)[Tile<D>::kQkSteps]) {
+    st.block(t, q, min(kBlockTokens, cur.L - cur.j * kBlockTokens), a.scale_log2, kg);
+    if (f + 1 == cur.fe) {
+      if (finish_segment<D>(a, cur, st, f0, park, row, kg)) {
+        parked |= cur.fs == f0 ? 1u : 2u;
+        const PendingPiece pp{cur.b, cur.kvh, cur.nb, cur.ps};
+        if (npend == 0) pend0 = pp; else pend1 = pp;
+        ++npend;
       }
-      const int32_t phys = a.block_tables[(size_t)nx.b * a.max_blocks + nx.j];
-      const size_t base = (size_t)phys * block_stride + (size_t)nx.kvh * tile_elems;
-      load_tile<D>(tn, kbase + base, vbase + base, row, kg);
-    }
-    st.block(tc, qb, min(kBlockTokens, cur.L - cur.j * kBlockTokens), a.scale_log2, kg);
-    if (seg_end) {
-      finish_segment<D>(a, cur, st, f0, chunk, wave_id, lane, row, kg);
       st.reset();
-#pragma unroll
-      for (int c = 0; c < Tile<D>::kQkSteps; ++c) qb[c] = qn[c];
     }
-    if (!more) break;
     cur = nx;
-    tc = tn;
+    ++f;
+  };
+  while (true) {
+    bool more = f + 1 < f1;
+    prefetch(tb, qz, more);
+    fold(ta, qa);
+    if (!more) break;
+    more = f + 1 < f1;
+    prefetch(ta, qa, more);
+    fold(tb, qz);
+    if (!more) break;
   }
+  publish_pieces<D>(a, pend0, pend1, npend, parked, chunk, wave_id, lane, park);
 }
 
 }  // namespace
@@ -576,12 +735,18 @@ const void* decode_mfma_fn(int head_dim, bool balanced) {
                         : (const void*)&decode_mfma_kernel<128>;
 }
 
+size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced) {
+  if (!balanced) return (size_t)(num_seqs + 1) * sizeof(int);
+  return (size_t)((num_seqs + 4) & ~3) * sizeof(int) +
+         (size_t)4 * balanced_wave_floats(group, head_dim) * sizeof(float);
+}
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, int grid,
                               hipStream_t s) {
   DecodeArgs arg = a;
   void* args[] = {&arg};
   return hipLaunchKernel(decode_mfma_fn(head_dim, balanced), dim3(grid), dim3(256), args,
-                         (size_t)(a.num_seqs + 1) * sizeof(int), s);
+                         decode_mfma_smem(a.num_seqs, a.group, head_dim, balanced), s);
 }
 
 }  // namespace pagedkv

@@ -51,7 +51,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int b, int kvh, i
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.group;
   const int Hq = a.num_q_heads;
   const int h0 = kvh * G;
@@ -87,11 +87,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int b, int kvh, i
   const int c = lane & 3;   // quarter of the row
   const T* kbase = (const T*)a.k_pool;
   const T* vbase = (const T*)a.v_pool;
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + tok0 / kBlockTokens;
+  const size_t bt_row = (size_t)b * a.max_blocks + tok0 / kBlockTokens;
   const size_t tile_elems = (size_t)kBlockTokens * D;
 
   for (int i = w; i < nblk; i += kWaves) {
-    const int phys = bt[i];
+    const int phys = uniform_load(a.block_tables, bt_row + i);
     const size_t tile = ((size_t)phys * a.num_kv_heads + kvh) * tile_elems;
     const T* kt = kbase + tile;
     const T* vt = vbase + tile;
@@ -231,8 +231,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int j = item / Hkv;
     const int kvh = item - j * Hkv;
     const int b = find_sequence(prefix, B, j);
-    const int part = j - prefix[b];
-    valu_item<T, D, GP>(a, b, kvh, part, a.seq_lens[b], sm);
+    const int bu = __builtin_amdgcn_readfirstlane(b);
+    valu_item<T, D, GP>(a, bu, kvh, j - prefix[bu], uniform_load(a.seq_lens, bu), sm);
   }
 }
 

@@ -74,6 +74,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---- uniform reads ---------------------------------------------------------
+
+// Read-only int32 inputs indexed by wave-uniform values (block tables,
+// lengths) are read through the constant address space, which makes them
+// scalar loads: they are counted apart from the vector loads of K/V tiles,
+// so waiting for a table entry never drains the tile prefetch.
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+__device__ __forceinline__ int32_t uniform_load(const int32_t* base, size_t idx) {
+  return ((const const_i32_t*)base)[idx];
+}
+
 // ---- decode arguments ------------------------------------------------------
 
 // Everything a decode kernel needs; passed by value.
@@ -85,11 +97,13 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   void* out;
   // fp32 partials (log2-domain max m, sum of 2^(s - m), unnormalised output):
-  //   fixed split     row (b * Hq + h) * NPmax + partition
-  //   balanced split  row (2 * wave + piece) * G + g
+  //   fixed split     ws_m, ws_l [rows], ws_o [rows, D] with
+  //                   row (b * Hq + h) * NPmax + partition
+  //   balanced split  ws_o holds one record per piece slot (2 * wave + k):
+  //                   O^T in accumulator order, then m[G], then l[G]
   float* ws_m;
   float* ws_l;
-  float* ws_o;   // [rows, D]
+  float* ws_o;
   int* ws_cnt;   // balanced split: pieces finished per (b, kvh); zero between calls
   float scale_log2;  // scale * log2(e)
   int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, part_tokens, num_parts;

@@ -17,6 +17,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, 
                               hipStream_t s);
 const void* decode_valu_fn(int dtype, int head_dim, int group);
 const void* decode_mfma_fn(int head_dim, bool balanced);
+// dynamic LDS bytes of a decode_mfma launch
+size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced);
+__host__ __device__ int balanced_wave_floats(int group, int head_dim);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,

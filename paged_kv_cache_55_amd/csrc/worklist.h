@@ -44,21 +44,24 @@ __device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int
 }
 
 // prefix[0..B] <- exclusive prefix of ceil(L_b / part_tokens) (0 for L_b <= 0).
-// Needs blockDim.x == 256 and B <= kMaxSeqs. Ends with a barrier.
+// Needs blockDim.x == 256 and B <= kMaxSeqs. The lengths are read with
+// coalesced loads into LDS, then each thread scans a contiguous chunk.
+// Ends with a barrier.
 __device__ __forceinline__ void build_partition_prefix(const int32_t* __restrict__ seq_lens, int B,
                                                        int part_tokens, int* prefix,
                                                        int* scratch) {
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const int L = seq_lens[i];
+    prefix[i] = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
+  }
+  __syncthreads();
   const int chunk = (B + 255) / 256;  // <= 16
   const int first = threadIdx.x * chunk;
   int counts[kMaxSeqs / 256];
   int local = 0;
 #pragma unroll
   for (int i = 0; i < kMaxSeqs / 256; ++i) {
-    int c = 0;
-    if (i < chunk && first + i < B) {
-      const int L = seq_lens[first + i];
-      c = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
-    }
+    const int c = (i < chunk && first + i < B) ? prefix[first + i] : 0;
     counts[i] = c;
     local += c;
   }

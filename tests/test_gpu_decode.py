@@ -249,6 +249,17 @@ def test_kernels_agree_within_tolerance():
     compare(gpu_out_f64(b), ref, c.seq_lens.numpy(), "bf16")
 
 
+@pytest.mark.parametrize("lens,hq,hkv", [
+    ([8000], 32, 2),     # G = 16: each pair cut into 32 pieces
+    ([70000], 2, 1),     # one pair cut into > 256 pieces (many merge batches)
+])
+def test_balanced_many_pieces(lens, hq, hkv):
+    c = wl.random_case(450 + hq, len(lens), hq, hkv, 128, "bf16", lens=lens)
+    ref, _, _ = oracle_step(c)
+    out, _, _ = run_step(c, kernel="mfma", partition_tokens=0)
+    compare(gpu_out_f64(out), ref, lens, "bf16")
+
+
 def test_workspace_reuse_across_calls():
     """The balanced split's counters return to zero: one workspace serves a
     sequence of different batches."""
