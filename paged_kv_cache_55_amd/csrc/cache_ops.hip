@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   uint4* pool = blockIdx.y ? v_pool : k_pool;
   const uint4* from = pool + (size_t)src * vecs_per_block;
   uint4* to = pool + (size_t)dst * vecs_per_block;
-  for (size_t j = threadIdx.x; j < vecs_per_block; j += blockDim.x) to[j] = from[j];
+  for (size_t j = threadIdx.x; j < vecs_per_block; j += blockDim.x) to[j] = stream_load16(from + j);
 }
 
 }  // namespace

@@ -104,7 +104,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int b, int kvh, i
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int d0 = ch * 4 * E + c * E;
-      const uint4 raw = *(const uint4*)(kt + (size_t)t * D + d0);
+      const uint4 raw = stream_load16(kt + (size_t)t * D + d0);
       float kf[E];
       Tr::unpack(raw, kf);
 #pragma unroll
@@ -144,7 +144,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int b, int kvh, i
       float vf[kBlockTokens];
 #pragma unroll
       for (int j = 0; j < kBlockTokens / E; ++j) {
-        const uint4 raw = *(const uint4*)(vrow + j * E);
+        const uint4 raw = stream_load16(vrow + j * E);
         Tr::unpack(raw, vf + j * E);
       }
       if (nvalid < kBlockTokens) {

@@ -74,6 +74,17 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---- streaming reads -------------------------------------------------------
+
+// 16 bytes of data that is read once per call (K/V tiles, blocks being
+// copied), with the nontemporal hint so it streams through the caches.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---- uniform reads ---------------------------------------------------------
 
 // Read-only int32 inputs indexed by wave-uniform values (block tables,
