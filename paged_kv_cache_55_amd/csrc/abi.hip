@@ -77,12 +77,12 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
   if (p->balanced) {
     p->part_tokens = max_tokens;
     p->num_parts = 1;
-    // counters, then one record per piece slot (two per wave): O^T, m, l
+    // counters, then one record per piece slot (two per wave): O, m, l
     const size_t slots = (size_t)2 * 4 * kMaxBalancedGrid;
     p->off_cnt = 0;
     p->off_o = align_up((size_t)d->num_seqs * d->num_kv_heads * sizeof(int));
     p->off_m = p->off_l = 0;
-    p->ws_bytes = p->off_o + slots * G * (size_t)(d->head_dim + 2) * sizeof(float);
+    p->ws_bytes = p->off_o + slots * (size_t)piece_floats(G, d->head_dim) * sizeof(float);
     return PA_OK;
   }
   const int part = (d->partition_tokens == 0 || d->partition_tokens >= max_tokens)

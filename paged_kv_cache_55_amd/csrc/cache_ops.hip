@@ -10,27 +10,40 @@ namespace pagedkv {
 
 namespace {
 
-// One workgroup per new token; threads stride over (kv head, dim).
+// One wave per (new token, KV head), four per workgroup. The K row (D
+// contiguous elements) moves as 16-byte vectors on the first
+// D * sizeof(W) / 16 lanes; the V column (one element per dim, 16 elements
+// apart) on all lanes, D / 64 elements each. All loads are issued before
+// the slot is known, so the copy costs one memory round trip.
 template <typename W>
 __global__ __launch_bounds__(256) void write_kv_kernel(const W* __restrict__ k_new,
                                                        const W* __restrict__ v_new,
                                                        const int32_t* __restrict__ slots,
                                                        W* __restrict__ k_pool,
-                                                       W* __restrict__ v_pool, int hkv, int d) {
-  const int t = blockIdx.x;
-  const int s = slots[t];
-  if (s < 0) return;
-  const int blk = s / kBlockTokens;
-  const int off = s % kBlockTokens;
-  const int n = hkv * d;
-  const W* kn = k_new + (size_t)t * n;
-  const W* vn = v_new + (size_t)t * n;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int h = i / d;
-    const int c = i - h * d;
+                                                       W* __restrict__ v_pool, int num_tokens,
+                                                       int hkv, int d) {
+  constexpr int kPerVec = 16 / sizeof(W);
+  const int lane = threadIdx.x & 63;
+  const int kvec = d / kPerVec;  // <= 32
+  const long long npairs = (long long)num_tokens * hkv;
+  const long long stride = (long long)gridDim.x * 4;
+  for (long long p = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); p < npairs; p += stride) {
+    const int t = (int)(p / hkv);
+    const int h = (int)(p - (long long)t * hkv);
+    const size_t src = (size_t)p * d;  // k_new / v_new [t, h, :]
+    uint4 kv = make_uint4(0, 0, 0, 0);
+    if (lane < kvec) kv = *(const uint4*)(k_new + src + lane * kPerVec);
+    W vv[2];
+    vv[0] = v_new[src + lane];
+    if (d > 64) vv[1] = v_new[src + 64 + lane];
+    const int s = uniform_load(slots, t);
+    if (s < 0) continue;
+    const int blk = s / kBlockTokens;
+    const int off = s - blk * kBlockTokens;
     const size_t tile = ((size_t)blk * hkv + h) * (size_t)(kBlockTokens * d);
-    k_pool[tile + (size_t)off * d + c] = kn[i];
-    v_pool[tile + (size_t)c * kBlockTokens + off] = vn[i];
+    if (lane < kvec) *(uint4*)(k_pool + tile + (size_t)off * d + lane * kPerVec) = kv;
+    v_pool[tile + (size_t)lane * kBlockTokens + off] = vv[0];
+    if (d > 64) v_pool[tile + (size_t)(64 + lane) * kBlockTokens + off] = vv[1];
   }
 }
 
@@ -53,20 +66,23 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,
                            int num_tokens, void* k_pool, void* v_pool, int num_kv_heads,
                            int head_dim, int elem_bytes, hipStream_t s) {
-  dim3 grid(num_tokens), block(256);
+  // four (token, head) pairs per workgroup; a grid-stride loop covers the rest
+  const long long pairs = (long long)num_tokens * num_kv_heads;
+  const long long wgs = (pairs + 3) / 4;
+  dim3 grid((unsigned)(wgs < (1 << 16) ? wgs : (1 << 16))), block(256);
   if (elem_bytes == 2) {
     const uint16_t* kn = (const uint16_t*)k_new;
     const uint16_t* vn = (const uint16_t*)v_new;
     uint16_t* kp = (uint16_t*)k_pool;
     uint16_t* vp = (uint16_t*)v_pool;
-    void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_kv_heads, &head_dim};
+    void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_tokens, &num_kv_heads, &head_dim};
     return hipLaunchKernel((const void*)&write_kv_kernel<uint16_t>, grid, block, args, 0, s);
   }
   const uint32_t* kn = (const uint32_t*)k_new;
   const uint32_t* vn = (const uint32_t*)v_new;
   uint32_t* kp = (uint32_t*)k_pool;
   uint32_t* vp = (uint32_t*)v_pool;
-  void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_kv_heads, &head_dim};
+  void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_tokens, &num_kv_heads, &head_dim};
   return hipLaunchKernel((const void*)&write_kv_kernel<uint32_t>, grid, block, args, 0, s);
 }
 

@@ -436,80 +436,72 @@ struct Pieces {
 };
 
 // Partials cross workgroups on different XCDs, whose L2 caches are not
-// coherent with each other. They are written and read with agent-scope
-// relaxed atomic accesses (coherent at the device level without flushing or
-// invalidating the whole L2), and the writer waits for its stores to
-// complete before it counts its piece.
-__device__ __forceinline__ void put_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// coherent with each other. Records of cut pieces are written and read 16
+// bytes at a time with the cache policy that agent-scope relaxed atomics
+// use (sc1: coherent at the device level without flushing or invalidating
+// the whole L2), and the writer waits for its stores to complete before it
+// counts its piece. Every access of a record goes through this descriptor.
+constexpr int kCoherent = 16;  // buffer cache policy: sc1
+
 __device__ __forceinline__ void wait_stores_complete() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-}  // namespace
-
-// LDS floats per wave of the balanced kernel: two parked pieces.
-__host__ __device__ int balanced_wave_floats(int group, int head_dim) {
-  return 2 * group * (head_dim + 2);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t records_rsrc(const DecodeArgs& a, int pf) {
+  return range_rsrc(a.ws_o, 2 * a.split_waves * pf * (int)sizeof(float));
 }
 
-namespace {
+// Byte offset of the record of piece slot `slot` (2 * wave + k).
+__device__ __forceinline__ int record_bytes(int slot, int pf) {
+  return slot * pf * (int)sizeof(float);
+}
 
-// Workspace record of one piece: O^T in accumulator order (element
-// (t = 4 n + r, kg, g) at (4 t + kg) G + g), then m[G], then l[G].
-template <int D>
-__device__ __forceinline__ size_t piece_record(int slot, int G) {
-  return (size_t)slot * G * (D + 2);
+__device__ __forceinline__ float load_coherent_f32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent));
 }
 
 // One wave merges every piece of pair (b, kvh), in piece order, and writes
 // the bf16 output; it runs after the wave's own stream, when the tile
-// registers are free. Work unit: 4 consecutive dims d = 16 n + 4 kg + r of
-// one head. For kUnits units per lane and kBatch pieces at a time, the
-// pieces' (m, l) and outputs are loaded in one round and folded into a
-// running (M, L, O) with the same rescaling as the online softmax, so a
-// merge of up to kBatch pieces costs one memory round trip.
+// registers are free. Work unit: 4 consecutive dims of one head (one
+// 16-byte piece of a record). For kUnits units per lane and kBatch pieces at
+// a time, the pieces' (m, l) and outputs are loaded in one round and folded
+// into a running (M, L, O) with the same rescaling as the online softmax,
+// so a merge of up to kBatch pieces costs one memory round trip.
 template <int D>
-__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int b, int kvh,
-                                             const Pieces& pc, int lane) {
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, __amdgpu_buffer_rsrc_t rec,
+                                             int pf, int b, int kvh, const Pieces& pc,
+                                             int lane) {
   constexpr int kBatch = 4;
   constexpr int kUnits = 2;
   const int G = a.group;
   const int n = pc.v1 - pc.v0 + 1;
-  const float* rec = a.ws_o;
   bf16_t* out = (bf16_t*)a.out + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * D;
   const int units = G * D / 4;
   for (int u0 = lane; u0 < units; u0 += 64 * kUnits) {
-    int g[kUnits], n16[kUnits], kq[kUnits];
-    float M[kUnits], L[kUnits], O[kUnits][4];
+    int u[kUnits], g[kUnits];
+    float M[kUnits], L[kUnits];
+    float4_t O[kUnits];
 #pragma unroll
     for (int h = 0; h < kUnits; ++h) {
-      const int u = min(u0 + 64 * h, units - 1);
-      g[h] = u / (D / 4);
-      const int q = u - g[h] * (D / 4);  // 4-dim quad of the head: d = 4 q
-      n16[h] = q >> 2;
-      kq[h] = q & 3;
+      u[h] = min(u0 + 64 * h, units - 1);
+      g[h] = u[h] / (D / 4);
       M[h] = -INFINITY;
       L[h] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[h][r] = 0.f;
+      O[h] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
     for (int p0 = 0; p0 < n; p0 += kBatch) {
-      float mb[kUnits][kBatch], lb[kUnits][kBatch], ob[kUnits][kBatch][4];
+      float mb[kUnits][kBatch], lb[kUnits][kBatch];
+      float4_t ob[kUnits][kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        const float* pr = rec + piece_record<D>(pc.slot(pc.v0 + min(p0 + i, n - 1)), G);
+        const int base = record_bytes(pc.slot(pc.v0 + min(p0 + i, n - 1)), pf);
 #pragma unroll
         for (int h = 0; h < kUnits; ++h) {
-          mb[h][i] = p0 + i < n ? get_coherent(pr + G * D + g[h]) : -INFINITY;
-          lb[h][i] = get_coherent(pr + G * D + G + g[h]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            ob[h][i][r] = get_coherent(pr + ((size_t)(n16[h] * 4 + r) * 4 + kq[h]) * G + g[h]);
+          const float m = load_coherent_f32(rec, base + (G * D + g[h]) * 4);
+          mb[h][i] = p0 + i < n ? m : -INFINITY;
+          lb[h][i] = load_coherent_f32(rec, base + (G * D + G + g[h]) * 4);
+          ob[h][i] = __builtin_bit_cast(
+              float4_t, __builtin_amdgcn_raw_buffer_load_b128(rec, base + u[h] * 16, 0, kCoherent));
         }
       }
 #pragma unroll
@@ -519,14 +511,12 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int b, int kvh
         for (int i = 0; i < kBatch; ++i) Mn = fmaxf(Mn, mb[h][i]);
         const float alpha = fast_exp2(M[h] - Mn);  // 0 before the first batch
         L[h] *= alpha;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) O[h][r] *= alpha;
+        O[h] *= alpha;
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
           const float f = fast_exp2(mb[h][i] - Mn);  // absent pieces: 2^-inf = 0
           L[h] = fmaf(lb[h][i], f, L[h]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[h][r] = fmaf(ob[h][i][r], f, O[h][r]);
+          O[h] += ob[h][i] * f;
         }
         M[h] = Mn;
       }
@@ -535,28 +525,26 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int b, int kvh
     for (int h = 0; h < kUnits; ++h) {
       if (u0 + 64 * h >= units) continue;
       const float inv = 1.f / L[h];
-      *(uint2*)(out + (size_t)g[h] * D + n16[h] * 16 + kq[h] * 4) =
+      *(uint2*)(out + (size_t)u[h] * 4) =
           make_uint2(pack_bf16x2(f32_to_bf16_bits(O[h][0] * inv), f32_to_bf16_bits(O[h][1] * inv)),
                      pack_bf16x2(f32_to_bf16_bits(O[h][2] * inv), f32_to_bf16_bits(O[h][3] * inv)));
     }
   }
 }
 
-// Partial of one piece in accumulator order: element (t = 4 n + r, kg, g)
-// of O^T at ((t * 4) + kg) * G + g, then m[G], then l[G]. During the stream
-// pieces are parked in the wave's LDS area and copied to the workspace only
-// after it: vector memory operations retire in order, so a store issued
-// mid-stream would hold up the wait for the next prefetched tile until the
-// store had reached memory.
+// Partial of one piece, in record layout: O[g][d] (this lane's 4 dims
+// 16 n + 4 kg .. + 3 of head `row` are contiguous), then m[G], then l[G].
+// During the stream pieces are parked in the wave's LDS area and copied to
+// the workspace only after it: vector memory operations retire in order, so
+// a store issued mid-stream would hold up the wait for the next prefetched
+// tile until the store had reached memory.
 template <int D>
 __device__ __forceinline__ void park_piece(float* dst, const WaveState<D>& st, float l, int G,
                                            int row, int kg) {
   constexpr int NDT = Tile<D>::kDimTiles;
   if (row >= G) return;
 #pragma unroll
-  for (int n = 0; n < NDT; ++n)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[((n * 4 + r) * 4 + kg) * G + row] = st.acc[n][r];
+  for (int n = 0; n < NDT; ++n) *(float4_t*)(dst + row * D + n * kTile + kg * 4) = st.acc[n];
   if (kg == 0) {
     dst[G * D + row] = st.m;
     dst[G * D + G + row] = l;
@@ -590,7 +578,7 @@ __device__ __forceinline__ bool finish_segment(const DecodeArgs& a, const Segmen
     return false;
   }
   // park slot 0: the wave's first segment; slot 1: its last
-  park_piece<D>(park + (s.fs == f0 ? 0 : a.group * (D + 2)), st, l, a.group, row, kg);
+  park_piece<D>(park + (s.fs == f0 ? 0 : piece_floats(a.group, D)), st, l, a.group, row, kg);
   return true;
 }
 
@@ -602,32 +590,41 @@ struct PendingPiece {
 
 // After the stream: copy the parked pieces to their workspace records
 // (slot 2 wave + k for the wave's k-th park slot), wait for the stores to
-// complete, then count the wave's pieces; the wave that brings a pair's
-// count to its number of pieces merges it and rearms the counter for the
-// next call. No wave ever waits for another.
+// complete, then count the wave's pieces (both counters in one round trip);
+// the wave that brings a pair's count to its number of pieces merges it and
+// rearms the counter for the next call. No wave ever waits for another.
 template <int D>
 __device__ __forceinline__ void publish_pieces(const DecodeArgs& a, const PendingPiece& p0,
                                                const PendingPiece& p1, int npend,
                                                unsigned parked, long long chunk, int wave_id,
-                                               int lane, float* lds) {
-  const int nf = a.group * (D + 2);
+                                               int lane, const float* lds) {
+  const int pf = piece_floats(a.group, D);
+  const __amdgpu_buffer_rsrc_t rec = records_rsrc(a, pf);
   for (int k = 0; k < 2; ++k) {
     if (!(parked & (1u << k))) continue;
-    float* dst = a.ws_o + piece_record<D>(2 * wave_id + k, a.group);
-    const float* src = lds + k * nf;
-    for (int i = lane; i < nf; i += 64) put_coherent(dst + i, src[i]);
+    const int base = record_bytes(2 * wave_id + k, pf);
+    const float4_t* src = (const float4_t*)(lds + k * pf);
+    for (int i = lane; i < pf / 4; i += 64)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, src[i]), rec,
+                                             base + i * 16, 0, kCoherent);
   }
   wait_stores_complete();
+  int* cnt0 = a.ws_cnt + (size_t)p0.b * a.num_kv_heads + p0.kvh;
+  int* cnt1 = a.ws_cnt + (size_t)p1.b * a.num_kv_heads + p1.kvh;
+  int old0 = 0, old1 = 0;
+  if (lane == 0) {
+    if (npend > 0) old0 = __hip_atomic_fetch_add(cnt0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (npend > 1) old1 = __hip_atomic_fetch_add(cnt1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  old0 = __shfl(old0, 0, 64);
+  old1 = __shfl(old1, 0, 64);
   for (int k = 0; k < npend; ++k) {
     const PendingPiece& pp = k == 0 ? p0 : p1;
     const Pieces pc(pp.ps, pp.nb, chunk);
-    int* cnt = a.ws_cnt + (size_t)pp.b * a.num_kv_heads + pp.kvh;
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old == pc.v1 - pc.v0) {
-      merge_pieces<D>(a, pp.b, pp.kvh, pc, lane);
-      if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((k == 0 ? old0 : old1) == pc.v1 - pc.v0) {
+      merge_pieces<D>(a, rec, pf, pp.b, pp.kvh, pc, lane);
+      if (lane == 0)
+        __hip_atomic_store(k == 0 ? cnt0 : cnt1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

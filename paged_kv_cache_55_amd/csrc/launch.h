@@ -19,7 +19,15 @@ const void* decode_valu_fn(int dtype, int head_dim, int group);
 const void* decode_mfma_fn(int head_dim, bool balanced);
 // dynamic LDS bytes of a decode_mfma launch
 size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced);
-__host__ __device__ int balanced_wave_floats(int group, int head_dim);
+// Balanced split: fp32 record of one piece of a (sequence, KV head) pair,
+// O[g][d] (head-major), then m[G], then l[G], padded to 16 bytes.
+__host__ __device__ inline int piece_floats(int group, int head_dim) {
+  return group * head_dim + ((2 * group + 3) & ~3);
+}
+// LDS floats per wave of the balanced kernel: two parked pieces.
+__host__ __device__ inline int balanced_wave_floats(int group, int head_dim) {
+  return 2 * piece_floats(group, head_dim);
+}
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,

@@ -68,11 +68,18 @@ def test_workspace_size(lib):
     align = lambda x: (x + 255) // 256 * 256
     assert pk.pa_decode_workspace_bytes(d) == 2 * align(rows * 4) + rows * 128 * 4
     # balanced split (matrix-core kernel, partition_tokens = 0): int32
-    # counters per (sequence, KV head), then one fp32 record (G x (D + 2))
-    # per piece slot, two slots per wave of at most 256 four-wave workgroups
+    # counters per (sequence, KV head), then one fp32 record (G x D outputs,
+    # G maxima, G sums, padded to 4 floats) per piece slot, two slots per
+    # wave of at most 256 four-wave workgroups
     slots = 2 * 4 * 256
     assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0)) == \
-        align(64 * 8 * 4) + slots * 4 * (128 + 2) * 4
+        align(64 * 8 * 4) + slots * (4 * 128 + 8) * 4
+    # G = 1: 2 floats of (m, l) padded to 4
+    assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0, num_q_heads=8)) == \
+        align(64 * 8 * 4) + slots * (128 + 4) * 4
+    # G = 3: 6 floats padded to 8
+    assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0, num_q_heads=24)) == \
+        align(64 * 8 * 4) + slots * (3 * 128 + 8) * 4
     assert pk.pa_decode_workspace_bytes(dims(partition_tokens=0, kernel="valu")) == 0
     assert pk.pa_decode_workspace_bytes(dims(partition_tokens=4096)) == 0
     assert pk.pa_decode_workspace_bytes(dims(max_blocks_per_seq=32)) == 0

@@ -40,6 +40,18 @@ def test_write_kv_bit_exact(dtype, hkv, d):
     assert bits_equal(kg, k_ref) and bits_equal(vg, v_ref)
 
 
+def test_write_kv_many_tokens():
+    """More (token, head) pairs than one launch covers at once: the kernel's
+    grid-stride loop takes the rest."""
+    k, v, kn, vn, slots = _write_case(11, 2600, 8, 64, "bf16", 40000, skip_every=7)
+    k_ref, v_ref = oracle.write_kv(to_numpy(k), to_numpy(v), to_numpy(kn), to_numpy(vn),
+                                   to_numpy(slots))
+    kg, vg = k.cuda(), v.cuda()
+    pk.pa_write_kv(kn.cuda(), vn.cuda(), slots.cuda(), kg, vg)
+    torch.cuda.synchronize()
+    assert bits_equal(kg, k_ref) and bits_equal(vg, v_ref)
+
+
 def test_write_kv_config2_tokens():
     c = wl.config2()
     k_ref, v_ref = oracle.write_kv(to_numpy(c.k_pool), to_numpy(c.v_pool), to_numpy(c.k_new),
