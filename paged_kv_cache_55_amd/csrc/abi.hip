@@ -129,6 +129,30 @@ hipError_t resident_workgroups(const void* fn, size_t smem, int* out) {
   return hipSuccess;
 }
 
+// Dynamic LDS one workgroup may use on the current device, capped at the
+// 160 KiB of a gfx950 compute unit and less 1 KiB for static LDS; cached
+// per device.
+hipError_t lds_per_workgroup(size_t* out) {
+  static std::mutex mu;
+  static std::map<int, size_t> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  int bytes = 0;
+  e = hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  size_t lim = bytes > 0 ? (size_t)bytes : 65536;
+  if (lim > 160 * 1024) lim = 160 * 1024;
+  *out = cache[dev] = lim - 1024;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,16 +197,27 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.num_parts = plan.num_parts;
   a.split_waves = 0;
   a.min_seg_blocks = 0;
+  a.stage_slots = 0;
 
   hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (plan.balanced) {
+    size_t lds = 0;
+    e = lds_per_workgroup(&lds);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+    a.stage_slots = balanced_stage_slots(dims->num_seqs, a.group, dims->head_dim, lds);
+    if (decode_mfma_smem(dims->num_seqs, a.group, dims->head_dim, true, 0) > lds)
+      return PA_ERR_UNSUPPORTED;  // the work list and parked pieces alone do not fit
+  }
   const void* fn = plan.kernel == PA_KERNEL_MFMA
                        ? decode_mfma_fn(dims->head_dim, plan.balanced)
                        : decode_valu_fn(dims->dtype, dims->head_dim, a.group);
   const size_t smem = plan.kernel == PA_KERNEL_MFMA
-                          ? decode_mfma_smem(dims->num_seqs, a.group, dims->head_dim, plan.balanced)
+                          ? decode_mfma_smem(dims->num_seqs, a.group, dims->head_dim,
+                                             plan.balanced, a.stage_slots)
                           : (size_t)(dims->num_seqs + 1) * sizeof(int);
   int resident = 0;
-  hipError_t e = resident_workgroups(fn, smem, &resident);
+  e = resident_workgroups(fn, smem, &resident);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
   if (plan.balanced) {
     const int grid = resident < kMaxBalancedGrid ? resident : kMaxBalancedGrid;

@@ -551,29 +551,70 @@ __device__ __forceinline__ void park_piece(float* dst, const WaveState<D>& st, f
   }
 }
 
+// Complete outputs staged in the wave's LDS area: `n` bf16 G x D blocks and
+// the pair index (b * Hkv + kvh) of each. Like parked pieces they are
+// written to memory after the stream (a store mid-stream holds up the next
+// tile's wait); outputs beyond the stage's capacity are stored directly.
+struct OutStage {
+  bf16_t* data;
+  int* dest;
+  int n;
+};
+
+// Copies the staged outputs to `out`, 16 bytes per lane and store.
+template <int D>
+__device__ __forceinline__ void flush_outputs(const DecodeArgs& a, OutStage& os, int lane) {
+  wave_lds_sync();
+  const int vecs = a.group * D / 8;
+  for (int k = 0; k < os.n; ++k) {
+    const int pair = __builtin_amdgcn_readfirstlane(os.dest[k]);
+    uint4* dst = (uint4*)((bf16_t*)a.out + (size_t)pair * a.group * D);
+    const uint4* src = (const uint4*)(os.data + (size_t)k * a.group * D);
+    for (int i = lane; i < vecs; i += 64) dst[i] = src[i];
+  }
+  os.n = 0;
+  wave_lds_sync();
+}
+
+// This lane's 4-dim pieces of its head's output, normalised by the
+// denominator `l`, as bf16 at o[16 n], n = 0 .. D / 16 - 1.
+template <int D>
+__device__ __forceinline__ void store_normalised(bf16_t* o, const WaveState<D>& st, float l) {
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int n = 0; n < Tile<D>::kDimTiles; ++n) {
+    const uint2 v = make_uint2(pack_bf16x2(f32_to_bf16_bits(st.acc[n][0] * inv),
+                                           f32_to_bf16_bits(st.acc[n][1] * inv)),
+                               pack_bf16x2(f32_to_bf16_bits(st.acc[n][2] * inv),
+                                           f32_to_bf16_bits(st.acc[n][3] * inv)));
+    *(uint2*)(o + n * kTile) = v;
+  }
+}
+
 // A finished segment: a pair that lies wholly in the wave's range is
-// normalised and written; a piece of a cut pair is parked in LDS as an fp32
-// partial and reported for publishing after the stream.
+// normalised and staged (or written, once the stage is full); a piece
+// of a cut pair is parked in LDS as an fp32 partial and reported for
+// publishing after the stream.
 template <int D>
 __device__ __forceinline__ bool finish_segment(const DecodeArgs& a, const Segment& s,
                                                WaveState<D>& st, long long f0, float* park,
-                                               int row, int kg) {
-  constexpr int NDT = Tile<D>::kDimTiles;
+                                               OutStage& os, int row, int kg) {
   const float l = st.total_l();
   const bool complete = s.fs == s.ps && s.fe == s.ps + s.nb;
   if (complete) {
-    if (row < a.group) {
-      const float inv = 1.f / l;
-      bf16_t* o = (bf16_t*)a.out +
-                  ((size_t)s.b * a.num_q_heads + (size_t)s.kvh * a.group + row) * D + kg * 4;
-#pragma unroll
-      for (int n = 0; n < NDT; ++n) {
-        const uint2 v = make_uint2(pack_bf16x2(f32_to_bf16_bits(st.acc[n][0] * inv),
-                                               f32_to_bf16_bits(st.acc[n][1] * inv)),
-                                   pack_bf16x2(f32_to_bf16_bits(st.acc[n][2] * inv),
-                                               f32_to_bf16_bits(st.acc[n][3] * inv)));
-        *(uint2*)(o + n * kTile) = v;
-      }
+    // two separate store paths keep each pointer's address space known
+    // (LDS or global); a pointer that may be either makes flat stores,
+    // which the compiler can only wait for by draining all memory traffic
+    if (os.n < a.stage_slots) {
+      if (kg == 0 && row == 0) os.dest[os.n] = s.b * a.num_kv_heads + s.kvh;
+      if (row < a.group)
+        store_normalised<D>(os.data + (size_t)os.n * a.group * D + row * D + kg * 4, st, l);
+      ++os.n;
+    } else if (row < a.group) {
+      store_normalised<D>((bf16_t*)a.out +
+                              ((size_t)s.b * a.num_q_heads + (size_t)s.kvh * a.group + row) * D +
+                              kg * 4,
+                          st, l);
     }
     return false;
   }
@@ -590,14 +631,15 @@ struct PendingPiece {
 
 // After the stream: copy the parked pieces to their workspace records
 // (slot 2 wave + k for the wave's k-th park slot), wait for the stores to
-// complete, then count the wave's pieces (both counters in one round trip);
+// complete, then count the wave's pieces (both counters in one round trip,
+// during which the staged complete outputs are written);
 // the wave that brings a pair's count to its number of pieces merges it and
 // rearms the counter for the next call. No wave ever waits for another.
 template <int D>
 __device__ __forceinline__ void publish_pieces(const DecodeArgs& a, const PendingPiece& p0,
                                                const PendingPiece& p1, int npend,
                                                unsigned parked, long long chunk, int wave_id,
-                                               int lane, const float* lds) {
+                                               int lane, const float* lds, OutStage& os) {
   const int pf = piece_floats(a.group, D);
   const __amdgpu_buffer_rsrc_t rec = records_rsrc(a, pf);
   for (int k = 0; k < 2; ++k) {
@@ -616,6 +658,8 @@ __device__ __forceinline__ void publish_pieces(const DecodeArgs& a, const Pendin
     if (npend > 0) old0 = __hip_atomic_fetch_add(cnt0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (npend > 1) old1 = __hip_atomic_fetch_add(cnt1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // staged outputs go out while the counters' round trip is in flight
+  flush_outputs<D>(a, os, lane);
   old0 = __shfl(old0, 0, 64);
   old1 = __shfl(old1, 0, 64);
   for (int k = 0; k < npend; ++k) {
@@ -632,7 +676,8 @@ __device__ __forceinline__ void publish_pieces(const DecodeArgs& a, const Pendin
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a) {
   // dynamic LDS: prefix [B + 1] ints, then per wave an area of
-  // balanced_wave_floats(G, D) floats for two parked pieces
+  // balanced_wave_floats(G, D, stage_slots) floats: two parked pieces, the
+  // staged outputs and their destinations
   extern __shared__ int prefix[];
   __shared__ int scan_scratch[kWaves];
 
@@ -680,7 +725,12 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   int npend = 0;
   unsigned parked = 0;
   float* park = (float*)(prefix + ((B + 4) & ~3)) +
-                (size_t)(threadIdx.x >> 6) * balanced_wave_floats(a.group, D);
+                (size_t)(threadIdx.x >> 6) * balanced_wave_floats(a.group, D, a.stage_slots);
+  OutStage os;
+  os.data = (bf16_t*)(park + 2 * piece_floats(a.group, D));
+  os.dest = (int*)(park + 2 * piece_floats(a.group, D) +
+                   a.stage_slots * staged_output_floats(a.group, D));
+  os.n = 0;
 
   // Two register tiles alternate: the loads of block f + 1 are issued before
   // block f is folded in. After the last block the current block is
@@ -707,7 +757,7 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   auto fold = [&](Tile<D>& t, const bf16x8_t (&q)[Tile<D>::kQkSteps]) {
     st.block(t, q, min(kBlockTokens, cur.L - cur.j * kBlockTokens), a.scale_log2, kg);
     if (f + 1 == cur.fe) {
-      if (finish_segment<D>(a, cur, st, f0, park, row, kg)) {
+      if (finish_segment<D>(a, cur, st, f0, park, os, row, kg)) {
         parked |= cur.fs == f0 ? 1u : 2u;
         const PendingPiece pp{cur.b, cur.kvh, cur.nb, cur.ps};
         if (npend == 0) pend0 = pp; else pend1 = pp;
@@ -728,7 +778,7 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
     fold(tb, qz);
     if (!more) break;
   }
-  publish_pieces<D>(a, pend0, pend1, npend, parked, chunk, wave_id, lane, park);
+  publish_pieces<D>(a, pend0, pend1, npend, parked, chunk, wave_id, lane, park, os);
 }
 
 }  // namespace
@@ -741,10 +791,10 @@ const void* decode_mfma_fn(int head_dim, bool balanced) {
                         : (const void*)&decode_mfma_kernel<128>;
 }
 
-size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced) {
+size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced, int stage_slots) {
   if (!balanced) return (size_t)(num_seqs + 1) * sizeof(int);
   return (size_t)((num_seqs + 4) & ~3) * sizeof(int) +
-         (size_t)4 * balanced_wave_floats(group, head_dim) * sizeof(float);
+         (size_t)4 * balanced_wave_floats(group, head_dim, stage_slots) * sizeof(float);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, int grid,
@@ -752,7 +802,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, 
   DecodeArgs arg = a;
   void* args[] = {&arg};
   return hipLaunchKernel(decode_mfma_fn(head_dim, balanced), dim3(grid), dim3(256), args,
-                         decode_mfma_smem(a.num_seqs, a.group, head_dim, balanced), s);
+                         decode_mfma_smem(a.num_seqs, a.group, head_dim, balanced,
+                                          a.stage_slots), s);
 }
 
 }  // namespace pagedkv

@@ -120,6 +120,7 @@ struct DecodeArgs {
   int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, part_tokens, num_parts;
   int split_waves;     // balanced split: waves of the decode grid (4 per workgroup)
   int min_seg_blocks;  // balanced split: least blocks per wave range
+  int stage_slots;     // balanced split: complete outputs a wave stages in LDS (0 = none)
 };
 
 }  // namespace pagedkv

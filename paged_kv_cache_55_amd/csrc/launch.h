@@ -17,16 +17,33 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, 
                               hipStream_t s);
 const void* decode_valu_fn(int dtype, int head_dim, int group);
 const void* decode_mfma_fn(int head_dim, bool balanced);
-// dynamic LDS bytes of a decode_mfma launch
-size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced);
+// dynamic LDS bytes of a decode_mfma launch (stage_slots: balanced split only)
+size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced, int stage_slots);
 // Balanced split: fp32 record of one piece of a (sequence, KV head) pair,
 // O[g][d] (head-major), then m[G], then l[G], padded to 16 bytes.
 __host__ __device__ inline int piece_floats(int group, int head_dim) {
   return group * head_dim + ((2 * group + 3) & ~3);
 }
-// LDS floats per wave of the balanced kernel: two parked pieces.
-__host__ __device__ inline int balanced_wave_floats(int group, int head_dim) {
-  return 2 * piece_floats(group, head_dim);
+// LDS area of one wave of the balanced kernel, in floats: two parked
+// pieces, then `slots` staged bf16 outputs of G x D, then their destination
+// pair indices (int32, padded to 16 bytes).
+__host__ __device__ inline int staged_output_floats(int group, int head_dim) {
+  return group * head_dim / 2;
+}
+__host__ __device__ inline int balanced_wave_floats(int group, int head_dim, int slots) {
+  return 2 * piece_floats(group, head_dim) + slots * staged_output_floats(group, head_dim) +
+         ((slots + 3) & ~3);
+}
+// Largest number of staged outputs per wave (bounded by kMaxStageSlots) for
+// which a balanced-split workgroup fits `lds_bytes` of LDS.
+constexpr int kMaxStageSlots = 16;
+inline int balanced_stage_slots(int num_seqs, int group, int head_dim, size_t lds_bytes) {
+  for (int slots = kMaxStageSlots; slots > 0; --slots) {
+    const size_t need = (size_t)((num_seqs + 4) & ~3) * sizeof(int) +
+                        (size_t)4 * balanced_wave_floats(group, head_dim, slots) * sizeof(float);
+    if (need <= lds_bytes) return slots;
+  }
+  return 0;
 }
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
 
