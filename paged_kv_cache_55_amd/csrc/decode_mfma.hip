@@ -179,9 +179,7 @@ struct WaveState {
       sv[r] = kg * 4 + r < nvalid ? s[r] * scale_log2 : -INFINITY;
       mloc = fmaxf(mloc, sv[r]);
     }
-    mloc = fmaxf(mloc, shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m, mloc);
+    const float m_new = fmaxf(m, max_over_kg(mloc));
     const float alpha = fast_exp2(m - m_new);
     m = m_new;
     uint16_t ph[4], pl[4];
@@ -220,12 +218,7 @@ struct WaveState {
     }
   }
   // Sum of the denominator over the 4 lanes that share head `row`.
-  __device__ __forceinline__ float total_l() const {
-    float t = l;
-    t += shfl_xor(t, 16);
-    t += shfl_xor(t, 32);
-    return t;
-  }
+  __device__ __forceinline__ float total_l() const { return sum_over_kg(l); }
 };
 
 template <typename T>
@@ -702,20 +695,33 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   const size_t block_stride = (size_t)Hkv * tile_elems;
 
   Segment cur = locate(prefix, a.seq_lens, B, Hkv, f0, f1);
-  auto tile_base = [&](const Segment& sg) {
-    const int32_t phys = uniform_load(a.block_tables, (size_t)sg.b * a.max_blocks + sg.j);
+  auto table_entry = [&](const Segment& sg) {
+    return uniform_load(a.block_tables, (size_t)sg.b * a.max_blocks + sg.j);
+  };
+  auto tile_base = [&](const Segment& sg, int32_t phys) {
     return (size_t)phys * block_stride + (size_t)sg.kvh * tile_elems;
   };
-  // A step's loads: the K and V tiles of a block and the Q^T operand of its
-  // (sequence, KV head) pair (a cache hit except at pair changes). All are
-  // unconditional and branch-free, so the compiler's wait counts can leave
-  // the prefetch in flight.
+  // The position after segment position `sg` (flat index `fpos`), which must
+  // lie before f1: the next block of the pair, else the next pair.
+  auto advance = [&](const Segment& sg, long long fpos) {
+    if (fpos + 1 == sg.fe) return next_segment(sg, prefix, a.seq_lens, Hkv, f1);
+    Segment r = sg;
+    r.j = sg.j + 1;
+    return r;
+  };
+  // A step's loads: the K and V tiles of a block and, when the block starts
+  // a new (sequence, KV head) pair, that pair's Q^T operand. Table entries
+  // are read one block further ahead, so a tile's address never waits for
+  // its table read.
   const LaneOffsets<D> lo(row, kg);
   const int qoff = q_lane_offset<D>(a.group, row, kg);
   Tile<D> ta, tb;
   bf16x8_t qa[Tile<D>::kQkSteps], qz[Tile<D>::kQkSteps];
+  int32_t phys_cur = table_entry(cur);
+  Segment nx = f0 + 1 < f1 ? advance(cur, f0) : cur;
+  int32_t phys_nx = table_entry(nx);
   {
-    const size_t base = tile_base(cur);
+    const size_t base = tile_base(cur, phys_cur);
     load_tile<D>(ta, kbase + base, vbase + base, lo);
     load_q_clamped<D>(qa, a, cur.b, cur.kvh, qoff);
   }
@@ -734,25 +740,27 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
 
   // Two register tiles alternate: the loads of block f + 1 are issued before
   // block f is folded in. After the last block the current block is
-  // requested again (a cache hit that is never used), which keeps the loads
-  // unconditional.
+  // requested again (a cache hit that is never used), which keeps the tile
+  // loads unconditional.
   long long f = f0;
-  Segment nx = cur;
-  auto prefetch = [&](Tile<D>& dst, bf16x8_t (&qdst)[Tile<D>::kQkSteps], bool more) {
-    if (!more) {
-      nx = cur;
-    } else if (f + 1 == cur.fe) {
-      nx = next_segment(cur, prefix, a.seq_lens, Hkv, f1);
-    } else {
-      nx = cur;
-      nx.j = cur.j + 1;
-    }
-    const size_t base = tile_base(nx);
+  Segment nn = nx;
+  int32_t phys_nn = phys_nx;
+  auto prefetch = [&](Tile<D>& dst, bf16x8_t (&qdst)[Tile<D>::kQkSteps],
+                      const bf16x8_t (&qsrc)[Tile<D>::kQkSteps], bool more) {
+    const Segment sg = more ? nx : cur;
+    const size_t base = tile_base(sg, more ? phys_nx : phys_cur);
     load_tile<D>(dst, kbase + base, vbase + base, lo);
-    load_q_clamped<D>(qdst, a, nx.b, nx.kvh, qoff);
+    if (sg.b == cur.b && sg.kvh == cur.kvh) {
+#pragma unroll
+      for (int c = 0; c < Tile<D>::kQkSteps; ++c) qdst[c] = qsrc[c];
+    } else {
+      load_q_clamped<D>(qdst, a, sg.b, sg.kvh, qoff);
+    }
     // keep the scheduler from sinking these loads below the math on the
     // current block (it would then reuse the current block's registers)
     __builtin_amdgcn_sched_barrier(0);
+    nn = f + 2 < f1 ? advance(nx, f + 1) : nx;
+    phys_nn = table_entry(nn);
   };
   auto fold = [&](Tile<D>& t, const bf16x8_t (&q)[Tile<D>::kQkSteps]) {
     st.block(t, q, min(kBlockTokens, cur.L - cur.j * kBlockTokens), a.scale_log2, kg);
@@ -766,15 +774,18 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
       st.reset();
     }
     cur = nx;
+    phys_cur = phys_nx;
+    nx = nn;
+    phys_nx = phys_nn;
     ++f;
   };
   while (true) {
     bool more = f + 1 < f1;
-    prefetch(tb, qz, more);
+    prefetch(tb, qz, qa, more);
     fold(ta, qa);
     if (!more) break;
     more = f + 1 < f1;
-    prefetch(ta, qa, more);
+    prefetch(ta, qa, qz, more);
     fold(tb, qz);
     if (!more) break;
   }

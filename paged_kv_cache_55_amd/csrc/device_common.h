@@ -65,6 +65,34 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// The value of lane l and of lane l ^ 16 (xor16) or l ^ 32 (xor32), lower
+// lane first, in every lane, through the gfx950 permlane swaps: VALU
+// instructions, so unlike LDS-based shuffles they never wait behind
+// outstanding scalar loads.
+__device__ __forceinline__ float2 pair_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 pair_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// max / sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (same in all four)
+__device__ __forceinline__ float max_over_kg(float v) {
+  float2 p = pair_xor16(v);
+  v = fmaxf(p.x, p.y);
+  p = pair_xor32(v);
+  return fmaxf(p.x, p.y);
+}
+__device__ __forceinline__ float sum_over_kg(float v) {
+  float2 p = pair_xor16(v);
+  v = p.x + p.y;
+  p = pair_xor32(v);
+  return p.x + p.y;
+}
+
 // Orders this wave's LDS writes before its later LDS reads (and vice versa)
 // without a workgroup barrier: waves of one workgroup run loops of
 // different trip counts, so only the issuing wave may be synchronised.
