@@ -5,7 +5,10 @@
 
 A step is one pass of the hot path over one batch:
   config 2 (default; Llama-3-8B-shaped layer, B = 64, L ~ U[128, 4096]):
-      pa_write_kv of the 64 new tokens, then pa_decode over all 64 rows;
+      the KV append of the 64 new tokens and pa_decode over all 64 rows,
+      as pa_write_kv then pa_decode (--step separate, the default) or as
+      one pa_decode_append call (--step fused); the line reports the other
+      form's step time too;
   config 4 (Llama-3.3-70B-shaped layer, B = 256, lognormal lengths):
       pa_decode;
   config 5 (8B decode step, 32 layers, bucket B of padded rows):
@@ -51,7 +54,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2, choices=[2, 4, 5])
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--partition", type=int, default=None,
@@ -59,6 +62,8 @@ def parse():
                          "configs 2 and 4, 512 for the 32-layer step)")
     ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--step", default="separate", choices=["fused", "separate"],
+                    help="8B batch: append + decode in one call, or two calls")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget for the oracle baseline (0 = skip)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -162,31 +167,50 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(i, events=None):
-        pre(i)
+    def step(i, events=None, mode=None):
+        mode = mode or args.step
+        fused = mode == "fused" and args.config == 2
+        if not fused:
+            pre(i)
         for (q, k, v, tb, ln, o) in decode_calls(i):
             if events is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part, kernel=kernel,
-                         workspace=ws, stream=stream)
+            if fused:
+                c = copies[i % len(copies)]
+                pk.pa_decode_append(q, c.k_new, c.v_new, c.slot_mapping, k, v, tb, ln, scale, o,
+                                    partition_tokens=part, kernel=kernel, workspace=ws,
+                                    stream=stream)
+            else:
+                pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part, kernel=kernel,
+                             workspace=ws, stream=stream)
             if events is not None:
                 e1.record(stream)
                 events.append((e0, e1))
+
+    def timed_steps(mode):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i, mode=mode)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
 
     # ---------------- timing ----------------
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step = timed_steps(args.step)
+    other_ms = None
+    if args.config == 2:  # the other form of the same step, for comparison
+        other = "separate" if args.step == "fused" else "fused"
+        for i in range(args.warmup):
+            step(i, mode=other)
+        other_ms = timed_steps(other)
 
     # per-call decode durations, measured in a second pass with events
     events = []
@@ -229,6 +253,10 @@ def main():
     value = kv_bytes / sec / 1e9
     table_bytes = int(sum(math.ceil(int(L) / 16) for L in lens_host)) * 4 * (1 if layers == 1 else 1)
     per_call_alg = (kv_bytes / layers) + 2 * B * Hq * D * 2 + table_bytes + 4 * B
+    fused = args.config == 2 and args.step == "fused"
+    if fused:  # the appended tokens: k_new/v_new read, their slots written, slot ids
+        T = int((case.slot_mapping >= 0).sum())
+        per_call_alg += 4 * T * Hkv * D * 2 + 4 * B
     mean_call_s = float(call_ms.mean()) / 1e3
     achieved = per_call_alg / mean_call_s / 1e9
     traffic = load_traffic(kernel, workload)
@@ -257,9 +285,12 @@ def main():
             "head_dim": D, "block_size": 16, "layers": layers,
             "partition_tokens": part, "kernel": kernel,
             "kv_bytes_per_step": kv_bytes,
-            "step": ("pa_write_kv(64 tokens) + pa_decode" if args.config == 2
+            "step": ("pa_decode_append (64-token KV append fused into the decode)"
+                     if fused else "pa_write_kv(64 tokens) + pa_decode" if args.config == 2
                      else "pa_decode" if args.config == 4 else "32 x pa_decode"),
         },
+        "other_step_form_ms": None if other_ms is None else {
+            ("separate" if args.step == "fused" else "fused"): round(other_ms, 5)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(n_real * layers / sec, 1) if layers == 1 else round(n_real / (sec / layers), 1),
         "decode_call_us": {"mean": round(float(call_ms.mean()) * 1e3, 2),
@@ -268,7 +299,8 @@ def main():
                            "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
         "copy_blocks_us": None if copy_us is None else round(copy_us, 2),
         "roofline": {
-            "kernel": roofline_kernel(kernel, part, D),
+            "kernel": roofline_kernel(kernel, part, D) + (" with the fused KV append"
+                                                          if fused else ""),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -124,6 +124,28 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     float scale, void* out, const pa_dims* dims,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step in one call: the KV append of every row's new token,
+ * then paged decode attention over the updated cache. Equivalent to
+ *   pa_write_kv(k_new, v_new, slot_mapping, num_seqs, ...);
+ *   pa_decode(q, k_pool, v_pool, block_tables, seq_lens, ...);
+ * for the usual decode step, where row b appends exactly one token, the
+ * newest one it attends to: k_new and v_new are [B, Hkv, D] and
+ * slot_mapping[b] is either negative (row b appends nothing) or the slot of
+ * position seq_lens[b] - 1 of row b's table, i.e.
+ *   block_tables[b][(seq_lens[b] - 1) / 16] * 16 + (seq_lens[b] - 1) % 16.
+ * A decode step writes the new token's K/V into its slot and then attends
+ * over the sequence including it [cs2680 Lecture 10, §10.3 and its notes on
+ * growing a sequence by one token]. With the balanced split (matrix-core
+ * kernel, partition_tokens == 0) the append runs inside the decode kernel
+ * (one launch); otherwise the append kernel runs first on the same stream.
+ * Any other slot_mapping gives undefined results. Arguments, workspace and
+ * errors as pa_decode. */
+pa_status pa_decode_append(const void* q, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, void* k_pool, void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           float scale, void* out, const pa_dims* dims,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* KV append: for t < num_tokens with s = slot_mapping[t] >= 0,
  *   k_pool[s / 16, h, s % 16, :] = k_new[t, h, :]
  *   v_pool[s / 16, h, :, s % 16] = v_new[t, h, :]   for every KV head h.

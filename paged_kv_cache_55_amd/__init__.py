@@ -7,6 +7,8 @@ HIP kernels of libpagedkv.so. The library is loaded on first use and a
 missing build is an error: there is no fallback path.
 
     pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, ...)
+    pa_decode_append(q, k_new, v_new, slot_mapping, k_pool, v_pool,
+                     block_tables, seq_lens, scale, out, ...)
     pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool)
     pa_copy_blocks(k_pool, v_pool, block_mapping)
     pa_decode_workspace_bytes(dims)
@@ -26,7 +28,8 @@ from .build import LIB_PATH
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_LAUNCH",
     "PaDims", "PagedKVError", "SYMBOLS", "load_library", "make_dims",
-    "pa_decode", "pa_decode_workspace_bytes", "pa_write_kv", "pa_copy_blocks",
+    "pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_write_kv",
+    "pa_copy_blocks",
     "pa_status_string", "pa_version", "validate",
 ]
 
@@ -35,7 +38,7 @@ PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 BLOCK_SIZE = 16
 
-SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_write_kv",
+SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_append", "pa_write_kv",
            "pa_copy_blocks", "pa_status_string", "pa_version")
 
 
@@ -71,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_bytes.restype = SZ
     lib.pa_decode.argtypes = [P, P, P, P, P, F32, P, D, P, SZ, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_append.argtypes = [P, P, P, P, P, P, P, P, F32, P, D, P, SZ, P]
+    lib.pa_decode_append.restype = ctypes.c_int
     lib.pa_write_kv.argtypes = [P, P, P, I32, P, P, D, P]
     lib.pa_write_kv.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
@@ -147,18 +152,7 @@ def pa_decode_workspace_bytes(dims: PaDims) -> int:
     return int(load_library().pa_decode_workspace_bytes(ctypes.byref(dims)))
 
 
-def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
-              partition_tokens=512, kernel="auto", workspace=None, stream=None):
-    """out[b, h] = softmax(scale * q[b, h] K_b^T) V_b over the paged K/V.
-
-    ``partition_tokens`` > 0 splits each sequence into partitions of that
-    many tokens; 0 asks for the balanced split (matrix-core kernel) or one
-    partition per sequence (vector-ALU kernel). A caller-provided
-    ``workspace`` (uint8 device tensor of at least
-    pa_decode_workspace_bytes bytes) must be zero-filled before its first
-    use; calls leave it reusable. One workspace must not serve two calls that
-    can run at the same time.
-    """
+def _decode_dims(q, k_pool, v_pool, block_tables, seq_lens, out, partition_tokens, kernel):
     torch = _torch()
     NB, Hkv, D = _pool_dims(k_pool, v_pool)
     _need(q.dim() == 3 and q.shape[2] == D, "q must be [B, Hq, D]")
@@ -177,18 +171,66 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
           and out.is_cuda, "out must match q")
     dims = make_dims(B, Hq, Hkv, D, block_tables.shape[1], NB, _dtype_code(q),
                      partition_tokens, kernel)
-    lib = load_library()
-    need = int(lib.pa_decode_workspace_bytes(ctypes.byref(dims)))
+    return dims, out
+
+
+def _workspace(dims, workspace, device):
+    need = pa_decode_workspace_bytes(dims)
     if need and workspace is None:
         # zero-filled once; pa_decode leaves it reusable
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = _torch().zeros(need, dtype=_torch().uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-                       _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
-                       ctypes.byref(dims), _ptr(workspace), ctypes.c_size_t(ws_bytes),
-                       _stream(stream))
+    return workspace, ws_bytes
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
+              partition_tokens=512, kernel="auto", workspace=None, stream=None):
+    """out[b, h] = softmax(scale * q[b, h] K_b^T) V_b over the paged K/V.
+
+    ``partition_tokens`` > 0 splits each sequence into partitions of that
+    many tokens; 0 asks for the balanced split (matrix-core kernel) or one
+    partition per sequence (vector-ALU kernel). A caller-provided
+    ``workspace`` (uint8 device tensor of at least
+    pa_decode_workspace_bytes bytes) must be zero-filled before its first
+    use; calls leave it reusable. One workspace must not serve two calls that
+    can run at the same time.
+    """
+    dims, out = _decode_dims(q, k_pool, v_pool, block_tables, seq_lens, out,
+                             partition_tokens, kernel)
+    workspace, ws_bytes = _workspace(dims, workspace, q.device)
+    st = load_library().pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                  _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                                  ctypes.byref(dims), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+                                  _stream(stream))
     if st != PA_OK:
         raise PagedKVError("pa_decode", st)
+    return out
+
+
+def pa_decode_append(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_tables, seq_lens,
+                     scale, out=None, *, partition_tokens=0, kernel="auto", workspace=None,
+                     stream=None):
+    """One decode step: row b's new token (k_new/v_new[b], [B, Hkv, D]) is
+    stored at slot_mapping[b] (negative = none), which must be the slot of
+    position seq_lens[b] - 1 of row b, then out = pa_decode(...) over the
+    updated pools. With the balanced split this is a single kernel."""
+    torch = _torch()
+    dims, out = _decode_dims(q, k_pool, v_pool, block_tables, seq_lens, out,
+                             partition_tokens, kernel)
+    B, Hkv, D = dims.num_seqs, dims.num_kv_heads, dims.head_dim
+    _need(slot_mapping.dtype == torch.int32 and tuple(slot_mapping.shape) == (B,)
+          and slot_mapping.is_contiguous() and slot_mapping.is_cuda,
+          "slot_mapping must be int32 [B] on the device")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(tuple(t.shape) == (B, Hkv, D) and t.dtype == k_pool.dtype
+              and t.is_contiguous() and t.is_cuda, f"{n} must be [B, Hkv, D] like the pools")
+    workspace, ws_bytes = _workspace(dims, workspace, q.device)
+    st = load_library().pa_decode_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+        ctypes.byref(dims), _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_decode_append", st)
     return out
 
 

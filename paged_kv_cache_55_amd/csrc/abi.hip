@@ -153,20 +153,14 @@ hipError_t lds_per_workgroup(size_t* out) {
   return hipSuccess;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t pa_decode_workspace_bytes(const pa_dims* dims) {
-  Plan p;
-  if (plan_decode(dims, &p) != PA_OK) return 0;
-  return p.ws_bytes;
-}
-
-pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
-                    const int32_t* block_tables, const int32_t* seq_lens, float scale,
-                    void* out, const pa_dims* dims, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+// pa_decode, and pa_decode_append when k_new is non-null: the balanced split
+// stores each row's new token inside the decode kernel; any other plan
+// launches the KV append kernel first.
+pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                      void* out, const pa_dims* dims, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   Plan plan;
   pa_status st = plan_decode(dims, &plan);
   if (st != PA_OK) return st;
@@ -198,9 +192,23 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.split_waves = 0;
   a.min_seg_blocks = 0;
   a.stage_slots = 0;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.slot_mapping = nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
+  if (k_new != nullptr) {
+    if (plan.balanced) {
+      a.k_new = k_new;
+      a.v_new = v_new;
+      a.slot_mapping = slot_mapping;
+    } else {
+      e = launch_write_kv(k_new, v_new, slot_mapping, dims->num_seqs, (void*)k_pool,
+                          (void*)v_pool, dims->num_kv_heads, dims->head_dim, elem_bytes(dims), s);
+      if (e != hipSuccess) return PA_ERR_LAUNCH;
+    }
+  }
   if (plan.balanced) {
     size_t lds = 0;
     e = lds_per_workgroup(&lds);
@@ -239,6 +247,34 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_workspace_bytes(const pa_dims* dims) {
+  Plan p;
+  if (plan_decode(dims, &p) != PA_OK) return 0;
+  return p.ws_bytes;
+}
+
+pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                    void* out, const pa_dims* dims, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_impl(q, nullptr, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens, scale,
+                     out, dims, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(const void* q, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, void* k_pool, void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                           void* out, const pa_dims* dims, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  return decode_impl(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_tables, seq_lens,
+                     scale, out, dims, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,

@@ -666,6 +666,45 @@ __device__ __forceinline__ void publish_pieces(const DecodeArgs& a, const Pendin
   }
 }
 
+// Fused KV append. Row b's new token is the last token of each of its pairs,
+// so the wave whose range holds a pair's last block stores that pair's K row
+// and V column of the new token (16-byte K vectors on the first D / 8
+// lanes, 2-byte V elements on all lanes) before issuing any tile load. Its
+// own later tile loads are issued after these stores and, vector memory
+// operations completing in order, are waited for only after them; a block
+// among the first two of the range, whose loads would be in flight before
+// that first wait, is covered by waiting for the stores here. Returns
+// whether that wait is needed.
+template <int D>
+__device__ __forceinline__ bool append_new_tokens(const DecodeArgs& a, const int* prefix,
+                                                  Segment s, long long f0, long long f1,
+                                                  int lane) {
+  const int Hkv = a.num_kv_heads;
+  bool early = false;
+  while (true) {
+    if (s.fe == s.ps + s.nb) {  // the pair's last block lies in this range
+      const int slot = uniform_load(a.slot_mapping, s.b);
+      if (slot >= 0) {
+        const size_t src = ((size_t)s.b * Hkv + s.kvh) * D;
+        const int blk = slot / kBlockTokens;
+        const int off = slot - blk * kBlockTokens;
+        const size_t tile = ((size_t)blk * Hkv + s.kvh) * (size_t)(kBlockTokens * D);
+        const bf16_t* kn = (const bf16_t*)a.k_new + src;
+        const bf16_t* vn = (const bf16_t*)a.v_new + src;
+        bf16_t* kp = (bf16_t*)a.k_pool + tile + (size_t)off * D;
+        bf16_t* vp = (bf16_t*)a.v_pool + tile + off;
+        if (lane < D / 8) *(uint4*)(kp + lane * 8) = *(const uint4*)(kn + lane * 8);
+#pragma unroll
+        for (int d = lane; d < D; d += 64) vp[(size_t)d * kBlockTokens] = vn[d];
+        early |= s.fe - 1 <= f0 + 1;
+      }
+    }
+    if (s.fe >= f1) break;
+    s = next_segment(s, prefix, a.seq_lens, Hkv, f1);
+  }
+  return early;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a) {
   // dynamic LDS: prefix [B + 1] ints, then per wave an area of
@@ -695,6 +734,8 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   const size_t block_stride = (size_t)Hkv * tile_elems;
 
   Segment cur = locate(prefix, a.seq_lens, B, Hkv, f0, f1);
+  if (a.k_new != nullptr && append_new_tokens<D>(a, prefix, cur, f0, f1, lane))
+    wait_stores_complete();
   auto table_entry = [&](const Segment& sg) {
     return uniform_load(a.block_tables, (size_t)sg.b * a.max_blocks + sg.j);
   };

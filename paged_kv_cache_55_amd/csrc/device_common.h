@@ -149,6 +149,12 @@ struct DecodeArgs {
   int split_waves;     // balanced split: waves of the decode grid (4 per workgroup)
   int min_seg_blocks;  // balanced split: least blocks per wave range
   int stage_slots;     // balanced split: complete outputs a wave stages in LDS (0 = none)
+  // fused KV append (balanced split): row b's new token k_new/v_new[b] is
+  // stored at slot_mapping[b] (skipped when negative) before it is read;
+  // null when the call appends nothing
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
 };
 
 }  // namespace pagedkv

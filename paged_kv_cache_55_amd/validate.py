@@ -7,7 +7,9 @@ copies, the conditions the kernels rely on:
   * every table entry a sequence uses is a block id in [0, NB);
   * write slots are distinct, and non-negative ones are < NB * 16;
   * copy pairs name blocks in [0, NB), destinations are distinct, and no
-    destination is also a source in the same call.
+    destination is also a source in the same call;
+  * for the fused decode step (``append_rows=True``): slot_mapping[b] is
+    negative or the slot of position seq_lens[b] - 1 of row b.
 It raises ValueError on the first violation.
 """
 
@@ -27,7 +29,7 @@ def _host(x):
 
 
 def validate(num_blocks, block_tables=None, seq_lens=None, slot_mapping=None,
-             block_mapping=None) -> None:
+             block_mapping=None, append_rows=False) -> None:
     nb = int(num_blocks)
     if block_tables is not None or seq_lens is not None:
         bt = _host(block_tables)
@@ -48,6 +50,21 @@ def validate(num_blocks, block_tables=None, seq_lens=None, slot_mapping=None,
             raise ValueError("slot out of range")
         if len(np.unique(live)) != len(live):
             raise ValueError("duplicate write slots race")
+    if append_rows:
+        bt = _host(block_tables)
+        lens = _host(seq_lens).astype(np.int64)
+        s = _host(slot_mapping).astype(np.int64)
+        if s.shape != lens.shape:
+            raise ValueError("the fused step takes one slot per row")
+        for b, (slot, L) in enumerate(zip(s.tolist(), lens.tolist())):
+            if slot < 0:
+                continue
+            if L == 0:
+                raise ValueError(f"row {b}: padded row appends a token")
+            pos = L - 1
+            want = int(bt[b, pos // BLOCK_SIZE]) * BLOCK_SIZE + pos % BLOCK_SIZE
+            if slot != want:
+                raise ValueError(f"row {b}: slot {slot} is not the slot of position {pos}")
     if block_mapping is not None:
         m = _host(block_mapping).astype(np.int64).reshape(-1, 2)
         if m.size and ((m < 0).any() or (m >= nb).any()):

@@ -159,6 +159,28 @@ def test_validator_accepts_good_inputs():
     pk.validate(c3.num_blocks, c3.block_tables, c3.seq_lens, c3.slot_mapping, c3.block_mapping)
 
 
+def test_append_rejects_null_new_tokens(lib):
+    d = dims(partition_tokens=0)
+    st = lib.pa_decode_append(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              ctypes.c_float(0.1), FAKE, ctypes.byref(d), FAKE,
+                              ctypes.c_size_t(1 << 30), None)
+    assert st == pk.PA_ERR_INVALID_ARG
+
+
+def test_validator_fused_step_contract():
+    import workloads as wl
+    c = wl.config2()
+    pk.validate(c.num_blocks, c.block_tables, c.seq_lens, c.slot_mapping, append_rows=True)
+    bad = c.slot_mapping.clone()
+    bad[3] += 1  # not the slot of position L - 1
+    with pytest.raises(ValueError):
+        pk.validate(c.num_blocks, c.block_tables, c.seq_lens, bad, append_rows=True)
+    lens = c.seq_lens.clone()
+    lens[5] = 0  # a padded row may not append
+    with pytest.raises(ValueError):
+        pk.validate(c.num_blocks, c.block_tables, lens, c.slot_mapping, append_rows=True)
+
+
 @pytest.mark.parametrize("case", ["len", "entry", "dup_slot", "slot_range", "dst_src", "dup_dst"])
 def test_validator_rejects(case):
     bt = np.array([[0, 1, 2]], dtype=np.int32)
