@@ -62,6 +62,9 @@ def parse():
                          "configs 2 and 4, 512 for the 32-layer step)")
     ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps in a HIP graph (one step per input copy) "
+                         "and time its replays")
     ap.add_argument("--step", default="separate", choices=["fused", "separate"],
                     help="8B batch: append + decode in one call, or two calls")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -158,6 +161,7 @@ def main():
         ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         scale = 1.0 / math.sqrt(D)
         case = None
+        copies = []
 
         def decode_calls(i):
             return [(q, k, v, bt, lens, out) for (q, k, v) in layer_t]
@@ -170,6 +174,7 @@ def main():
     def step(i, events=None, mode=None):
         mode = mode or args.step
         fused = mode == "fused" and args.config == 2
+        stream = torch.cuda.current_stream()  # the capture stream inside a graph capture
         if not fused:
             pre(i)
         for (q, k, v, tb, ln, o) in decode_calls(i):
@@ -192,6 +197,23 @@ def main():
     def timed_steps(mode):
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        if args.graph:
+            # one graph holds one step per input copy; replays cover the steps
+            per_graph = len(copies) if copies else 1
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(per_graph):
+                    step(i, mode=mode)
+            replays = max(1, args.steps // per_graph)
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for _ in range(replays):
+                g.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / (replays * per_graph)
         torch.cuda.synchronize()
         t0.record(stream)
         for i in range(args.steps):
@@ -283,7 +305,7 @@ def main():
             "workload": workload,
             "batch": B, "real_rows": n_real, "q_heads": Hq, "kv_heads": Hkv,
             "head_dim": D, "block_size": 16, "layers": layers,
-            "partition_tokens": part, "kernel": kernel,
+            "partition_tokens": part, "kernel": kernel, "graph": args.graph,
             "kv_bytes_per_step": kv_bytes,
             "step": ("pa_decode_append (64-token KV append fused into the decode)"
                      if fused else "pa_write_kv(64 tokens) + pa_decode" if args.config == 2
