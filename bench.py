@@ -62,6 +62,11 @@ def parse():
                          "configs 2 and 4, 512 for the 32-layer step)")
     ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--block-size", type=int, default=16,
+                    help="tokens per KV block for the 8B/70B layers (8 .. 256; other than 16 "
+                         "needs the balanced split)")
+    ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
+                    help="physical block placement of the 8B/70B layers")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed steps in a HIP graph (one step per input copy) "
                          "and time its replays")
@@ -120,7 +125,8 @@ def main():
 
     # ---------------- inputs ----------------
     if args.config in (2, 4):
-        case = wl.config2() if args.config == 2 else wl.config4()
+        mk = wl.config2 if args.config == 2 else wl.config4
+        case = mk(block_size=args.block_size, placement=args.placement)
         copies = [case.to(dev) for _ in range(max(1, args.copies))]
         B, Hq, Hkv, D = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
         n_real = int((case.seq_lens > 0).sum())
@@ -129,9 +135,13 @@ def main():
         lens_host = case.seq_lens.numpy()
         workload = ("llama3_8b_layer_b64_u128_4096" if args.config == 2
                     else "llama33_70b_layer_b256_lognormal1024")
+        if args.block_size != 16:
+            workload += f"_block{args.block_size}"
+        if args.placement != "random":
+            workload += f"_{args.placement}"
         outs = [torch.empty_like(c.q) for c in copies]
         dims = pk.make_dims(B, Hq, Hkv, D, case.max_blocks_per_seq, case.num_blocks,
-                            pk.PA_BF16, part, kernel)
+                            pk.PA_BF16, part, kernel, case.block_size)
         ws_bytes = pk.pa_decode_workspace_bytes(dims)
         ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         scale = case.scale
@@ -273,7 +283,8 @@ def main():
     # ---------------- figures ----------------
     sec = ms_per_step / 1e3
     value = kv_bytes / sec / 1e9
-    table_bytes = int(sum(math.ceil(int(L) / 16) for L in lens_host)) * 4 * (1 if layers == 1 else 1)
+    bsz = case.block_size if case is not None else 16
+    table_bytes = int(sum(math.ceil(int(L) / bsz) for L in lens_host)) * 4
     per_call_alg = (kv_bytes / layers) + 2 * B * Hq * D * 2 + table_bytes + 4 * B
     fused = args.config == 2 and args.step == "fused"
     if fused:  # the appended tokens: k_new/v_new read, their slots written, slot ids
@@ -304,7 +315,9 @@ def main():
         "config": {
             "workload": workload,
             "batch": B, "real_rows": n_real, "q_heads": Hq, "kv_heads": Hkv,
-            "head_dim": D, "block_size": 16, "layers": layers,
+            "head_dim": D, "layers": layers,
+            "block_size": case.block_size if case is not None else 16,
+            "placement": args.placement if case is not None else "random",
             "partition_tokens": part, "kernel": kernel, "graph": args.graph,
             "kv_bytes_per_step": kv_bytes,
             "step": ("pa_decode_append (64-token KV append fused into the decode)"

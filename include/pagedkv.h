@@ -3,7 +3,8 @@
  * (gfx950), plus the two cache-maintenance calls it needs.
  *
  * What the calls compute
- *   The KV cache is one preallocated pool of fixed-size blocks of 16 tokens;
+ *   The KV cache is one preallocated pool of fixed-size blocks of BS tokens
+ *   (BS = block_size, 16 by default);
  *   every sequence has a block table mapping its logical block j to a
  *   physical block, and a length; blocks need not be adjacent
  *   [cs2680 Lecture 10, §10.3 "PagedAttention: the KV cache as virtual
@@ -17,14 +18,14 @@
  *
  * Layouts (row-major, contiguous; all device memory unless noted)
  *   q, out        [B, Hq, D]                        element type = dtype
- *   k_pool        [NB, Hkv, 16, D]   token-major K tiles
- *   v_pool        [NB, Hkv, D, 16]   dim-major (transposed) V tiles
+ *   k_pool        [NB, Hkv, BS, D]   token-major K blocks
+ *   v_pool        [NB, Hkv, D, BS]   dim-major (transposed) V blocks
  *   block_tables  int32 [B, MB]      row b, entry j = physical block of
- *                                    tokens 16j .. 16j+15 of sequence b
+ *                                    tokens BS*j .. BS*j+BS-1 of sequence b
  *   seq_lens      int32 [B]          tokens attended, newest included;
  *                                    0 = padded row (output is exact zeros)
  *   k_new, v_new  [T, Hkv, D]
- *   slot_mapping  int32 [T]          slot = block * 16 + offset; < 0 = skip
+ *   slot_mapping  int32 [T]          slot = block * BS + offset; < 0 = skip
  *   block_mapping int32 [n, 2]       (src, dst) physical block pairs
  *   Query head h reads KV head h / (Hq / Hkv).
  *
@@ -45,9 +46,9 @@
  *   PA_ERR_UNSUPPORTED and nothing runs. A launch failure reported by the
  *   HIP runtime returns PA_ERR_LAUNCH. Device-resident values are NOT
  *   checked (that would need a synchronisation); the caller guarantees:
- *     0 <= seq_lens[b] <= MB * 16;
- *     0 <= block_tables[b][j] < NB for every j < ceil(seq_lens[b] / 16);
- *     write slots are distinct and < NB * 16;
+ *     0 <= seq_lens[b] <= MB * BS;
+ *     0 <= block_tables[b][j] < NB for every j < ceil(seq_lens[b] / BS);
+ *     write slots are distinct and < NB * BS;
  *     copy pairs name blocks < NB, destinations are distinct and no
  *     destination is also a source in the same call.
  *   Violations give undefined results (out-of-range reads or racing
@@ -82,7 +83,8 @@ typedef struct {
   int32_t num_q_heads;        /* Hq  (multiple of Hkv, Hq / Hkv <= 16) */
   int32_t num_kv_heads;       /* Hkv (>= 1) */
   int32_t head_dim;           /* D   (64 or 128) */
-  int32_t block_size;         /* must be 16 */
+  int32_t block_size;         /* tokens per block: 16; 8, 32, 64, 128 or 256
+                                 are taken by the balanced split only */
   int32_t max_blocks_per_seq; /* MB: row stride of block_tables (>= 1) */
   int32_t num_blocks;         /* NB: pool capacity in blocks (>= 1) */
   int32_t partition_tokens;   /* split-K partition length: a multiple of 16,
@@ -116,7 +118,7 @@ size_t pa_decode_workspace_bytes(const pa_dims* dims);
  * Results do not depend on timing: pieces merge in a fixed order.
  * Rows with seq_lens[b] == 0 get zeros. Slots at or past seq_lens[b] never
  * reach the result (they are masked, so they may hold anything, NaN
- * included), and table entries at or past ceil(seq_lens[b] / 16) are never
+ * included), and table entries at or past ceil(seq_lens[b] / BS) are never
  * read. bf16 output is rounded to nearest even.
  * `workspace` may be NULL when pa_decode_workspace_bytes() is 0. */
 pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -132,7 +134,7 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
  * newest one it attends to: k_new and v_new are [B, Hkv, D] and
  * slot_mapping[b] is either negative (row b appends nothing) or the slot of
  * position seq_lens[b] - 1 of row b's table, i.e.
- *   block_tables[b][(seq_lens[b] - 1) / 16] * 16 + (seq_lens[b] - 1) % 16.
+ *   block_tables[b][(seq_lens[b] - 1) / BS] * BS + (seq_lens[b] - 1) % BS.
  * A decode step writes the new token's K/V into its slot and then attends
  * over the sequence including it [cs2680 Lecture 10, §10.3 and its notes on
  * growing a sequence by one token]. With the balanced split (matrix-core
@@ -147,8 +149,8 @@ pa_status pa_decode_append(const void* q, const void* k_new, const void* v_new,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* KV append: for t < num_tokens with s = slot_mapping[t] >= 0,
- *   k_pool[s / 16, h, s % 16, :] = k_new[t, h, :]
- *   v_pool[s / 16, h, :, s % 16] = v_new[t, h, :]   for every KV head h.
+ *   k_pool[s / BS, h, s % BS, :] = k_new[t, h, :]
+ *   v_pool[s / BS, h, :, s % BS] = v_new[t, h, :]   for every KV head h.
  * A bit copy: no value is converted. Growth takes a new block only when a
  * sequence's last block is full [cs2680 Lecture 10, §10.3 and its notes on
  * growing a sequence by one token]. Uses num_kv_heads, head_dim,

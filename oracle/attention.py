@@ -27,10 +27,15 @@ Readings where the pages are silent (each also listed in the design notes):
 * ``seq_lens[b]`` counts every cached token including the newest one; a
   row with length 0 is a padded row whose output is exactly zero.
 * Pool layout (the library's interface; the pages leave it open):
-      k_pool[block, kv_head, slot, d]     token-major K tiles
-      v_pool[block, kv_head, d, slot]     dim-major V tiles
+      k_pool[block, kv_head, slot, d]     token-major K blocks
+      v_pool[block, kv_head, d, slot]     dim-major V blocks (blocks of up
+                                          to 16 tokens)
+      v_pool[block, kv_head, slot // 16, d, slot % 16]
+                                          blocks longer than 16 tokens: a
+                                          dim-major V tile per 16 slots
   A token at position t of sequence b lives in block
-  ``block_tables[b, t // 16]`` at slot ``t % 16``.
+  ``block_tables[b, t // block_size]`` at slot ``t % block_size``
+  (block_size = 16 unless stated).
 * Inputs are exact: bf16 values are widened to float64 without rounding.
 
 The arithmetic is done in float64 with a naive (two-pass) softmax over the
@@ -86,6 +91,15 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 # Table walk and attention
 # --------------------------------------------------------------------------
 
+def v_at(v_pool, phys, slot):
+    """V values [.., Hkv, D] of slot(s) ``slot`` of block(s) ``phys``, in
+    either V layout (4-D: [NB, Hkv, D, slot]; 5-D: [NB, Hkv, slot // 16, D,
+    slot % 16])."""
+    if v_pool.ndim == 5:
+        return v_pool[phys, :, slot // 16, :, slot % 16]
+    return v_pool[phys, :, :, slot]
+
+
 def gather_sequence(k_pool, v_pool, table_row, seq_len, dtype,
                     block_size=BLOCK_SIZE):
     """Materialise one sequence's contiguous K and V by walking its table.
@@ -107,7 +121,7 @@ def gather_sequence(k_pool, v_pool, table_row, seq_len, dtype,
     slot = t % block_size
     # k_pool[phys, :, slot, :] -> [L, Hkv, D]; v_pool[phys, :, :, slot] -> [L, Hkv, D]
     k = k_pool[phys, :, slot, :]
-    v = v_pool[phys, :, :, slot]
+    v = v_at(v_pool, phys, slot)
     K = as_f64(k, dtype).transpose(1, 0, 2)
     V = as_f64(v, dtype).transpose(1, 0, 2)
     return K, V
@@ -141,8 +155,9 @@ def paged_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, dtype,
                  rows=None, block_size=BLOCK_SIZE):
     """Paged decode attention for a batch, in float64.
 
-    q [B, Hq, D], k_pool [NB, Hkv, 16, D], v_pool [NB, Hkv, D, 16] (storage
-    format ``dtype``), block_tables int [B, MB], seq_lens int [B]. For each
+    q [B, Hq, D], k_pool [NB, Hkv, bs, D], v_pool in either V layout
+    (storage format ``dtype``), block_tables int [B, MB], seq_lens int [B],
+    bs = ``block_size``. For each
     selected row b the sequence is gathered through its table and attended
     contiguously; rows with length 0 are zero. ``rows`` selects a subset of
     sequences (for sampled checks at full size); the result then has one
@@ -197,7 +212,11 @@ def brute_force_decode(q, k_pool, v_pool, block_tables, seq_lens, scale,
                 num = 0.0
                 for t in range(L):
                     blk = int(block_tables[b][t // block_size])
-                    num += w[t] * float(vf[blk, kv, d, t % block_size])
+                    slot = t % block_size
+                    if vf.ndim == 5:
+                        num += w[t] * float(vf[blk, kv, slot // 16, d, slot % 16])
+                    else:
+                        num += w[t] * float(vf[blk, kv, d, slot])
                 out[b][h][d] = num / tot
     return np.array(out, dtype=np.float64).reshape(B, Hq, D)
 
@@ -224,7 +243,10 @@ def write_kv(k_pool, v_pool, k_new, v_new, slot_mapping,
             continue
         blk, pos = divmod(int(s), block_size)
         k_out[blk, :, pos, :] = k_new[i]
-        v_out[blk, :, :, pos] = v_new[i]
+        if v_out.ndim == 5:
+            v_out[blk, :, pos // 16, :, pos % 16] = v_new[i]
+        else:
+            v_out[blk, :, :, pos] = v_new[i]
     return k_out, v_out
 
 

@@ -13,7 +13,9 @@ missing build is an error: there is no fallback path.
     pa_copy_blocks(k_pool, v_pool, block_mapping)
     pa_decode_workspace_bytes(dims)
 
-Layouts: q/out [B, Hq, D]; k_pool [NB, Hkv, 16, D]; v_pool [NB, Hkv, D, 16];
+Layouts: q/out [B, Hq, D]; k_pool [NB, Hkv, BS, D]; v_pool [NB, Hkv, D, BS]
+(BS = 16 tokens per block; 8 .. 256 with the balanced split, V as
+[NB, Hkv, BS // 16, D, 16] beyond 16);
 block_tables int32 [B, MB]; seq_lens int32 [B]; k_new/v_new [T, Hkv, D];
 slot_mapping int32 [T]; block_mapping int32 [n, 2].
 """
@@ -131,21 +133,29 @@ def _need(cond, msg):
 
 
 def make_dims(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-              num_blocks, dtype, partition_tokens=512, kernel="auto") -> PaDims:
+              num_blocks, dtype, partition_tokens=512, kernel="auto",
+              block_size=BLOCK_SIZE) -> PaDims:
     return PaDims(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
-                  BLOCK_SIZE, int(max_blocks_per_seq), int(num_blocks),
+                  int(block_size), int(max_blocks_per_seq), int(num_blocks),
                   int(partition_tokens), int(dtype), KERNELS[kernel])
 
 
 def _pool_dims(k_pool, v_pool):
-    _need(k_pool.dim() == 4 and v_pool.dim() == 4, "pools must be 4-D")
+    """(NB, Hkv, D, block size) of a K/V pool pair; the library checks that
+    the block size is supported. V is [NB, Hkv, D, BS] for blocks of up to
+    16 tokens and [NB, Hkv, BS // 16, D, 16] (a dim-major tile per 16
+    tokens) for longer ones."""
+    _need(k_pool.dim() == 4, "k_pool must be [NB, Hkv, BS, D]")
     NB, Hkv, BS, D = k_pool.shape
-    _need(BS == BLOCK_SIZE, f"k_pool block dim must be {BLOCK_SIZE}")
-    _need(tuple(v_pool.shape) == (NB, Hkv, D, BS), "v_pool must be [NB, Hkv, D, 16]")
+    if BS <= BLOCK_SIZE:
+        _need(tuple(v_pool.shape) == (NB, Hkv, D, BS), "v_pool must be [NB, Hkv, D, BS]")
+    else:
+        _need(tuple(v_pool.shape) == (NB, Hkv, BS // BLOCK_SIZE, D, BLOCK_SIZE)
+              and BS % BLOCK_SIZE == 0, "v_pool must be [NB, Hkv, BS // 16, D, 16]")
     _need(k_pool.dtype == v_pool.dtype, "k_pool and v_pool dtypes differ")
     _need(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
     _need(k_pool.is_cuda and v_pool.is_cuda, "pools must be device tensors")
-    return NB, Hkv, D
+    return NB, Hkv, D, BS
 
 
 def pa_decode_workspace_bytes(dims: PaDims) -> int:
@@ -154,7 +164,7 @@ def pa_decode_workspace_bytes(dims: PaDims) -> int:
 
 def _decode_dims(q, k_pool, v_pool, block_tables, seq_lens, out, partition_tokens, kernel):
     torch = _torch()
-    NB, Hkv, D = _pool_dims(k_pool, v_pool)
+    NB, Hkv, D, BS = _pool_dims(k_pool, v_pool)
     _need(q.dim() == 3 and q.shape[2] == D, "q must be [B, Hq, D]")
     B, Hq, _ = q.shape
     _need(q.dtype == k_pool.dtype, "q and pools must share a dtype")
@@ -170,7 +180,7 @@ def _decode_dims(q, k_pool, v_pool, block_tables, seq_lens, out, partition_token
     _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
           and out.is_cuda, "out must match q")
     dims = make_dims(B, Hq, Hkv, D, block_tables.shape[1], NB, _dtype_code(q),
-                     partition_tokens, kernel)
+                     partition_tokens, kernel, BS)
     return dims, out
 
 
@@ -237,7 +247,7 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_tables
 def pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, *, stream=None):
     """k_pool/v_pool[slot] = k_new/v_new[t] for every t with slot >= 0."""
     torch = _torch()
-    NB, Hkv, D = _pool_dims(k_pool, v_pool)
+    NB, Hkv, D, BS = _pool_dims(k_pool, v_pool)
     T = slot_mapping.shape[0]
     _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1
           and slot_mapping.is_contiguous() and slot_mapping.is_cuda,
@@ -245,7 +255,7 @@ def pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, *, stream=None):
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _need(tuple(t.shape) == (T, Hkv, D) and t.dtype == k_pool.dtype
               and t.is_contiguous() and t.is_cuda, f"{n} must be [T, Hkv, D] like the pools")
-    dims = make_dims(1, Hkv, Hkv, D, 1, NB, _dtype_code(k_pool))
+    dims = make_dims(1, Hkv, Hkv, D, 1, NB, _dtype_code(k_pool), block_size=BS)
     st = load_library().pa_write_kv(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T,
                                     _ptr(k_pool), _ptr(v_pool), ctypes.byref(dims),
                                     _stream(stream))
@@ -256,11 +266,11 @@ def pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, *, stream=None):
 def pa_copy_blocks(k_pool, v_pool, block_mapping, *, stream=None):
     """Whole-block copy dst <- src for every (src, dst) row of block_mapping."""
     torch = _torch()
-    NB, Hkv, D = _pool_dims(k_pool, v_pool)
+    NB, Hkv, D, BS = _pool_dims(k_pool, v_pool)
     _need(block_mapping.dtype == torch.int32 and block_mapping.dim() == 2
           and block_mapping.shape[1] == 2 and block_mapping.is_contiguous()
           and block_mapping.is_cuda, "block_mapping must be int32 [n, 2] on the device")
-    dims = make_dims(1, Hkv, Hkv, D, 1, NB, _dtype_code(k_pool))
+    dims = make_dims(1, Hkv, Hkv, D, 1, NB, _dtype_code(k_pool), block_size=BS)
     st = load_library().pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(block_mapping),
                                        block_mapping.shape[0], ctypes.byref(dims),
                                        _stream(stream))

@@ -21,9 +21,16 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Checks shared by every call: pool geometry and dtype.
+// log2 of a supported block size (8 .. 256 tokens, a power of two), else -1
+int block_shift(int block_size) {
+  for (int sh = 3; sh <= 8; ++sh)
+    if (block_size == (1 << sh)) return sh;
+  return -1;
+}
+
 pa_status check_pool(const pa_dims* d) {
   if (!d) return PA_ERR_INVALID_ARG;
-  if (d->block_size != kBlockTokens) return PA_ERR_INVALID_ARG;
+  if (block_shift(d->block_size) < 0) return PA_ERR_INVALID_ARG;
   if (d->num_kv_heads < 1 || d->head_dim < 1 || d->num_blocks < 1) return PA_ERR_INVALID_ARG;
   if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
@@ -72,8 +79,10 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
   if (d->kernel == PA_KERNEL_MFMA && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   p->kernel = pick_kernel(d);
   const int G = d->num_q_heads / d->num_kv_heads;
-  const int max_tokens = d->max_blocks_per_seq * kBlockTokens;
+  const int max_tokens = d->max_blocks_per_seq * d->block_size;
   p->balanced = p->kernel == PA_KERNEL_MFMA && d->partition_tokens == 0;
+  // blocks of other than 16 tokens: the balanced split only
+  if (d->block_size != kBlockTokens && !p->balanced) return PA_ERR_UNSUPPORTED;
   if (p->balanced) {
     p->part_tokens = max_tokens;
     p->num_parts = 1;
@@ -192,6 +201,7 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
   a.split_waves = 0;
   a.min_seg_blocks = 0;
   a.stage_slots = 0;
+  a.block_shift = block_shift(dims->block_size);
   a.k_new = nullptr;
   a.v_new = nullptr;
   a.slot_mapping = nullptr;
@@ -205,7 +215,8 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
       a.slot_mapping = slot_mapping;
     } else {
       e = launch_write_kv(k_new, v_new, slot_mapping, dims->num_seqs, (void*)k_pool,
-                          (void*)v_pool, dims->num_kv_heads, dims->head_dim, elem_bytes(dims), s);
+                          (void*)v_pool, dims->num_kv_heads, dims->head_dim,
+                          block_shift(dims->block_size), elem_bytes(dims), s);
       if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
   }
@@ -218,7 +229,7 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
       return PA_ERR_UNSUPPORTED;  // the work list and parked pieces alone do not fit
   }
   const void* fn = plan.kernel == PA_KERNEL_MFMA
-                       ? decode_mfma_fn(dims->head_dim, plan.balanced)
+                       ? decode_mfma_fn(dims->head_dim, plan.balanced, a.block_shift)
                        : decode_valu_fn(dims->dtype, dims->head_dim, a.group);
   const size_t smem = plan.kernel == PA_KERNEL_MFMA
                           ? decode_mfma_smem(dims->num_seqs, a.group, dims->head_dim,
@@ -286,7 +297,8 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool) return PA_ERR_INVALID_ARG;
   hipError_t e = launch_write_kv(k_new, v_new, slot_mapping, num_tokens, k_pool, v_pool,
-                                 dims->num_kv_heads, dims->head_dim, elem_bytes(dims),
+                                 dims->num_kv_heads, dims->head_dim,
+                                 block_shift(dims->block_size), elem_bytes(dims),
                                  (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -299,7 +311,7 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
   if (num_pairs == 0) return PA_OK;
   if (!k_pool || !v_pool || !block_mapping) return PA_ERR_INVALID_ARG;
   const size_t block_bytes =
-      (size_t)dims->num_kv_heads * kBlockTokens * dims->head_dim * elem_bytes(dims);
+      (size_t)dims->num_kv_heads * dims->block_size * dims->head_dim * elem_bytes(dims);
   hipError_t e = launch_copy_blocks(k_pool, v_pool, block_mapping, num_pairs, block_bytes,
                                     (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

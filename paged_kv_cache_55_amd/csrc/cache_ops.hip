@@ -1,9 +1,10 @@
 // KV append (pa_write_kv) and copy-on-write block copy (pa_copy_blocks).
 //
 // Both are bit copies. A new token's K row is contiguous in the token-major
-// K tile; its V column is strided by 16 elements in the dim-major V tile.
-// A block of one pool is a contiguous run of Hkv * 16 * D elements, so a
-// block copy is a flat 16-byte-vector copy.
+// K region of its block; its V column is strided in the dim-major V tile
+// that holds it (the whole block up to 16 tokens, else the 16-token tile).
+// A block of one pool is a contiguous run of Hkv * block_size * D elements,
+// so a block copy is a flat 16-byte-vector copy.
 #include "launch.h"
 
 namespace pagedkv {
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const W* __restrict__ k_n
                                                        const int32_t* __restrict__ slots,
                                                        W* __restrict__ k_pool,
                                                        W* __restrict__ v_pool, int num_tokens,
-                                                       int hkv, int d) {
+                                                       int hkv, int d, int block_shift) {
   constexpr int kPerVec = 16 / sizeof(W);
   const int lane = threadIdx.x & 63;
   const int kvec = d / kPerVec;  // <= 32
@@ -38,12 +39,15 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const W* __restrict__ k_n
     if (d > 64) vv[1] = v_new[src + 64 + lane];
     const int s = uniform_load(slots, t);
     if (s < 0) continue;
-    const int blk = s / kBlockTokens;
-    const int off = s - blk * kBlockTokens;
-    const size_t tile = ((size_t)blk * hkv + h) * (size_t)(kBlockTokens * d);
-    if (lane < kvec) *(uint4*)(k_pool + tile + (size_t)off * d + lane * kPerVec) = kv;
-    v_pool[tile + (size_t)lane * kBlockTokens + off] = vv[0];
-    if (d > 64) v_pool[tile + (size_t)(64 + lane) * kBlockTokens + off] = vv[1];
+    const int bs = 1 << block_shift;
+    const int inner = bs < kBlockTokens ? bs : kBlockTokens;  // V: dim-major tiles
+    const int blk = s >> block_shift;
+    const int off = s & (bs - 1);
+    const size_t region = (((size_t)blk * hkv + h) << block_shift) * d;
+    if (lane < kvec) *(uint4*)(k_pool + region + (size_t)off * d + lane * kPerVec) = kv;
+    W* vp = v_pool + region + (size_t)(off & ~(inner - 1)) * d + (off & (inner - 1));
+    vp[(size_t)lane * inner] = vv[0];
+    if (d > 64) vp[(size_t)(64 + lane) * inner] = vv[1];
   }
 }
 
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,
                            int num_tokens, void* k_pool, void* v_pool, int num_kv_heads,
-                           int head_dim, int elem_bytes, hipStream_t s) {
+                           int head_dim, int block_shift, int elem_bytes, hipStream_t s) {
   // four (token, head) pairs per workgroup; a grid-stride loop covers the rest
   const long long pairs = (long long)num_tokens * num_kv_heads;
   const long long wgs = (pairs + 3) / 4;
@@ -75,14 +79,16 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* 
     const uint16_t* vn = (const uint16_t*)v_new;
     uint16_t* kp = (uint16_t*)k_pool;
     uint16_t* vp = (uint16_t*)v_pool;
-    void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_tokens, &num_kv_heads, &head_dim};
+    void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_tokens, &num_kv_heads, &head_dim,
+                    &block_shift};
     return hipLaunchKernel((const void*)&write_kv_kernel<uint16_t>, grid, block, args, 0, s);
   }
   const uint32_t* kn = (const uint32_t*)k_new;
   const uint32_t* vn = (const uint32_t*)v_new;
   uint32_t* kp = (uint32_t*)k_pool;
   uint32_t* vp = (uint32_t*)v_pool;
-  void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_tokens, &num_kv_heads, &head_dim};
+  void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_tokens, &num_kv_heads, &head_dim,
+                  &block_shift};
   return hipLaunchKernel((const void*)&write_kv_kernel<uint32_t>, grid, block, args, 0, s);
 }
 

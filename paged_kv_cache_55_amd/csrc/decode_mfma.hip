@@ -111,6 +111,51 @@ __device__ __forceinline__ void load_tile(Tile<D>& tl, const bf16_t* kt, const b
                                                        kStreamLoad));
 }
 
+// A 16-token tile made of two 8-token blocks: tokens 0-7 from block A
+// (`region_a`), 8-15 from block B. Every lane issues each load against both
+// blocks' descriptors with an offset that is out of range for the block it
+// does not read; a range-checked buffer load returns zero there without
+// touching memory, so OR-ing the two results gives the lane's data with no
+// divergent branch and no extra traffic.
+template <int D>
+__device__ __forceinline__ void load_tile_two_blocks(Tile<D>& tl, const bf16_t* kpool,
+                                                     const bf16_t* vpool, size_t region_a,
+                                                     size_t region_b, int row, int kg) {
+  constexpr int kHalf = 8;
+  constexpr int kBytes = kHalf * D * 2;
+  constexpr int kOut = 0x40000000;  // beyond any 8-token block
+  const __amdgpu_buffer_rsrc_t ka = range_rsrc(kpool + region_a, kBytes);
+  const __amdgpu_buffer_rsrc_t kb = range_rsrc(kpool + region_b, kBytes);
+  const __amdgpu_buffer_rsrc_t va = range_rsrc(vpool + region_a, kBytes);
+  const __amdgpu_buffer_rsrc_t vb = range_rsrc(vpool + region_b, kBytes);
+  const int k_off = ((row & 7) * D + kg * 8) * 2;
+  const int k_a = row < kHalf ? k_off : kOut;
+  const int k_b = row < kHalf ? kOut : k_off;
+  const int v_off = (row * kHalf + (kg & 1) * 4) * 2;
+  const int v_a = kg < 2 ? v_off : kOut;
+  const int v_b = kg < 2 ? kOut : v_off;
+#pragma unroll
+  for (int c = 0; c < Tile<D>::kQkSteps; ++c) {
+    const u32x4_t x = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ka, k_a + c * 64, 0, kStreamLoad));
+    const u32x4_t y = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kb, k_b + c * 64, 0, kStreamLoad));
+    tl.k[c] = __builtin_bit_cast(bf16x8_t, x | y);
+  }
+#pragma unroll
+  for (int n = 0; n < Tile<D>::kDimTiles; ++n) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    // the step goes into the vector offset: out-of-range masking must see it
+    const u32x2_t x = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(va, v_a + n * kTile * kHalf * 2, 0,
+                                                      kStreamLoad));
+    const u32x2_t y = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(vb, v_b + n * kTile * kHalf * 2, 0,
+                                                      kStreamLoad));
+    tl.v[n] = __builtin_bit_cast(short4_t, x | y);
+  }
+}
+
 // Q^T operand of one (sequence, KV head), branch-free: column g = row for
 // g < G; the padded columns g >= G repeat head G - 1. Their scores and
 // outputs land in MFMA columns that are never written out, so they only
@@ -686,16 +731,19 @@ __device__ __forceinline__ bool append_new_tokens(const DecodeArgs& a, const int
       const int slot = uniform_load(a.slot_mapping, s.b);
       if (slot >= 0) {
         const size_t src = ((size_t)s.b * Hkv + s.kvh) * D;
-        const int blk = slot / kBlockTokens;
-        const int off = slot - blk * kBlockTokens;
-        const size_t tile = ((size_t)blk * Hkv + s.kvh) * (size_t)(kBlockTokens * D);
+        const int bs = 1 << a.block_shift;
+        const int inner = bs < kTile ? bs : kTile;  // V: dim-major tiles of `inner` slots
+        const int blk = slot >> a.block_shift;
+        const int off = slot & (bs - 1);
+        const size_t region = (((size_t)blk * Hkv + s.kvh) << a.block_shift) * D;
         const bf16_t* kn = (const bf16_t*)a.k_new + src;
         const bf16_t* vn = (const bf16_t*)a.v_new + src;
-        bf16_t* kp = (bf16_t*)a.k_pool + tile + (size_t)off * D;
-        bf16_t* vp = (bf16_t*)a.v_pool + tile + off;
+        bf16_t* kp = (bf16_t*)a.k_pool + region + (size_t)off * D;
+        bf16_t* vp = (bf16_t*)a.v_pool + region + (size_t)(off & ~(inner - 1)) * D +
+                     (off & (inner - 1));
         if (lane < D / 8) *(uint4*)(kp + lane * 8) = *(const uint4*)(kn + lane * 8);
 #pragma unroll
-        for (int d = lane; d < D; d += 64) vp[(size_t)d * kBlockTokens] = vn[d];
+        for (int d = lane; d < D; d += 64) vp[(size_t)d * inner] = vn[d];
         early |= s.fe - 1 <= f0 + 1;
       }
     }
@@ -705,7 +753,14 @@ __device__ __forceinline__ bool append_new_tokens(const DecodeArgs& a, const int
   return early;
 }
 
-template <int D>
+// Block shapes of the balanced kernel: 8-token blocks (two per 16-token
+// tile) or blocks of 16 << k tokens (1 << k tiles each). In the latter every
+// tile is contiguous in both pools: K rows [16, D] and a dim-major V tile
+// [D, 16] (longer blocks store V as one such tile per 16 tokens), both at
+// ((block * Hkv + head) * bs + 16 * sub) * D.
+enum BlockShape { kHalfTileBlocks = 0, kTileBlocks = 1 };
+
+template <int D, int kShape>
 __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a) {
   // dynamic LDS: prefix [B + 1] ints, then per wave an area of
   // balanced_wave_floats(G, D, stage_slots) floats: two parked pieces, the
@@ -730,17 +785,42 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
 
   const bf16_t* kbase = (const bf16_t*)a.k_pool;
   const bf16_t* vbase = (const bf16_t*)a.v_pool;
-  const size_t tile_elems = (size_t)kBlockTokens * D;
-  const size_t block_stride = (size_t)Hkv * tile_elems;
+  // flat positions count 16-token tiles, whatever the block size
+  const int sub_shift = kShape == kHalfTileBlocks ? 0 : a.block_shift - 4;
+  const int sub_mask = (1 << sub_shift) - 1;
+  const LaneOffsets<D> lo(row, kg);
 
   Segment cur = locate(prefix, a.seq_lens, B, Hkv, f0, f1);
   if (a.k_new != nullptr && append_new_tokens<D>(a, prefix, cur, f0, f1, lane))
     wait_stores_complete();
-  auto table_entry = [&](const Segment& sg) {
-    return uniform_load(a.block_tables, (size_t)sg.b * a.max_blocks + sg.j);
+  // physical block(s) of a tile: one, or two for 8-token blocks (the second
+  // read only when the sequence reaches into it)
+  struct Phys {
+    int32_t a, b;
   };
-  auto tile_base = [&](const Segment& sg, int32_t phys) {
-    return (size_t)phys * block_stride + (size_t)sg.kvh * tile_elems;
+  auto table_entry = [&](const Segment& sg) {
+    const size_t rowb = (size_t)sg.b * a.max_blocks;
+    Phys p;
+    if (kShape == kHalfTileBlocks) {
+      const int j0 = 2 * sg.j;
+      p.a = uniform_load(a.block_tables, rowb + j0);
+      p.b = j0 + 1 < ((sg.L + 7) >> 3) ? uniform_load(a.block_tables, rowb + j0 + 1) : p.a;
+    } else {
+      p.a = uniform_load(a.block_tables, rowb + (sg.j >> sub_shift));
+      p.b = p.a;
+    }
+    return p;
+  };
+  auto load_tile_at = [&](Tile<D>& dst, const Segment& sg, const Phys& p) {
+    if (kShape == kHalfTileBlocks) {
+      load_tile_two_blocks<D>(dst, kbase, vbase, ((size_t)p.a * Hkv + sg.kvh) * (8 * D),
+                              ((size_t)p.b * Hkv + sg.kvh) * (8 * D), row, kg);
+    } else {
+      const size_t base =
+          ((((size_t)p.a * Hkv + sg.kvh) << a.block_shift) + (size_t)(sg.j & sub_mask) * kTile) *
+          D;
+      load_tile<D>(dst, kbase + base, vbase + base, lo);
+    }
   };
   // The position after segment position `sg` (flat index `fpos`), which must
   // lie before f1: the next block of the pair, else the next pair.
@@ -754,18 +834,14 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   // a new (sequence, KV head) pair, that pair's Q^T operand. Table entries
   // are read one block further ahead, so a tile's address never waits for
   // its table read.
-  const LaneOffsets<D> lo(row, kg);
   const int qoff = q_lane_offset<D>(a.group, row, kg);
   Tile<D> ta, tb;
   bf16x8_t qa[Tile<D>::kQkSteps], qz[Tile<D>::kQkSteps];
-  int32_t phys_cur = table_entry(cur);
+  Phys phys_cur = table_entry(cur);
   Segment nx = f0 + 1 < f1 ? advance(cur, f0) : cur;
-  int32_t phys_nx = table_entry(nx);
-  {
-    const size_t base = tile_base(cur, phys_cur);
-    load_tile<D>(ta, kbase + base, vbase + base, lo);
-    load_q_clamped<D>(qa, a, cur.b, cur.kvh, qoff);
-  }
+  Phys phys_nx = table_entry(nx);
+  load_tile_at(ta, cur, phys_cur);
+  load_q_clamped<D>(qa, a, cur.b, cur.kvh, qoff);
   WaveState<D> st;
   st.reset();
   PendingPiece pend0{0, 0, 1, 0}, pend1{0, 0, 1, 0};  // at most two cut pieces per wave
@@ -785,12 +861,11 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   // loads unconditional.
   long long f = f0;
   Segment nn = nx;
-  int32_t phys_nn = phys_nx;
+  Phys phys_nn = phys_nx;
   auto prefetch = [&](Tile<D>& dst, bf16x8_t (&qdst)[Tile<D>::kQkSteps],
                       const bf16x8_t (&qsrc)[Tile<D>::kQkSteps], bool more) {
     const Segment sg = more ? nx : cur;
-    const size_t base = tile_base(sg, more ? phys_nx : phys_cur);
-    load_tile<D>(dst, kbase + base, vbase + base, lo);
+    load_tile_at(dst, sg, more ? phys_nx : phys_cur);
     if (sg.b == cur.b && sg.kvh == cur.kvh) {
 #pragma unroll
       for (int c = 0; c < Tile<D>::kQkSteps; ++c) qdst[c] = qsrc[c];
@@ -835,10 +910,15 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
 
 }  // namespace
 
-const void* decode_mfma_fn(int head_dim, bool balanced) {
-  if (balanced)
-    return head_dim == 64 ? (const void*)&decode_mfma_balanced_kernel<64>
-                          : (const void*)&decode_mfma_balanced_kernel<128>;
+const void* decode_mfma_fn(int head_dim, bool balanced, int block_shift) {
+  if (balanced) {
+    const bool half = block_shift == 3;
+    if (head_dim == 64)
+      return half ? (const void*)&decode_mfma_balanced_kernel<64, kHalfTileBlocks>
+                  : (const void*)&decode_mfma_balanced_kernel<64, kTileBlocks>;
+    return half ? (const void*)&decode_mfma_balanced_kernel<128, kHalfTileBlocks>
+                : (const void*)&decode_mfma_balanced_kernel<128, kTileBlocks>;
+  }
   return head_dim == 64 ? (const void*)&decode_mfma_kernel<64>
                         : (const void*)&decode_mfma_kernel<128>;
 }
@@ -853,7 +933,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, 
                               hipStream_t s) {
   DecodeArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(decode_mfma_fn(head_dim, balanced), dim3(grid), dim3(256), args,
+  return hipLaunchKernel(decode_mfma_fn(head_dim, balanced, a.block_shift), dim3(grid), dim3(256), args,
                          decode_mfma_smem(a.num_seqs, a.group, head_dim, balanced,
                                           a.stage_slots), s);
 }

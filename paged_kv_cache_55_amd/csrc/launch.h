@@ -16,7 +16,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, int grid,
                               hipStream_t s);
 const void* decode_valu_fn(int dtype, int head_dim, int group);
-const void* decode_mfma_fn(int head_dim, bool balanced);
+const void* decode_mfma_fn(int head_dim, bool balanced, int block_shift);
 // dynamic LDS bytes of a decode_mfma launch (stage_slots: balanced split only)
 size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced, int stage_slots);
 // Balanced split: fp32 record of one piece of a (sequence, KV head) pair,
@@ -49,7 +49,7 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,
                            int num_tokens, void* k_pool, void* v_pool, int num_kv_heads,
-                           int head_dim, int elem_bytes, hipStream_t s);
+                           int head_dim, int block_shift, int elem_bytes, hipStream_t s);
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
                               size_t block_bytes, hipStream_t s);
 

@@ -85,9 +85,9 @@ def oracle_step(case, rows=None):
         k, v = oracle.copy_blocks(k, v, to_numpy(case.block_mapping))
     if case.slot_mapping is not None:
         k, v = oracle.write_kv(k, v, to_numpy(case.k_new), to_numpy(case.v_new),
-                               to_numpy(case.slot_mapping))
+                               to_numpy(case.slot_mapping), block_size=case.block_size)
     a["k_pool"], a["v_pool"] = k, v
-    return oracle.paged_decode(**a, rows=rows), k, v
+    return oracle.paged_decode(**a, rows=rows, block_size=case.block_size), k, v
 
 
 def bits_equal(gpu_t: torch.Tensor, host: np.ndarray) -> bool:

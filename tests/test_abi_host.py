@@ -112,10 +112,22 @@ def test_decode_rejects_bad_dims(lib, kw, status):
     assert decode_status(lib, dims(**kw)) == status
 
 
-def test_decode_rejects_bad_block_size(lib):
-    d = dims()
-    d.block_size = 32
+@pytest.mark.parametrize("bs", [0, 4, 12, 24, 512, -16])
+def test_decode_rejects_bad_block_size(lib, bs):
+    d = dims(partition_tokens=0)
+    d.block_size = bs
     assert decode_status(lib, d) == pk.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bs", [8, 32, 64, 128, 256])
+def test_other_block_sizes_need_the_balanced_split(lib, bs):
+    # fixed partitions and the vector-ALU kernel take 16-token blocks only
+    for kw in (dict(partition_tokens=512), dict(partition_tokens=0, kernel="valu")):
+        d = dims(**kw)
+        d.block_size = bs
+        assert decode_status(lib, d) == pk.PA_ERR_UNSUPPORTED
+    d = dims(partition_tokens=0, block_size=bs)
+    assert pk.pa_decode_workspace_bytes(d) > 0
 
 
 def test_decode_rejects_bad_kernel_code(lib):

@@ -38,16 +38,18 @@ def np_case(case):
 # contiguous K/V scattered into a pool by the test itself
 # --------------------------------------------------------------------------
 
-def scatter_pool(K_list, V_list, rng, extra_blocks=3):
+def scatter_pool(K_list, V_list, rng, extra_blocks=3, block_size=B16):
     """Pools (float32) holding per-sequence contiguous K/V [Hkv, L, D]
-    at random physical blocks; returns (k_pool, v_pool, tables, lens)."""
+    at random physical blocks of ``block_size`` tokens; returns
+    (k_pool, v_pool, tables, lens)."""
+    B16 = block_size  # noqa: N806 (the block size this pool uses)
     lens = [k.shape[1] for k in K_list]
     Hkv, _, D = K_list[0].shape
     nblk = [math.ceil(L / B16) for L in lens]
     nb = sum(nblk) + extra_blocks
     perm = rng.permutation(nb)
     k_pool = np.full((nb, Hkv, B16, D), np.nan, dtype=np.float32)
-    v_pool = np.full((nb, Hkv, D, B16), np.nan, dtype=np.float32)
+    v_pool = np.full(wl.v_pool_shape(nb, Hkv, D, B16), np.nan, dtype=np.float32)
     mb = max(1, max(nblk))
     tables = np.full((len(lens), mb), perm[-1], dtype=np.int32)
     i = 0
@@ -58,7 +60,11 @@ def scatter_pool(K_list, V_list, rng, extra_blocks=3):
         for t in range(L):
             blk = tables[b, t // B16]
             k_pool[blk, :, t % B16, :] = K_list[b][:, t, :]
-            v_pool[blk, :, :, t % B16] = V_list[b][:, t, :]
+            slot = t % B16
+            if v_pool.ndim == 5:  # a dim-major V tile per 16 slots
+                v_pool[blk, :, slot // 16, :, slot % 16] = V_list[b][:, t, :]
+            else:
+                v_pool[blk, :, :, slot] = V_list[b][:, t, :]
     return k_pool, v_pool, tables, np.array(lens, dtype=np.int32)
 
 
@@ -80,25 +86,26 @@ def sdpa_reference(q, K_list, V_list, scale):
     return out
 
 
-def sdpa_error(seed, B=3, Hq=8, Hkv=2, D=32, max_len=70):
+def sdpa_error(seed, B=3, Hq=8, Hkv=2, D=32, max_len=70, block_size=B16):
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, max_len, size=B)
     K_list = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in lens]
     V_list = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in lens]
     q = rng.standard_normal((B, Hq, D)).astype(np.float32)
     scale = 1.0 / math.sqrt(D)
-    k_pool, v_pool, tables, lens32 = scatter_pool(K_list, V_list, rng)
-    got = oracle.paged_decode(q, k_pool, v_pool, tables, lens32, scale, "f32")
+    k_pool, v_pool, tables, lens32 = scatter_pool(K_list, V_list, rng, block_size=block_size)
+    got = oracle.paged_decode(q, k_pool, v_pool, tables, lens32, scale, "f32",
+                              block_size=block_size)
     ref = sdpa_reference(q, K_list, V_list, scale)
     err = np.abs(got - ref)
     return float("inf") if np.isnan(err).any() else float(np.max(err))
 
 
-def brute_error(seed, B=3, Hq=4, Hkv=2, D=8, max_len=40, dtype="f32"):
-    case = wl.random_case(seed, B, Hq, Hkv, D, dtype, max_len=max_len)
+def brute_error(seed, B=3, Hq=4, Hkv=2, D=8, max_len=40, dtype="f32", block_size=B16):
+    case = wl.random_case(seed, B, Hq, Hkv, D, dtype, max_len=max_len, block_size=block_size)
     a = np_case(case)
-    got = oracle.paged_decode(**a)
-    ref = oracle.brute_force_decode(**a)
+    got = oracle.paged_decode(**a, block_size=block_size)
+    ref = oracle.brute_force_decode(**a, block_size=block_size)
     return float(np.max(np.abs(got - ref))) if got.size else 0.0
 
 
@@ -111,6 +118,18 @@ def brute_error(seed, B=3, Hq=4, Hkv=2, D=8, max_len=40, dtype="f32"):
 def test_brute_force_tiny(seed, G, dtype):
     Hkv = 2
     assert brute_error(seed, Hq=G * Hkv, Hkv=Hkv, dtype=dtype) < 1e-12
+
+
+@pytest.mark.parametrize("bs", [8, 32, 64, 256])
+def test_brute_force_other_block_sizes(bs):
+    """Blocks of other sizes (the block-size sweep): the table walk indexes
+    block t // bs at slot t % bs."""
+    assert brute_error(70 + bs, Hq=8, Hkv=2, max_len=300, dtype="bf16", block_size=bs) < 1e-12
+
+
+@pytest.mark.parametrize("bs", [8, 32, 256])
+def test_sdpa_library_other_block_sizes(bs):
+    assert sdpa_error(30 + bs, max_len=600, block_size=bs) < 1e-12
 
 
 def test_brute_force_config1():
@@ -220,16 +239,17 @@ def test_physical_placement_invariance_bitwise(dtype):
     np.testing.assert_array_equal(oracle.paged_decode(**a), oracle.paged_decode(**b))
 
 
-def test_paged_equals_contiguous_bitwise():
+@pytest.mark.parametrize("bs", [16, 8, 64, 256])
+def test_paged_equals_contiguous_bitwise(bs):
     rng = np.random.default_rng(41)
     Hkv, D = 2, 32
-    lens = [5, 16, 33, 64]
+    lens = [5, 16, 33, 64, 300]
     K_list = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in lens]
     V_list = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in lens]
-    q = rng.standard_normal((4, 4, D)).astype(np.float32)
-    k_pool, v_pool, tables, lens32 = scatter_pool(K_list, V_list, rng)
-    paged = oracle.paged_decode(q, k_pool, v_pool, tables, lens32, 0.3, "f32")
-    for b in range(4):
+    q = rng.standard_normal((5, 4, D)).astype(np.float32)
+    k_pool, v_pool, tables, lens32 = scatter_pool(K_list, V_list, rng, block_size=bs)
+    paged = oracle.paged_decode(q, k_pool, v_pool, tables, lens32, 0.3, "f32", block_size=bs)
+    for b in range(5):
         contig = oracle.decode_contiguous(q[b].astype(np.float64),
                                           K_list[b].astype(np.float64),
                                           V_list[b].astype(np.float64), 0.3)

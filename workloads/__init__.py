@@ -90,6 +90,10 @@ class Case:
     def max_blocks_per_seq(self):
         return self.block_tables.shape[1]
 
+    @property
+    def block_size(self):
+        return self.k_pool.shape[2]
+
     def kv_bytes(self) -> int:
         """Bytes of K and V the decode must read: valid tokens only."""
         elem = 4 if self.dtype == "f32" else 2
@@ -126,31 +130,53 @@ def _poison_value(dtype: str):
     return float("nan")
 
 
-def _poison_tails(k_pool, v_pool, tables, lens):
+def v_pool_shape(num_blocks, num_kv_heads, head_dim, block_size):
+    """V pool layout: [NB, Hkv, D, bs] (dim-major blocks) up to 16 tokens per
+    block; longer blocks are a run of 16-token dim-major tiles,
+    [NB, Hkv, bs // 16, D, 16]."""
+    if block_size <= BLOCK:
+        return (num_blocks, num_kv_heads, head_dim, block_size)
+    return (num_blocks, num_kv_heads, block_size // BLOCK, head_dim, BLOCK)
+
+
+def set_v_slot(v_pool, blk, pos, value):
+    """v_pool[blk, :, slot pos, :] = value in either V layout."""
+    if v_pool.dim() == 5:
+        v_pool[blk, :, pos // BLOCK, :, pos % BLOCK] = value
+    else:
+        v_pool[blk, :, :, pos] = value
+
+
+def _poison_tails(k_pool, v_pool, tables, lens, block_size=BLOCK):
     """NaN in every slot at or past L inside a sequence's last block."""
     for b, L in enumerate(lens.tolist()):
-        if L % BLOCK == 0:
+        if L % block_size == 0:
             continue
-        blk = int(tables[b, L // BLOCK])
-        k_pool[blk, :, L % BLOCK:, :] = float("nan")
-        v_pool[blk, :, :, L % BLOCK:] = float("nan")
+        blk = int(tables[b, L // block_size])
+        k_pool[blk, :, L % block_size:, :] = float("nan")
+        for pos in range(L % block_size, block_size):
+            set_v_slot(v_pool, blk, pos, float("nan"))
 
 
-def place_blocks(lens, rng, pool_blocks=None, mb=None, consecutive=False):
+def place_blocks(lens, rng, pool_blocks=None, mb=None, consecutive=False, block_size=BLOCK):
     """Assign physical blocks to every logical block of every sequence.
 
     Returns (tables int32 [B, MB], num_blocks, poison_block). Physical ids
-    come from a seeded permutation of the pool; logical blocks take
-    consecutive entries of it in (sequence, block) order. One block outside
-    all tables is the poison block that unused table entries name.
+    come from a seeded permutation of the pool (``consecutive``: the
+    identity, so every sequence's blocks are physically contiguous and the
+    sequences lie back to back); logical blocks take consecutive entries of
+    it in (sequence, block) order. One block outside all tables is the
+    poison block that unused table entries name.
     """
     lens = np.asarray(lens, dtype=np.int64)
-    nblk = [math.ceil(int(L) / BLOCK) for L in lens]
+    nblk = [math.ceil(int(L) / block_size) for L in lens]
     total = int(sum(nblk))
     nb = pool_blocks if pool_blocks is not None else total + 1
     if nb < total + 1:
         raise ValueError("pool too small for the tables plus a poison block")
     perm = rng.permutation(nb)
+    if consecutive:
+        perm = np.arange(nb)
     width = mb if mb is not None else max(1, max(nblk) if nblk else 1)
     poison = int(perm[total])
     tables = np.full((len(lens), width), poison, dtype=np.int32)
@@ -165,7 +191,8 @@ def place_blocks(lens, rng, pool_blocks=None, mb=None, consecutive=False):
 
 def build_case(name, lens, num_q_heads, num_kv_heads, head_dim, dtype, seed,
                *, pool_blocks=None, mb=None, with_write=False,
-               partition_tokens=512, scale=None) -> Case:
+               partition_tokens=512, scale=None, block_size=BLOCK,
+               placement="random") -> Case:
     """A decode batch with the given lengths and random block placement.
 
     With ``with_write`` the newest token of each sequence (position L - 1)
@@ -176,18 +203,22 @@ def build_case(name, lens, num_q_heads, num_kv_heads, head_dim, dtype, seed,
     rng = np.random.default_rng(seed)
     gen = torch.Generator().manual_seed(seed)
     lens = np.asarray(lens, dtype=np.int64)
-    tables, nb, poison = place_blocks(lens, rng, pool_blocks, mb)
+    if placement not in ("random", "contiguous"):
+        raise ValueError("placement is 'random' or 'contiguous'")
+    bs = int(block_size)
+    tables, nb, poison = place_blocks(lens, rng, pool_blocks, mb,
+                                      consecutive=placement == "contiguous", block_size=bs)
     B = len(lens)
     q = _randn(gen, (B, num_q_heads, head_dim), dtype)
-    k_pool = _randn(gen, (nb, num_kv_heads, BLOCK, head_dim), dtype)
-    v_pool = _randn(gen, (nb, num_kv_heads, head_dim, BLOCK), dtype)
+    k_pool = _randn(gen, (nb, num_kv_heads, bs, head_dim), dtype)
+    v_pool = _randn(gen, v_pool_shape(nb, num_kv_heads, head_dim, bs), dtype)
     used = np.zeros(nb, dtype=bool)
     for b, L in enumerate(lens.tolist()):
-        used[tables[b, :math.ceil(L / BLOCK)]] = True
+        used[tables[b, :math.ceil(L / bs)]] = True
     unused = torch.from_numpy(np.nonzero(~used)[0])
     k_pool[unused] = float("nan")
     v_pool[unused] = float("nan")
-    _poison_tails(k_pool, v_pool, tables, lens)
+    _poison_tails(k_pool, v_pool, tables, lens, bs)
     case = Case(name, dtype, q, k_pool, v_pool,
                 torch.from_numpy(tables), torch.from_numpy(lens.astype(np.int32)),
                 scale if scale is not None else 1.0 / math.sqrt(head_dim),
@@ -200,10 +231,10 @@ def build_case(name, lens, num_q_heads, num_kv_heads, head_dim, dtype, seed,
             if L == 0:
                 continue
             pos = L - 1
-            blk = int(tables[b, pos // BLOCK])
-            slots[b] = blk * BLOCK + pos % BLOCK
-            k_pool[blk, :, pos % BLOCK, :] = float("nan")
-            v_pool[blk, :, :, pos % BLOCK] = float("nan")
+            blk = int(tables[b, pos // bs])
+            slots[b] = blk * bs + pos % bs
+            k_pool[blk, :, pos % bs, :] = float("nan")
+            set_v_slot(v_pool, blk, pos % bs, float("nan"))
         case.k_new, case.v_new = k_new, v_new
         case.slot_mapping = torch.from_numpy(slots)
     return case
@@ -229,16 +260,19 @@ def config2_lens(seed=SEED_BASE + 2, batch=64):
     return rng.integers(128, 4096, size=batch, endpoint=True)
 
 
-def config2(batch: int = 64) -> Case:
+def config2(batch: int = 64, block_size: int = BLOCK, placement: str = "random") -> Case:
     """Llama-3-8B-shaped layer: bf16, 32/8 heads, D = 128, B = 64.
 
     Lengths uniform in [128, 4096]; the pool holds exactly the needed blocks
-    plus one poison block, randomly permuted; the newest token of every
-    sequence is appended through ``slot_mapping`` before decoding.
+    plus one poison block, randomly permuted (or, for the contiguity sweep,
+    in order); the newest token of every sequence is appended through
+    ``slot_mapping`` before decoding. ``block_size`` other than 16 serves
+    the block-size sweep.
     """
     lens = config2_lens(batch=batch)
     return build_case("config2_llama3_8b_layer", lens, 32, 8, 128, "bf16",
-                      SEED_BASE + 2, with_write=True)
+                      SEED_BASE + 2, with_write=True, block_size=block_size,
+                      placement=placement)
 
 
 def config4_lens(seed=SEED_BASE + 4, batch=256):
@@ -247,15 +281,16 @@ def config4_lens(seed=SEED_BASE + 4, batch=256):
     return np.clip(np.rint(np.exp(math.log(1024.0) + 1.0 * z)), 16, 8192).astype(np.int64)
 
 
-def config4(batch: int = 256) -> Case:
+def config4(batch: int = 256, block_size: int = BLOCK, placement: str = "random") -> Case:
     """Llama-3.3-70B-shaped layer: bf16, 64/8 heads (GQA 8), D = 128, B = 256.
 
     Lengths lognormal with median 1024 and sigma 1, clipped to [16, 8192];
-    randomly permuted physical blocks.
+    randomly permuted physical blocks (``placement`` and ``block_size`` as
+    for the 8B layer).
     """
     lens = config4_lens(batch=batch)
     return build_case("config4_llama3_70b_layer", lens, 64, 8, 128, "bf16",
-                      SEED_BASE + 4)
+                      SEED_BASE + 4, block_size=block_size, placement=placement)
 
 
 def config3() -> Case:
@@ -412,15 +447,18 @@ def config5_layer(spec: StepSpec, layer: int, device) -> tuple:
 
 def random_case(seed, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                 max_len=300, min_len=0, lens=None, with_write=False,
-                partition_tokens=512, extra_table_cols=0) -> Case:
+                partition_tokens=512, extra_table_cols=0, block_size=BLOCK,
+                placement="random") -> Case:
     rng = np.random.default_rng([seed, 1])
     if lens is None:
         lens = rng.integers(min_len, max_len, size=batch, endpoint=True)
     lens = np.asarray(lens, dtype=np.int64)
-    mb = max(1, max((math.ceil(int(L) / BLOCK) for L in lens), default=1)) + extra_table_cols
+    mb = max(1, max((math.ceil(int(L) / block_size) for L in lens), default=1)) \
+        + extra_table_cols
     return build_case(f"random_{seed}", lens, num_q_heads, num_kv_heads,
                       head_dim, dtype, seed, mb=mb, with_write=with_write,
-                      partition_tokens=partition_tokens)
+                      partition_tokens=partition_tokens, block_size=block_size,
+                      placement=placement)
 
 
 def permute_physical(case: Case, seed: int) -> Case:
