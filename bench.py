@@ -45,8 +45,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s per layer"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
-    "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h", "worklist.h"],
-    "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h", "worklist.h"],
+    "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
+    "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
 }
 
 
@@ -72,6 +72,8 @@ def parse():
                          "and time its replays")
     ap.add_argument("--step", default="separate", choices=["fused", "separate"],
                     help="8B batch: append + decode in one call, or two calls")
+    ap.add_argument("--no-other-form", action="store_true",
+                    help="8B batch: do not also time the other form of the step (profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget for the oracle baseline (0 = skip)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -238,7 +240,7 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = timed_steps(args.step)
     other_ms = None
-    if args.config == 2:  # the other form of the same step, for comparison
+    if args.config == 2 and not args.no_other_form:  # the other form, for comparison
         other = "separate" if args.step == "fused" else "fused"
         for i in range(args.warmup):
             step(i, mode=other)
