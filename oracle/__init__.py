@@ -11,7 +11,8 @@ helpers or constants. The two meet only through the seeded inputs that
 ``workloads`` produces and that callers pass to both sides.
 
 Modules
-  attention  paged decode attention, KV append (write) and block copy
+  attention  paged decode and chunked-prefill attention, KV append (write)
+             and block copy
   pages      page / block-table arithmetic of the admission ledger
 
 Every function names the passage of the pages it follows. No function here
@@ -27,6 +28,7 @@ from .attention import (  # noqa: F401
     gather_sequence,
     decode_contiguous,
     paged_decode,
+    paged_prefill,
     brute_force_decode,
     write_kv,
     copy_blocks,

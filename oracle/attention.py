@@ -176,6 +176,40 @@ def paged_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, dtype,
     return out
 
 
+def paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale,
+                  dtype, block_size=BLOCK_SIZE, seqs=None):
+    """Chunked-prefill paged attention for a batch, in float64.
+
+    q [T, Hq, D] holds the query tokens of every sequence back to back:
+    sequence s owns rows query_start[s] .. query_start[s + 1] - 1, its
+    newest n_s tokens, at positions L_s - n_s .. L_s - 1 (L_s = seq_lens[s]
+    counts them, and their K/V are already in the pool). The query token at
+    position p attends to the sequence's tokens 0 .. p: a chunk of a long
+    prompt sees the earlier chunks and, causally, itself, and a sequence
+    with one query token is a decode row ["The inference server"
+    (srikanthmalla.com), the answer on prefill and decode competing for the
+    device: chunked prefill runs pieces of a prompt in the same step as
+    decode rows; cs2680 Lecture 10, §10.3 for the table walk]. ``seqs``
+    restricts the work to some sequences (other rows stay zero).
+    """
+    T, Hq, D = q.shape
+    out = np.zeros((T, Hq, D))
+    seqs = range(len(seq_lens)) if seqs is None else seqs
+    for s in seqs:
+        r0, r1 = int(query_start[s]), int(query_start[s + 1])
+        n, L = r1 - r0, int(seq_lens[s])
+        if n == 0:
+            continue
+        if n > L:
+            raise ValueError(f"sequence {s}: {n} query tokens but length {L}")
+        K, V = gather_sequence(k_pool, v_pool, block_tables[s], L, dtype, block_size)
+        for i in range(n):
+            p = L - n + i
+            out[r0 + i] = decode_contiguous(as_f64(q[r0 + i], dtype), K[:, :p + 1],
+                                            V[:, :p + 1], scale)
+    return out
+
+
 def brute_force_decode(q, k_pool, v_pool, block_tables, seq_lens, scale,
                        dtype, block_size=BLOCK_SIZE):
     """Same quantity as ``paged_decode`` with scalar Python loops.

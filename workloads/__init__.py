@@ -64,6 +64,7 @@ class Case:
     slot_mapping: Optional[torch.Tensor] = None
     block_mapping: Optional[torch.Tensor] = None
     meta: dict = field(default_factory=dict)
+    query_start: Optional[torch.Tensor] = None  # chunked prefill: int32 [S + 1]
 
     # shapes
     @property
@@ -107,7 +108,7 @@ class Case:
                     mv(self.v_pool), mv(self.block_tables), mv(self.seq_lens),
                     self.scale, self.partition_tokens, self.poison_block,
                     mv(self.k_new), mv(self.v_new), mv(self.slot_mapping),
-                    mv(self.block_mapping), dict(self.meta))
+                    mv(self.block_mapping), dict(self.meta), mv(self.query_start))
 
 
 def to_numpy(t: torch.Tensor) -> np.ndarray:
@@ -459,6 +460,66 @@ def random_case(seed, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                       head_dim, dtype, seed, mb=mb, with_write=with_write,
                       partition_tokens=partition_tokens, block_size=block_size,
                       placement=placement)
+
+
+def prefill_case(seed, chunks, contexts, num_q_heads, num_kv_heads, head_dim, dtype="bf16",
+                 block_size=BLOCK, name=None) -> Case:
+    """A chunked-prefill batch: sequence s has ``contexts[s]`` tokens cached
+    and appends a chunk of ``chunks[s]`` new tokens (length
+    L_s = contexts[s] + chunks[s]). q is [T, Hq, D] with T = sum(chunks),
+    sequence s owning rows query_start[s] .. query_start[s + 1] - 1. The
+    chunk's K/V come as k_new / v_new [T, Hkv, D] with their slots in
+    slot_mapping (positions L_s - n_s .. L_s - 1, in order); those slots are
+    poisoned in the pool until the append writes them."""
+    chunks = np.asarray(chunks, dtype=np.int64)
+    contexts = np.asarray(contexts, dtype=np.int64)
+    lens = contexts + chunks
+    rng = np.random.default_rng([seed, 7])
+    gen = torch.Generator().manual_seed(seed)
+    bs = int(block_size)
+    tables, nb, poison = place_blocks(lens, rng, block_size=bs)
+    T = int(chunks.sum())
+    S = len(lens)
+    q = _randn(gen, (T, num_q_heads, head_dim), dtype)
+    k_pool = _randn(gen, (nb, num_kv_heads, bs, head_dim), dtype)
+    v_pool = _randn(gen, v_pool_shape(nb, num_kv_heads, head_dim, bs), dtype)
+    used = np.zeros(nb, dtype=bool)
+    for b, L in enumerate(lens.tolist()):
+        used[tables[b, :math.ceil(L / bs)]] = True
+    unused = torch.from_numpy(np.nonzero(~used)[0])
+    k_pool[unused] = float("nan")
+    v_pool[unused] = float("nan")
+    _poison_tails(k_pool, v_pool, tables, lens, bs)
+    k_new = _randn(gen, (T, num_kv_heads, head_dim), dtype)
+    v_new = _randn(gen, (T, num_kv_heads, head_dim), dtype)
+    slots = np.empty(T, dtype=np.int32)
+    qs = np.zeros(S + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(chunks)
+    for b in range(S):
+        for i in range(int(chunks[b])):
+            pos = int(contexts[b]) + i
+            blk = int(tables[b, pos // bs])
+            slots[qs[b] + i] = blk * bs + pos % bs
+            k_pool[blk, :, pos % bs, :] = float("nan")
+            set_v_slot(v_pool, blk, pos % bs, float("nan"))
+    case = Case(name or f"prefill_{seed}", dtype, q, k_pool, v_pool, torch.from_numpy(tables),
+                torch.from_numpy(lens.astype(np.int32)), 1.0 / math.sqrt(head_dim), 0,
+                poison)
+    case.k_new, case.v_new = k_new, v_new
+    case.slot_mapping = torch.from_numpy(slots)
+    case.query_start = torch.from_numpy(qs)
+    return case
+
+
+def prefill_step_8b(num_chunks: int = 8, chunk: int = 512, block_size: int = BLOCK) -> Case:
+    """One chunked-prefill step on an 8B-shaped layer (bf16, 32/8 heads,
+    D = 128): ``num_chunks`` prompts, each at a different point of its
+    prefill, contribute one ``chunk``-token piece; prompt s has s * chunk
+    tokens cached (the pieces of one 4,096-token prompt at 8 x 512, side
+    by side)."""
+    contexts = [s * chunk for s in range(num_chunks)]
+    return prefill_case(SEED_BASE + 6, [chunk] * num_chunks, contexts, 32, 8, 128, "bf16",
+                        block_size=block_size, name="prefill_step_llama3_8b_8x512")
 
 
 def permute_physical(case: Case, seed: int) -> Case:
