@@ -148,6 +148,30 @@ pa_status pa_decode_append(const void* q, const void* k_new, const void* v_new,
                            float scale, void* out, const pa_dims* dims,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked-prefill paged attention. Sequence s owns the query rows
+ * query_start[s] .. query_start[s+1]-1 of q ([T, Hq, D], T =
+ * num_query_tokens = query_start[num_seqs]): its newest
+ * n_s = query_start[s+1] - query_start[s] tokens, at positions
+ * seq_lens[s] - n_s .. seq_lens[s] - 1, whose K/V are already in the pools
+ * (written by pa_write_kv). The query token at position p attends to the
+ * sequence's tokens 0 .. p:
+ *   out[r,h,:] = sum_{t<=p} softmax_t(scale * <q[r,h,:], K_s[t]>) V_s[t]
+ * with K_s/V_s gathered through block_tables[s] and KV head h / (Hq / Hkv).
+ * A long prompt is prefilled in pieces of a few hundred tokens that share a
+ * step with decode rows; each piece sees the earlier pieces and itself
+ * ["The inference server" (srikanthmalla.com), the answer on prefill and
+ * decode competing for the device]. A sequence with n_s = 1 is a decode
+ * row, n_s = 0 a row with nothing to do. Matrix-core kernel: bf16, D = 64
+ * or 128, block_size >= 16 (PA_ERR_UNSUPPORTED otherwise); no workspace.
+ * The caller guarantees 0 = query_start[0] <= ... <= query_start[num_seqs]
+ * = num_query_tokens and n_s <= seq_lens[s]; other values give undefined
+ * results. out[r] is written for every query row r; bf16 rounding is to
+ * nearest even. dims->partition_tokens and dims->kernel are ignored. */
+pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     const int32_t* query_start, int32_t num_query_tokens, float scale,
+                     void* out, const pa_dims* dims, void* stream);
+
 /* KV append: for t < num_tokens with s = slot_mapping[t] >= 0,
  *   k_pool[s / BS, h, s % BS, :] = k_new[t, h, :]
  *   v_pool[s / BS, h, :, s % BS] = v_new[t, h, :]   for every KV head h.

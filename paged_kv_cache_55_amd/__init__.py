@@ -9,6 +9,7 @@ missing build is an error: there is no fallback path.
     pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, ...)
     pa_decode_append(q, k_new, v_new, slot_mapping, k_pool, v_pool,
                      block_tables, seq_lens, scale, out, ...)
+    pa_prefill(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale, out)
     pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool)
     pa_copy_blocks(k_pool, v_pool, block_mapping)
     pa_decode_workspace_bytes(dims)
@@ -30,7 +31,7 @@ from .build import LIB_PATH
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_LAUNCH",
     "PaDims", "PagedKVError", "SYMBOLS", "load_library", "make_dims",
-    "pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_write_kv",
+    "pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_prefill", "pa_write_kv",
     "pa_copy_blocks",
     "pa_status_string", "pa_version", "validate",
 ]
@@ -40,8 +41,8 @@ PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 BLOCK_SIZE = 16
 
-SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_append", "pa_write_kv",
-           "pa_copy_blocks", "pa_status_string", "pa_version")
+SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_append", "pa_prefill",
+           "pa_write_kv", "pa_copy_blocks", "pa_status_string", "pa_version")
 
 
 class PaDims(ctypes.Structure):
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode_append.argtypes = [P, P, P, P, P, P, P, P, F32, P, D, P, SZ, P]
     lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [P, P, P, P, P, P, I32, F32, P, D, P]
+    lib.pa_prefill.restype = ctypes.c_int
     lib.pa_write_kv.argtypes = [P, P, P, I32, P, P, D, P]
     lib.pa_write_kv.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
@@ -241,6 +244,38 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_tables
         ctypes.byref(dims), _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream))
     if st != PA_OK:
         raise PagedKVError("pa_decode_append", st)
+    return out
+
+
+def pa_prefill(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale, out=None, *,
+               stream=None):
+    """Chunked-prefill attention: sequence s owns q rows query_start[s] ..
+    query_start[s + 1] - 1 (its newest tokens, already in the pools), each
+    attending causally to the sequence's tokens up to its own position."""
+    torch = _torch()
+    NB, Hkv, D, BS = _pool_dims(k_pool, v_pool)
+    _need(q.dim() == 3 and q.shape[2] == D and q.dtype == k_pool.dtype
+          and q.is_contiguous() and q.is_cuda, "q must be [T, Hq, D] like the pools")
+    T, Hq, _ = q.shape
+    S = seq_lens.shape[0]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S and block_tables.is_contiguous()
+          and block_tables.is_cuda, "block_tables must be int32 [S, MB] on the device")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1 and seq_lens.is_contiguous()
+          and seq_lens.is_cuda, "seq_lens must be int32 [S] on the device")
+    _need(query_start.dtype == torch.int32 and tuple(query_start.shape) == (S + 1,)
+          and query_start.is_contiguous() and query_start.is_cuda,
+          "query_start must be int32 [S + 1] on the device")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
+          and out.is_cuda, "out must match q")
+    dims = make_dims(S, Hq, Hkv, D, block_tables.shape[1], NB, _dtype_code(q), 0, "mfma", BS)
+    st = load_library().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                   _ptr(seq_lens), _ptr(query_start), T, ctypes.c_float(scale),
+                                   _ptr(out), ctypes.byref(dims), _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_prefill", st)
     return out
 
 

@@ -52,6 +52,8 @@ int pick_kernel(const pa_dims* d) {
 // keeps enough loads in flight.
 constexpr int kMaxBalancedGrid = 256;
 constexpr int kMinSegBlocks = 16;
+// Chunked prefill: at most this many persistent workgroups.
+constexpr int kMaxPrefillGrid = 1024;
 
 struct Plan {
   int kernel;       // PA_KERNEL_VALU or PA_KERNEL_MFMA
@@ -286,6 +288,48 @@ pa_status pa_decode_append(const void* q, const void* k_new, const void* v_new,
   if (!k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
   return decode_impl(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_tables, seq_lens,
                      scale, out, dims, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     const int32_t* query_start, int32_t num_query_tokens, float scale,
+                     void* out, const pa_dims* dims, void* stream) {
+  pa_status st = check_pool(dims);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs < 1 || dims->num_q_heads < 1 || dims->max_blocks_per_seq < 1)
+    return PA_ERR_INVALID_ARG;
+  if (dims->num_q_heads % dims->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (num_query_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (dims->dtype != PA_BF16 || dims->block_size < kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (dims->num_seqs > kMaxSeqs || dims->max_blocks_per_seq > (1 << 26))
+    return PA_ERR_UNSUPPORTED;
+  if (num_query_tokens == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+
+  PrefillArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start = query_start;
+  a.out = out;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = dims->num_seqs;
+  a.num_q_heads = dims->num_q_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.group = dims->num_q_heads / dims->num_kv_heads;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.block_shift = block_shift(dims->block_size);
+  int resident = 0;
+  hipError_t e = resident_workgroups(prefill_mfma_fn(dims->head_dim),
+                                     (size_t)(dims->num_seqs + 1) * sizeof(int), &resident);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  const int grid = resident < kMaxPrefillGrid ? resident : kMaxPrefillGrid;
+  e = launch_prefill_mfma(a, dims->head_dim, grid, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 pa_status pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,

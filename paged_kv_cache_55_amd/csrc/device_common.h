@@ -158,4 +158,17 @@ struct DecodeArgs {
   const int32_t* slot_mapping;
 };
 
+// Everything the chunked-prefill kernel needs; passed by value.
+struct PrefillArgs {
+  const void* q;             // [T, Hq, D]
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;     // [S], the chunk included
+  const int32_t* query_start;  // [S + 1]: rows of q owned by each sequence
+  void* out;                   // [T, Hq, D]
+  float scale_log2;
+  int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, block_shift;
+};
+
 }  // namespace pagedkv

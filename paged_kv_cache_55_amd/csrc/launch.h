@@ -47,6 +47,11 @@ inline int balanced_stage_slots(int num_seqs, int group, int head_dim, size_t ld
 }
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
 
+// Chunked-prefill attention (bf16, blocks of 16 or more tokens): persistent
+// grid of `grid` workgroups, dynamic LDS of (num_seqs + 1) ints.
+const void* prefill_mfma_fn(int head_dim);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int head_dim, int grid, hipStream_t s);
+
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,
                            int num_tokens, void* k_pool, void* v_pool, int num_kv_heads,
                            int head_dim, int block_shift, int elem_bytes, hipStream_t s);

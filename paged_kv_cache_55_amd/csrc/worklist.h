@@ -43,18 +43,10 @@ __device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int
   return base + inc - v;
 }
 
-// prefix[0..B] <- exclusive prefix of ceil(L_b / part_tokens) (0 for L_b <= 0).
-// Needs blockDim.x == 256 and B <= kMaxSeqs. The lengths are read with
-// coalesced loads into LDS, then each thread scans a contiguous chunk.
-// Ends with a barrier.
-__device__ __forceinline__ void build_partition_prefix(const int32_t* __restrict__ seq_lens, int B,
-                                                       int part_tokens, int* prefix,
-                                                       int* scratch) {
-  for (int i = threadIdx.x; i < B; i += blockDim.x) {
-    const int L = seq_lens[i];
-    prefix[i] = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
-  }
-  __syncthreads();
+// prefix[0..B] <- exclusive prefix of the counts already in prefix[0..B-1].
+// Needs blockDim.x == 256 and B <= kMaxSeqs; each thread scans a contiguous
+// chunk. Ends with a barrier.
+__device__ __forceinline__ void scan_counts_in_place(int B, int* prefix, int* scratch) {
   const int chunk = (B + 255) / 256;  // <= 16
   const int first = threadIdx.x * chunk;
   int counts[kMaxSeqs / 256];
@@ -76,6 +68,20 @@ __device__ __forceinline__ void build_partition_prefix(const int32_t* __restrict
   }
   if (threadIdx.x == 0) prefix[B] = total;
   __syncthreads();
+}
+
+// prefix[0..B] <- exclusive prefix of ceil(L_b / part_tokens) (0 for L_b <= 0).
+// Needs blockDim.x == 256 and B <= kMaxSeqs. The lengths are read with
+// coalesced loads into LDS, then scanned. Ends with a barrier.
+__device__ __forceinline__ void build_partition_prefix(const int32_t* __restrict__ seq_lens, int B,
+                                                       int part_tokens, int* prefix,
+                                                       int* scratch) {
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const int L = seq_lens[i];
+    prefix[i] = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
+  }
+  __syncthreads();
+  scan_counts_in_place(B, prefix, scratch);
 }
 
 // Sequence owning partition index j: the largest b with prefix[b] <= j.

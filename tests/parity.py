@@ -3,12 +3,16 @@ binding, run the oracle on the same seeded inputs, compare.
 
 Tolerances (spec bar):
   f32   max |gpu - oracle| <= 2e-3 over every element;
-  bf16  for every sequence b, max |gpu - oracle| <= 2e-2 * RMS(oracle[b]),
-        the RMS taken over all query heads and dims of that sequence, and the
-        oracle unrounded (float64). Output magnitudes scale like
-        sqrt(e / L), so sequences of different lengths are normalised by
-        their own RMS; bf16 output rounding alone costs up to 2^-8 of an
-        element's magnitude.
+  bf16  for every row b (a sequence in decode, a query token in prefill) and
+        element e:
+            |gpu - oracle| <= 2e-2 * RMS(oracle[b]) + 2^-8 * |oracle[b, e]|,
+        the RMS taken over all query heads and dims of the row and the oracle
+        unrounded (float64). The first term is the arithmetic budget,
+        relative to the row's own output RMS (output magnitudes scale like
+        sqrt(e / L), so rows of different lengths are normalised by their
+        own RMS); the second is the bf16 output format's own rounding (half
+        an ulp is at most 2^-8 of the value), which even the correctly
+        rounded exact result needs on rows with a few large elements.
   Padded rows (L = 0) must be exact zeros (bitwise).
 """
 
@@ -23,6 +27,7 @@ from workloads import to_numpy
 
 F32_ATOL = 2e-3
 BF16_RMS_RTOL = 2e-2
+BF16_ROUNDING = 2.0 ** -8
 
 
 def gpu_out_f64(out: torch.Tensor, rows=None) -> np.ndarray:
@@ -42,15 +47,17 @@ def compare(got: np.ndarray, ref: np.ndarray, lens, dtype: str) -> float:
             assert np.all(got[i] == 0.0), f"row {i}: padded row not zero"
             continue
         assert np.all(np.isfinite(got[i])), f"row {i}: non-finite output"
-        err = float(np.max(np.abs(got[i] - ref[i])))
+        err = np.abs(got[i] - ref[i])
         if dtype == "f32":
-            allowed = F32_ATOL
+            allowed = np.full(err.shape, F32_ATOL)
         else:
             rms = float(np.sqrt(np.mean(ref[i] ** 2)))
-            allowed = BF16_RMS_RTOL * rms
+            allowed = BF16_RMS_RTOL * rms + BF16_ROUNDING * np.abs(ref[i])
         ratio = err / allowed
-        worst = max(worst, ratio)
-        assert err <= allowed, f"row {i} (L={L}): max err {err:.3e} > {allowed:.3e}"
+        k = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        worst = max(worst, float(ratio[k]))
+        assert ratio[k] <= 1.0, (f"row {i} (L={L}): err {err[k]:.3e} > allowed "
+                                 f"{allowed[k]:.3e} at {k}")
     return worst
 
 
@@ -95,3 +102,15 @@ def bits_equal(gpu_t: torch.Tensor, host: np.ndarray) -> bool:
     g = np.ascontiguousarray(to_numpy(gpu_t))
     h = np.ascontiguousarray(host)
     return g.shape == h.shape and np.array_equal(g.view(np.uint8), h.view(np.uint8))
+
+
+def oracle_prefill(case):
+    """The oracle's chunk append then chunked-prefill attention; returns
+    (out, k, v) on the host."""
+    k, v = oracle.write_kv(to_numpy(case.k_pool), to_numpy(case.v_pool), to_numpy(case.k_new),
+                           to_numpy(case.v_new), to_numpy(case.slot_mapping),
+                           block_size=case.block_size)
+    out = oracle.paged_prefill(to_numpy(case.q), k, v, to_numpy(case.block_tables),
+                               to_numpy(case.seq_lens), to_numpy(case.query_start), case.scale,
+                               case.dtype, block_size=case.block_size)
+    return out, k, v

@@ -179,6 +179,20 @@ def test_append_rejects_null_new_tokens(lib):
     assert st == pk.PA_ERR_INVALID_ARG
 
 
+def prefill_status(lib, d, tokens=8, q=FAKE, qs=FAKE):
+    return lib.pa_prefill(q, FAKE, FAKE, FAKE, FAKE, qs, tokens, ctypes.c_float(0.1), FAKE,
+                          ctypes.byref(d), None)
+
+
+def test_prefill_host_checks(lib):
+    assert prefill_status(lib, dims(dtype=pk.PA_F32)) == pk.PA_ERR_UNSUPPORTED
+    assert prefill_status(lib, dims(block_size=8)) == pk.PA_ERR_UNSUPPORTED
+    assert prefill_status(lib, dims(), qs=None) == pk.PA_ERR_INVALID_ARG
+    assert prefill_status(lib, dims(), tokens=-1) == pk.PA_ERR_INVALID_ARG
+    assert prefill_status(lib, dims(num_q_heads=12)) == pk.PA_ERR_INVALID_ARG
+    assert prefill_status(lib, dims(), tokens=0) == pk.PA_OK  # nothing to do, nothing launched
+
+
 def test_validator_fused_step_contract():
     import workloads as wl
     c = wl.config2()
