@@ -1,6 +1,6 @@
 """Paged decode attention benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|4|5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|4|5|6]
                     [--kernel auto|mfma|valu] [--partition P] [--bucket B]
 
 A step is one pass of the hot path over one batch:
@@ -12,7 +12,11 @@ A step is one pass of the hot path over one batch:
   config 4 (Llama-3.3-70B-shaped layer, B = 256, lognormal lengths):
       pa_decode;
   config 5 (8B decode step, 32 layers, bucket B of padded rows):
-      pa_decode for each of the 32 layers.
+      pa_decode for each of the 32 layers;
+  config 6 (chunked prefill on an 8B-shaped layer: 8 prompts, one 512-token
+      chunk each, 0 .. 3,584 tokens already cached):
+      pa_write_kv of the 4,096 chunk tokens, then pa_prefill; its roofline is
+      the matrix cores' (bf16 dense), in TFLOP/s.
 Copy-on-write block copies fire only on a divergent write to a shared block,
 which these batches do not have; pa_copy_blocks is timed separately
 (`copy_blocks_us`) on one 8B-shaped block pair per call.
@@ -42,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s per layer"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
@@ -55,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 4, 5, 6])
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition tokens; 0 = balanced split (default 0 for "
@@ -156,6 +161,28 @@ def main():
             c = copies[i % len(copies)]
             if c.slot_mapping is not None:
                 pk.pa_write_kv(c.k_new, c.v_new, c.slot_mapping, c.k_pool, c.v_pool)
+    elif args.config == 6:
+        case = wl.prefill_step_8b(block_size=args.block_size)
+        copies = [case.to(dev) for _ in range(max(1, args.copies))]
+        Hq, Hkv, D = case.num_q_heads, case.num_kv_heads, case.head_dim
+        B = n_real = int(case.seq_lens.shape[0])  # sequences (q holds their chunk rows)
+        kv_bytes = case.kv_bytes()
+        layers = 1
+        lens_host = case.seq_lens.numpy()
+        workload = "prefill_step_llama3_8b_8x512"
+        if args.block_size != 16:
+            workload += f"_block{args.block_size}"
+        outs = [torch.empty_like(c.q) for c in copies]
+        ws = None
+        scale = case.scale
+
+        def decode_calls(i):
+            c = copies[i % len(copies)]
+            return [(c.q, c.k_pool, c.v_pool, c.block_tables, c.seq_lens, outs[i % len(copies)])]
+
+        def pre(i):
+            c = copies[i % len(copies)]
+            pk.pa_write_kv(c.k_new, c.v_new, c.slot_mapping, c.k_pool, c.v_pool)
     else:
         spec = wl.config5_spec(args.bucket)
         B, Hq, Hkv, D = spec.bucket, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
@@ -199,6 +226,9 @@ def main():
                 pk.pa_decode_append(q, c.k_new, c.v_new, c.slot_mapping, k, v, tb, ln, scale, o,
                                     partition_tokens=part, kernel=kernel, workspace=ws,
                                     stream=stream)
+            elif args.config == 6:
+                pk.pa_prefill(q, k, v, tb, ln, copies[i % len(copies)].query_start, scale, o,
+                              stream=stream)
             else:
                 pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part, kernel=kernel,
                              workspace=ws, stream=stream)
@@ -295,6 +325,16 @@ def main():
     mean_call_s = float(call_ms.mean()) / 1e3
     achieved = per_call_alg / mean_call_s / 1e9
     traffic = load_traffic(kernel, workload)
+    prefill_flops = None
+    if args.config == 6:  # QK and PV: 2 D flops each per (query head, key) pair
+        qs = case.query_start.numpy()
+        prefill_flops = 0
+        for s_i, L in enumerate(lens_host.tolist()):
+            n = int(qs[s_i + 1] - qs[s_i])
+            keys = n * (L - n) + n * (n + 1) // 2  # sum over chunk rows of (p + 1)
+            prefill_flops += 4 * Hq * D * keys
+        achieved = prefill_flops / mean_call_s / 1e12
+        traffic = None
 
     # ---------------- CPU oracle baseline ----------------
     cpu = None
@@ -324,7 +364,9 @@ def main():
             "kv_bytes_per_step": kv_bytes,
             "step": ("pa_decode_append (64-token KV append fused into the decode)"
                      if fused else "pa_write_kv(64 tokens) + pa_decode" if args.config == 2
-                     else "pa_decode" if args.config == 4 else "32 x pa_decode"),
+                     else "pa_decode" if args.config == 4
+                     else "pa_write_kv(4096 chunk tokens) + pa_prefill" if args.config == 6
+                     else "32 x pa_decode"),
         },
         "other_step_form_ms": None if other_ms is None else {
             ("separate" if args.step == "fused" else "fused"): round(other_ms, 5)},
@@ -336,15 +378,17 @@ def main():
                            "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
         "copy_blocks_us": None if copy_us is None else round(copy_us, 2),
         "roofline": {
-            "kernel": roofline_kernel(kernel, part, D) + (" with the fused KV append"
-                                                          if fused else ""),
-            "bound": "hbm",
+            "kernel": (f"prefill_mfma_kernel<{D}>" if args.config == 6 else
+                       roofline_kernel(kernel, part, D) + (" with the fused KV append"
+                                                           if fused else "")),
+            "bound": "mfma" if args.config == 6 else "hbm",
             "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "peak": MFMA_BF16_TFLOPS if args.config == 6 else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if args.config == 6 else "GB/s",
+            "frac": round(achieved / (MFMA_BF16_TFLOPS if args.config == 6 else HBM_PEAK_GBS), 4),
             "traffic": traffic,
             "algorithmic_bytes_per_call": int(per_call_alg),
+            "algorithmic_flops_per_call": prefill_flops,
         },
         "cpu_baseline": cpu,
     }
@@ -371,6 +415,8 @@ def cpu_baseline(args, case, lens_host, kv_bytes_per_layer, workload):
 
     if case is None:  # config 5: one layer's sample of rows, drawn on the host
         return None
+    if case.query_start is not None:
+        return cpu_baseline_prefill(args, case, kv_bytes_per_layer, workload)
     a = dict(q=to_numpy(case.q), k_pool=to_numpy(case.k_pool), v_pool=to_numpy(case.v_pool),
              block_tables=to_numpy(case.block_tables), seq_lens=to_numpy(case.seq_lens),
              scale=case.scale, dtype=case.dtype)
@@ -396,6 +442,48 @@ def cpu_baseline(args, case, lens_host, kv_bytes_per_layer, workload):
                   f"{done_bytes / 1e6:.1f} MB of K/V) in {t_total:.1f} s, float64 numpy, "
                   "BLAS limited to 1 thread",
         "seqs_per_s": round(done_rows / t_total, 2),
+    }
+
+
+def cpu_baseline_prefill(args, case, kv_bytes, workload):
+    """The float64 chunked-prefill oracle on one host core, one whole
+    sequence at a time until the time budget is spent; its (query, key)
+    rate gives the time of the whole step."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import to_numpy
+
+    k, v = oracle.write_kv(to_numpy(case.k_pool), to_numpy(case.v_pool), to_numpy(case.k_new),
+                           to_numpy(case.v_new), to_numpy(case.slot_mapping),
+                           block_size=case.block_size)
+    q, bt, lens = to_numpy(case.q), to_numpy(case.block_tables), to_numpy(case.seq_lens)
+    qs = to_numpy(case.query_start)
+    keys = []
+    for s_i, L in enumerate(lens.tolist()):
+        n = int(qs[s_i + 1] - qs[s_i])
+        keys.append(n * (L - n) + n * (n + 1) // 2)
+    done_keys, t_total, seqs = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while t_total < args.cpu_seconds:
+            s_i = seqs % len(lens)
+            t = time.perf_counter()
+            oracle.paged_prefill(q, k, v, bt, lens, qs, case.scale, case.dtype,
+                                 block_size=case.block_size, seqs=[s_i])
+            t_total += time.perf_counter() - t
+            done_keys += keys[s_i]
+            seqs += 1
+    step_s = t_total * sum(keys) / done_keys
+    return {
+        "value": round(kv_bytes / step_s / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{seqs} whole-sequence chunks of {workload} ({done_keys} query-key pairs "
+                  f"of {sum(keys)} per step) in {t_total:.1f} s, float64 numpy, BLAS limited "
+                  "to 1 thread; the step time is scaled by query-key pairs",
+        "step_s": round(step_s, 3),
     }
 
 

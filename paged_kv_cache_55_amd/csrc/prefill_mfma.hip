@@ -22,11 +22,14 @@
 // a single bf16 (2^-9) measured just above the parity bar on some rows,
 // where the output's own bf16 rounding already takes most of it.
 //
-// Work items are (sequence, 64-column block, KV head); every workgroup
-// counts the blocks per sequence into an LDS prefix, and the waves of a
+// Work items are (sequence, KV head, 64-column block); every workgroup
+// counts the items per sequence into an LDS prefix, and the waves of a
 // persistent grid take items in serpentine order (w, 2W - 1 - w, 2W + w,
 // ...), which pairs long items with short ones when their cost grows with
-// the item index.
+// the item index. The four waves of a workgroup get neighbouring column
+// blocks of one (sequence, KV head) and read the same K/V tiles at about the
+// same time, so the tiles are loaded with the default cache policy (they
+// are shared through the caches, unlike decode's read-once tiles).
 #include "launch.h"
 #include "mfma_tile.h"
 #include "worklist.h"
@@ -40,6 +43,8 @@ using namespace mfma;
 constexpr int kWaves = 4;
 constexpr int kColTiles = 4;
 constexpr int kCols = kColTiles * kTile;  // columns per work item
+constexpr float kLazyLog2 = 8.f;          // reference-max slack, log2 units
+constexpr bool kSplitP = true;            // probabilities as bf16 hi + lo
 
 template <int D>
 struct ColState {
@@ -85,28 +90,40 @@ __device__ __forceinline__ void fold_tile(Tile<D>& t, const bf16x8_t (&qb)[kColT
       sv[r] = tok0 + kg * 4 + r <= pos[ct] ? s[r] * scale_log2 : -INFINITY;
       mloc = fmaxf(mloc, sv[r]);
     }
-    const float m_new = fmaxf(st[ct].m, max_over_kg(mloc));  // finite: token 0 is seen
-    const float alpha = fast_exp2(st[ct].m - m_new);
-    st[ct].m = m_new;
-    uint16_t ph[4], pl[4];
+    // lazy reference max: the column keeps its reference m until a score
+    // exceeds it by 2^kLazyLog2 (its first tile always does: m starts at
+    // -inf, and token 0 is seen by every column); p = 2^(s - m) then stays
+    // <= 2^kLazyLog2, and the rescale of O and l runs only when some column
+    // of the wave moves its reference
+    const float mcol = max_over_kg(mloc);
+    const bool grow = mcol > st[ct].m + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mcol : st[ct].m;
+      const float alpha = fast_exp2(st[ct].m - m_new);  // 1 for columns that keep m
+      st[ct].m = m_new;
+      st[ct].l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) st[ct].acc[n] *= alpha;
+    }
     float psum = 0.f;
+    uint16_t ph[4], pl[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(sv[r] - m_new);
+      const float p = fast_exp2(sv[r] - st[ct].m);
       psum += p;
       ph[r] = bf16_rne(p);
       pl[r] = bf16_rne(p - __uint_as_float((uint32_t)ph[r] << 16));
     }
-    st[ct].l = st[ct].l * alpha + psum;
+    st[ct].l += psum;
     const short4_t bhi = __builtin_bit_cast(
         short4_t, make_uint2(pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])));
     const short4_t blo = __builtin_bit_cast(
         short4_t, make_uint2(pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3])));
 #pragma unroll
     for (int n = 0; n < NDT; ++n) {
-      float4_t o = st[ct].acc[n] * alpha;
-      o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[n], bhi, o, 0, 0, 0);
-      st[ct].acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[n], blo, o, 0, 0, 0);
+      float4_t o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[n], bhi, st[ct].acc[n], 0, 0, 0);
+      if (kSplitP) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[n], blo, o, 0, 0, 0);
+      st[ct].acc[n] = o;
     }
   }
 }
@@ -162,7 +179,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int kv
   auto load = [&](Tile<D>& dst, int j, int32_t phys) {
     const size_t base =
         ((((size_t)phys * Hkv + kvh) << a.block_shift) + (size_t)(j & sub_mask) * kTile) * D;
-    load_tile<D>(dst, kbase + base, vbase + base, lo);
+    load_tile<D, 0>(dst, kbase + base, vbase + base, lo);
   };
 
   // two register tiles alternate; the table entry of tile j + 2 is read
@@ -215,18 +232,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int kv
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
-  extern __shared__ int prefix[];  // [S + 1]: 64-column blocks before each sequence
+  extern __shared__ int prefix[];  // [S + 1]: work items before each sequence
   __shared__ int scan_scratch[kWaves];
   const int S = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
   for (int i = threadIdx.x; i < S; i += blockDim.x) {
     const int n = a.query_start[i + 1] - a.query_start[i];
-    prefix[i] = n > 0 ? (n * a.group + kCols - 1) / kCols : 0;
+    prefix[i] = n > 0 ? (n * a.group + kCols - 1) / kCols * Hkv : 0;
   }
   __syncthreads();
   scan_counts_in_place(S, prefix, scan_scratch);
 
-  const int Hkv = a.num_kv_heads;
-  const int total = prefix[S] * Hkv;
+  const int total = prefix[S];
   const int lane = threadIdx.x & 63;
   const int row = lane & 15;
   const int kg = lane >> 4;
@@ -235,10 +252,15 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
   for (int k = 0; k * W < total; ++k) {
     const int item = (k & 1) ? (k + 1) * W - 1 - w : k * W + w;
     if (item >= total) continue;
-    const int jb = item / Hkv;  // global column block
-    const int kvh = item - jb * Hkv;
-    const int s = __builtin_amdgcn_readfirstlane(find_sequence(prefix, S, jb));
-    prefill_item<D>(a, s, kvh, jb - prefix[s], row, kg);
+    // items of one sequence: KV head major, column block minor, so the waves
+    // of a workgroup take neighbouring column blocks of one (sequence, KV
+    // head) and stream the same K/V tiles at the same time
+    const int s = __builtin_amdgcn_readfirstlane(find_sequence(prefix, S, item));
+    const int r = item - prefix[s];
+    const int n = uniform_load(a.query_start, s + 1) - uniform_load(a.query_start, s);
+    const int ncb = (n * a.group + kCols - 1) / kCols;
+    const int kvh = r / ncb;
+    prefill_item<D>(a, s, kvh, r - kvh * ncb, row, kg);
   }
 }
 
