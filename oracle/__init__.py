@@ -11,8 +11,8 @@ helpers or constants. The two meet only through the seeded inputs that
 ``workloads`` produces and that callers pass to both sides.
 
 Modules
-  attention  paged decode and chunked-prefill attention, KV append (write)
-             and block copy
+  attention  paged decode, chunked-prefill and latent (MLA-style) decode
+             attention, KV append (write) and block copy
   pages      page / block-table arithmetic of the admission ledger
 
 Every function names the passage of the pages it follows. No function here
@@ -29,6 +29,7 @@ from .attention import (  # noqa: F401
     decode_contiguous,
     paged_decode,
     paged_prefill,
+    latent_decode,
     brute_force_decode,
     write_kv,
     copy_blocks,

@@ -210,6 +210,44 @@ def paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale,
     return out
 
 
+def latent_decode(q, kv_pool, block_tables, seq_lens, scale, dtype, value_dim=512,
+                  rows=None):
+    """Latent (MLA-style) paged decode, in float64.
+
+    Every cached token holds one latent vector of C elements (kv_pool
+    [NB, block, C]: a 512-element compressed KV plus a 64-element positional
+    key, C = 576); all H query heads of a row attend to that one latent, so
+    this is multi-query attention with head dim C. Each head's (absorbed)
+    query q[b, h] (C elements) scores against every cached latent,
+    s_t = scale * <q[b, h], c_t>, and the head's output is the softmax-
+    weighted sum of the first ``value_dim`` latent elements,
+    out[b, h] = sum_t softmax(s)_t c_t[:value_dim]; the up-projection back
+    to the model width is outside attention [llm-serving.xyz "KV-cache
+    systems", the MLA section: cached latent and decoupled RoPE key (576
+    elements per token), the absorbed computation mode, and its reading as
+    MQA with head dim 576; block size from the kernel's page size].
+    q [B, H, C]; returns [B or len(rows), H, value_dim]. Rows of length 0
+    are zero; slots past a row's length are never read.
+    """
+    B, H, C = q.shape
+    bs = kv_pool.shape[1]
+    rows = range(B) if rows is None else list(rows)
+    out = np.zeros((len(rows), H, value_dim))
+    for i, b in enumerate(rows):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        phys = np.asarray(block_tables[b])[t // bs].astype(np.int64)
+        lat = as_f64(kv_pool[phys, t % bs, :], dtype)   # [L, C]
+        qb = as_f64(q[b], dtype)                       # [H, C]
+        sc = scale * (qb @ lat.T)                      # [H, L]
+        m = sc.max(axis=1, keepdims=True)
+        p = np.exp(sc - m)
+        out[i] = (p @ lat[:, :value_dim]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 def brute_force_decode(q, k_pool, v_pool, block_tables, seq_lens, scale,
                        dtype, block_size=BLOCK_SIZE):
     """Same quantity as ``paged_decode`` with scalar Python loops.

@@ -20,6 +20,13 @@ Plain formulas, each the definition stated on the pages:
 * a prefix-cache hit reuses only complete matching blocks:
   floor(matched / block) [llm-serving.xyz "KV-cache systems", prefix-caching
   worked example].
+* a latent (MLA) cache holds one latent of (compressed + positional)
+  elements per token per layer, so bytes per token = (c + r) x layers x
+  bytes per element [llm-serving.xyz "KV-cache systems", MLA section,
+  cached-latent equation and the 34 KB/token figure].
+* attention costs 4 x query heads x effective head dim flops per cached
+  token per layer (a multiply-add for the score and one for the value, per
+  head and dim) [same section, the costs paragraph].
 """
 
 from __future__ import annotations
@@ -106,3 +113,11 @@ def prefix_hit_blocks(matched_tokens: int, block_tokens: int) -> int:
 def blocks_after_growth(seq_len: int, block_tokens: int) -> int:
     """Blocks a sequence holds at length L under on-demand growth."""
     return ceil_div(seq_len, block_tokens)
+
+
+def latent_bytes_per_token(latent: int, rope: int, n_layers: int, bytes_per_elem: int) -> int:
+    return (latent + rope) * n_layers * bytes_per_elem
+
+
+def attention_flops_per_cached_token(n_q_heads: int, head_dim: int) -> int:
+    return 4 * n_q_heads * head_dim

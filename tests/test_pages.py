@@ -93,3 +93,23 @@ def test_growth_takes_a_block_only_when_full():
     v, i = fact("growth_new_block_only_when_full")
     for L, n in v.items():
         assert P.blocks_after_growth(int(L), i["block_tokens"]) == n
+
+
+def test_latent_cache_bytes():
+    for name in ("mla_elements_per_token_layer", "mla_bytes_per_token_v3_fp8",
+                 "mla_bytes_per_token_k3_bf16"):
+        v, i = fact(name)
+        assert P.latent_bytes_per_token(**i) == v
+    # the printed ratio of the 70B shape's bytes per token to the latent cache's
+    ratio = fact("kv_bytes_per_token_70b_shape")[0] / fact("mla_bytes_per_token_v3_fp8")[0]
+    assert round(ratio, 1) == 9.3
+
+
+def test_attention_flops_per_cached_token():
+    for name in ("mla_attention_flops_per_cached_token",
+                 "gqa70b_attention_flops_per_cached_token"):
+        v, i = fact(name)
+        assert P.attention_flops_per_cached_token(**i) == v
+    # nine times the flops, as printed
+    assert (fact("mla_attention_flops_per_cached_token")[0]
+            // fact("gqa70b_attention_flops_per_cached_token")[0]) == 9

@@ -108,3 +108,20 @@ def test_permutation_relabels_consistently():
             i0, i1 = int(c.block_tables[b, t // 16]), int(p.block_tables[b, t // 16])
             assert torch.equal(c.k_pool[i0, :, t % 16], p.k_pool[i1, :, t % 16])
             assert torch.equal(c.v_pool[i0, :, :, t % 16], p.v_pool[i1, :, :, t % 16])
+
+
+def test_latent_case_layout_and_poison():
+    c = wl.latent_case(31, [1, 64, 65, 0, 200], num_heads=8)
+    assert c.q.shape == (5, 8, wl.LATENT_DIM)
+    nb, bs, C = c.kv_pool.shape
+    assert (bs, C) == (wl.LATENT_BLOCK, wl.LATENT_DIM)
+    used = np.zeros((nb, bs), bool)
+    for b, L in enumerate(c.seq_lens.tolist()):
+        for t in range(L):
+            used[int(c.block_tables[b, t // bs]), t % bs] = True
+    nan = torch.isnan(c.kv_pool.float()).all(dim=2).numpy()
+    assert np.array_equal(nan, ~used)          # every unread slot is poison, no read slot is
+    assert nb == sum(math.ceil(L / bs) for L in c.seq_lens.tolist()) + 1
+    b = wl.latent_decode_batch()
+    assert b.q.shape == (256, 128, 576) and b.kv_pool.dtype == torch.bfloat16
+    assert np.array_equal(b.seq_lens.numpy(), wl.config4_lens())

@@ -522,6 +522,64 @@ def prefill_step_8b(num_chunks: int = 8, chunk: int = 512, block_size: int = BLO
                         block_size=block_size, name="prefill_step_llama3_8b_8x512")
 
 
+LATENT_DIM = 576      # 512-element compressed KV + 64-element positional key
+LATENT_VALUE_DIM = 512
+LATENT_BLOCK = 64     # the latent kernels' page size
+
+
+@dataclass
+class LatentCase:
+    """Inputs of a latent (MLA-style) decode batch."""
+
+    q: torch.Tensor             # [B, H, 576]
+    kv_pool: torch.Tensor       # [NB, block, 576]
+    block_tables: torch.Tensor  # int32 [B, MB]
+    seq_lens: torch.Tensor      # int32 [B]
+    scale: float
+    dtype: str = "bf16"
+
+    def to(self, device) -> "LatentCase":
+        return LatentCase(self.q.to(device), self.kv_pool.to(device),
+                          self.block_tables.to(device), self.seq_lens.to(device), self.scale,
+                          self.dtype)
+
+    def kv_bytes(self) -> int:
+        elem = 4 if self.dtype == "f32" else 2
+        return int(self.seq_lens.to(torch.int64).sum()) * self.kv_pool.shape[2] * elem
+
+
+def latent_case(seed, lens, num_heads=128, block_size=LATENT_BLOCK, dtype="bf16",
+                scale=None) -> LatentCase:
+    """A latent decode batch: random block placement (seeded permutation of
+    a pool of exactly the needed blocks plus a poison block), N(0, 1) values,
+    NaN in unused blocks and in the tail slots of each last block. The scale
+    defaults to 1 / sqrt(576), the softmax scale of attention with head dim
+    576."""
+    lens = np.asarray(lens, dtype=np.int64)
+    rng = np.random.default_rng([seed, 9])
+    gen = torch.Generator().manual_seed(seed)
+    tables, nb, poison = place_blocks(lens, rng, block_size=block_size)
+    q = _randn(gen, (len(lens), num_heads, LATENT_DIM), dtype)
+    kv = _randn(gen, (nb, block_size, LATENT_DIM), dtype)
+    used = np.zeros(nb, dtype=bool)
+    for b, L in enumerate(lens.tolist()):
+        used[tables[b, :math.ceil(L / block_size)]] = True
+    kv[torch.from_numpy(np.nonzero(~used)[0])] = float("nan")
+    for b, L in enumerate(lens.tolist()):
+        if L % block_size:
+            kv[int(tables[b, L // block_size]), L % block_size:, :] = float("nan")
+    return LatentCase(q, kv, torch.from_numpy(tables), torch.from_numpy(lens.astype(np.int32)),
+                      scale if scale is not None else 1.0 / math.sqrt(LATENT_DIM), dtype)
+
+
+def latent_decode_batch(batch: int = 256) -> LatentCase:
+    """A DeepSeek-V3-shaped MLA decode layer: 128 heads over one 576-element
+    latent per token, 64-token pages, bf16, with the 70B serving batch's
+    length mix (B = 256, lognormal, median 1,024, sigma 1, clipped to
+    [16, 8192])."""
+    return latent_case(SEED_BASE + 7, config4_lens(batch=batch))
+
+
 def permute_physical(case: Case, seed: int) -> Case:
     """The same logical contents under another physical placement:
     pool'[pi(i)] = pool[i] and table' = pi(table)."""
