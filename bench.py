@@ -1,6 +1,6 @@
 """Paged decode attention benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|4|5|6]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|4|5|6|7]
                     [--kernel auto|mfma|valu] [--partition P] [--bucket B]
 
 A step is one pass of the hot path over one batch:
@@ -16,7 +16,11 @@ A step is one pass of the hot path over one batch:
   config 6 (chunked prefill on an 8B-shaped layer: 8 prompts, one 512-token
       chunk each, 0 .. 3,584 tokens already cached):
       pa_write_kv of the 4,096 chunk tokens, then pa_prefill; its roofline is
-      the matrix cores' (bf16 dense), in TFLOP/s.
+      the matrix cores' (bf16 dense), in TFLOP/s;
+  config 7 (MLA-style latent decode on a DeepSeek-V3-shaped layer: 128 heads
+      over one 576-element latent per token, 64-token pages, B = 256 with
+      the 70B batch's lengths): pa_latent_decode; HBM roofline, with the
+      matrix cores' share reported beside it.
 Copy-on-write block copies fire only on a divergent write to a shared block,
 which these batches do not have; pa_copy_blocks is timed separately
 (`copy_blocks_us`) on one 8B-shaped block pair per call.
@@ -52,6 +56,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
     "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
+    "latent": ["latent_mfma.hip", "mfma_tile.h", "device_common.h", "worklist.h", "launch.h"],
 }
 
 
@@ -60,7 +65,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 4, 5, 6, 7])
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition tokens; 0 = balanced split (default 0 for "
@@ -183,6 +188,28 @@ def main():
         def pre(i):
             c = copies[i % len(copies)]
             pk.pa_write_kv(c.k_new, c.v_new, c.slot_mapping, c.k_pool, c.v_pool)
+    elif args.config == 7:
+        case = wl.latent_decode_batch()
+        copies = [case.to(dev) for _ in range(max(1, args.copies))]
+        B, Hq, Hkv, D = case.q.shape[0], case.q.shape[1], 1, case.q.shape[2]
+        n_real = int((case.seq_lens > 0).sum())
+        kv_bytes = case.kv_bytes()
+        layers = 1
+        lens_host = case.seq_lens.numpy()
+        workload = "deepseek_v3_mla_layer_b256_lognormal1024"
+        outs = [torch.empty((B, Hq, wl.LATENT_VALUE_DIM), dtype=torch.bfloat16, device=dev)
+                for _ in copies]
+        ldims = pk.make_latent_dims(B, case.block_tables.shape[1], case.kv_pool.shape[0])
+        ws = torch.zeros(pk.pa_latent_workspace_bytes(ldims), dtype=torch.uint8, device=dev)
+        scale = case.scale
+        kernel = "latent"
+
+        def decode_calls(i):
+            c = copies[i % len(copies)]
+            return [(c.q, c.kv_pool, None, c.block_tables, c.seq_lens, outs[i % len(copies)])]
+
+        def pre(i):
+            pass
     else:
         spec = wl.config5_spec(args.bucket)
         B, Hq, Hkv, D = spec.bucket, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
@@ -229,6 +256,8 @@ def main():
             elif args.config == 6:
                 pk.pa_prefill(q, k, v, tb, ln, copies[i % len(copies)].query_start, scale, o,
                               stream=stream)
+            elif args.config == 7:
+                pk.pa_latent_decode(q, k, tb, ln, scale, o, workspace=ws, stream=stream)
             else:
                 pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part, kernel=kernel,
                              workspace=ws, stream=stream)
@@ -315,9 +344,14 @@ def main():
     # ---------------- figures ----------------
     sec = ms_per_step / 1e3
     value = kv_bytes / sec / 1e9
-    bsz = case.block_size if case is not None else 16
+    bsz = (case.block_size if args.config != 7 else wl.LATENT_BLOCK) if case is not None else 16
     table_bytes = int(sum(math.ceil(int(L) / bsz) for L in lens_host)) * 4
     per_call_alg = (kv_bytes / layers) + 2 * B * Hq * D * 2 + table_bytes + 4 * B
+    latent_flops = None
+    if args.config == 7:  # q read, out written (512 of 576 elements), latents, tables
+        per_call_alg = kv_bytes + B * Hq * (D + wl.LATENT_VALUE_DIM) * 2 + table_bytes + 4 * B
+        # scores: 2 * 576 flops, values: 2 * 512 flops per (head, cached token)
+        latent_flops = int(lens_host.sum()) * Hq * 2 * (D + wl.LATENT_VALUE_DIM)
     fused = args.config == 2 and args.step == "fused"
     if fused:  # the appended tokens: k_new/v_new read, their slots written, slot ids
         T = int((case.slot_mapping >= 0).sum())
@@ -335,6 +369,12 @@ def main():
             prefill_flops += 4 * Hq * D * keys
         achieved = prefill_flops / mean_call_s / 1e12
         traffic = None
+    mfma_share = None
+    if latent_flops is not None:
+        mfma_share = {"achieved_tflops": round(latent_flops / mean_call_s / 1e12, 1),
+                      "peak_tflops": MFMA_BF16_TFLOPS,
+                      "frac": round(latent_flops / mean_call_s / 1e12 / MFMA_BF16_TFLOPS, 4),
+                      "flops_per_call": latent_flops}
 
     # ---------------- CPU oracle baseline ----------------
     cpu = None
@@ -358,7 +398,7 @@ def main():
             "workload": workload,
             "batch": B, "real_rows": n_real, "q_heads": Hq, "kv_heads": Hkv,
             "head_dim": D, "layers": layers,
-            "block_size": case.block_size if case is not None else 16,
+            "block_size": bsz,
             "placement": args.placement if case is not None else "random",
             "partition_tokens": part, "kernel": kernel, "graph": args.graph,
             "kv_bytes_per_step": kv_bytes,
@@ -366,6 +406,7 @@ def main():
                      if fused else "pa_write_kv(64 tokens) + pa_decode" if args.config == 2
                      else "pa_decode" if args.config == 4
                      else "pa_write_kv(4096 chunk tokens) + pa_prefill" if args.config == 6
+                     else "pa_latent_decode" if args.config == 7
                      else "32 x pa_decode"),
         },
         "other_step_form_ms": None if other_ms is None else {
@@ -379,6 +420,8 @@ def main():
         "copy_blocks_us": None if copy_us is None else round(copy_us, 2),
         "roofline": {
             "kernel": (f"prefill_mfma_kernel<{D}>" if args.config == 6 else
+                       "latent_decode_kernel (one launch per call; cut rows merged inside it)"
+                       if args.config == 7 else
                        roofline_kernel(kernel, part, D) + (" with the fused KV append"
                                                            if fused else "")),
             "bound": "mfma" if args.config == 6 else "hbm",
@@ -389,6 +432,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_call": int(per_call_alg),
             "algorithmic_flops_per_call": prefill_flops,
+            "matrix_cores": mfma_share,
         },
         "cpu_baseline": cpu,
     }
@@ -415,6 +459,8 @@ def cpu_baseline(args, case, lens_host, kv_bytes_per_layer, workload):
 
     if case is None:  # config 5: one layer's sample of rows, drawn on the host
         return None
+    if isinstance(case, wl.LatentCase):
+        return cpu_baseline_latent(args, case, lens_host, workload)
     if case.query_start is not None:
         return cpu_baseline_prefill(args, case, kv_bytes_per_layer, workload)
     a = dict(q=to_numpy(case.q), k_pool=to_numpy(case.k_pool), v_pool=to_numpy(case.v_pool),
@@ -440,6 +486,37 @@ def cpu_baseline(args, case, lens_host, kv_bytes_per_layer, workload):
         "kind": "oracle",
         "sample": f"{done_rows} sequence decodes of {workload} (rows in batch order, "
                   f"{done_bytes / 1e6:.1f} MB of K/V) in {t_total:.1f} s, float64 numpy, "
+                  "BLAS limited to 1 thread",
+        "seqs_per_s": round(done_rows / t_total, 2),
+    }
+
+
+def cpu_baseline_latent(args, case, lens_host, workload):
+    """The float64 latent-decode oracle on one host core, one row at a time
+    (rows in batch order) until the time budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import to_numpy
+
+    q, kv = to_numpy(case.q), to_numpy(case.kv_pool)
+    bt, lens = to_numpy(case.block_tables), to_numpy(case.seq_lens)
+    done_bytes, done_rows, t_total = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_total < args.cpu_seconds:
+            b = done_rows % len(lens_host)
+            t = time.perf_counter()
+            oracle.latent_decode(q, kv, bt, lens, case.scale, case.dtype, rows=[b])
+            t_total += time.perf_counter() - t
+            done_bytes += int(lens_host[b]) * kv.shape[2] * 2
+            done_rows += 1
+    return {
+        "value": round(done_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done_rows} row decodes of {workload} (rows in batch order, "
+                  f"{done_bytes / 1e6:.1f} MB of latents) in {t_total:.1f} s, float64 numpy, "
                   "BLAS limited to 1 thread",
         "seqs_per_s": round(done_rows / t_total, 2),
     }

@@ -195,6 +195,72 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool,
                          const int32_t* block_mapping, int32_t num_pairs,
                          const pa_dims* dims, void* stream);
 
+/* ---- Latent (MLA-style) decode ------------------------------------------
+ *
+ * Multi-head latent attention caches, per token, one latent vector of
+ * latent_dim = 576 elements: a 512-element compressed KV and a 64-element
+ * positional key, shared by every query head; keys and values are never
+ * materialised. With the up-projections absorbed into the queries and the
+ * output projection, decode is multi-query attention with head dim 576
+ * whose values are the first 512 latent elements [llm-serving.xyz
+ * "KV-cache systems", MLA section: the cached latent and its decoupled
+ * positional key, the two computation modes (the absorbed one here), the
+ * 64-token page of the dedicated decode kernels].
+ *
+ * Layouts (row-major, contiguous, device memory)
+ *   q             [B, H, 576]       absorbed queries (compressed part, then
+ *                                   positional part), dtype
+ *   kv_pool       [NB, BS, 576]     latent blocks, token-major
+ *   block_tables  int32 [B, MB]     as for pa_decode, entry j = block of
+ *                                   tokens BS*j .. BS*j+BS-1
+ *   seq_lens      int32 [B]         tokens attended; 0 = padded row (zeros)
+ *   out           [B, H, 512]
+ *   kv_new        [T, 576], slot_mapping int32 [T] (slot = block*BS + offset)
+ * Ownership, stream semantics and device-value guarantees as for the calls
+ * above (table entries below NB for the blocks a row uses, lengths at most
+ * MB * BS). */
+typedef struct {
+  int32_t num_seqs;           /* B   (1 .. 4096) */
+  int32_t num_heads;          /* H   query heads sharing each latent: 128 */
+  int32_t latent_dim;         /* elements per cached latent: 576 */
+  int32_t value_dim;          /* leading latent elements that form the values: 512 */
+  int32_t block_size;         /* BS  tokens per block: 64 */
+  int32_t max_blocks_per_seq; /* MB: row stride of block_tables (1 .. 2^20) */
+  int32_t num_blocks;         /* NB: pool capacity in blocks (>= 1) */
+  int32_t dtype;              /* pa_dtype; PA_BF16 */
+} pa_latent_dims;
+
+/* Bytes of device workspace pa_latent_decode needs: control counters, per
+ * row two piece counters and an overflow flag, then fp32 partial records
+ * (O, max, sum of 128 heads) for two pieces per workgroup of a grid of at
+ * most 256. Zero-fill it before its first use; every call leaves it
+ * reusable. Calls that may overlap in time need separate workspaces.
+ * Returns 0 for invalid dims (pa_latent_decode reports those). */
+size_t pa_latent_workspace_bytes(const pa_latent_dims* dims);
+
+/* Latent decode: for every row b and head h,
+ *   out[b,h,:] = sum_t softmax_t(scale * <q[b,h,:], c_b[t]>) c_b[t][0:512]
+ * over t < seq_lens[b], with the latents c_b gathered through
+ * block_tables[b] (fp32 accumulation; weights enter the value product as
+ * bf16). A persistent grid streams equal shares of all 32-token tiles; a
+ * row split across workgroups is merged (log-sum-exp) by its last piece.
+ * A row whose scores rise more than 2^32 above a piece's first-tile maximum
+ * is recomputed exactly (two passes) at the end of the call. Slots at or
+ * past seq_lens[b] never reach the result; bf16 output is rounded to
+ * nearest even. PA_ERR_UNSUPPORTED for any shape but H = 128, 576 / 512,
+ * BS = 64, bf16. */
+pa_status pa_latent_decode(const void* q, const void* kv_pool, const int32_t* block_tables,
+                           const int32_t* seq_lens, float scale, void* out,
+                           const pa_latent_dims* dims, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Latent append: kv_pool row slot_mapping[t] (block s / BS, offset s % BS)
+ * becomes kv_new[t] for every t < num_tokens with slot_mapping[t] >= 0; a
+ * bit copy. The cache grows by one latent per generated token [same MLA
+ * section]. num_tokens == 0 is a no-op. */
+pa_status pa_latent_write(const void* kv_new, const int32_t* slot_mapping, int32_t num_tokens,
+                          void* kv_pool, const pa_latent_dims* dims, void* stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(pa_status status);
 

@@ -13,12 +13,17 @@ missing build is an error: there is no fallback path.
     pa_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool)
     pa_copy_blocks(k_pool, v_pool, block_mapping)
     pa_decode_workspace_bytes(dims)
+    pa_latent_decode(q, kv_pool, block_tables, seq_lens, scale, out, ...)
+    pa_latent_write(kv_new, slot_mapping, kv_pool)
+    pa_latent_workspace_bytes(dims)
 
 Layouts: q/out [B, Hq, D]; k_pool [NB, Hkv, BS, D]; v_pool [NB, Hkv, D, BS]
 (BS = 16 tokens per block; 8 .. 256 with the balanced split, V as
 [NB, Hkv, BS // 16, D, 16] beyond 16);
 block_tables int32 [B, MB]; seq_lens int32 [B]; k_new/v_new [T, Hkv, D];
 slot_mapping int32 [T]; block_mapping int32 [n, 2].
+Latent decode: q [B, 128, 576], kv_pool [NB, 64, 576], out [B, 128, 512],
+kv_new [T, 576].
 """
 
 from __future__ import annotations
@@ -32,7 +37,8 @@ __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_LAUNCH",
     "PaDims", "PagedKVError", "SYMBOLS", "load_library", "make_dims",
     "pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_prefill", "pa_write_kv",
-    "pa_copy_blocks",
+    "pa_copy_blocks", "PaLatentDims", "make_latent_dims", "pa_latent_decode",
+    "pa_latent_write", "pa_latent_workspace_bytes",
     "pa_status_string", "pa_version", "validate",
 ]
 
@@ -42,7 +48,9 @@ KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 BLOCK_SIZE = 16
 
 SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_append", "pa_prefill",
-           "pa_write_kv", "pa_copy_blocks", "pa_status_string", "pa_version")
+           "pa_write_kv", "pa_copy_blocks", "pa_latent_workspace_bytes", "pa_latent_decode",
+           "pa_latent_write", "pa_status_string", "pa_version")
+LATENT_HEADS, LATENT_DIM, LATENT_VALUE_DIM, LATENT_BLOCK = 128, 576, 512, 64
 
 
 class PaDims(ctypes.Structure):
@@ -50,6 +58,12 @@ class PaDims(ctypes.Structure):
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
         "max_blocks_per_seq", "num_blocks", "partition_tokens", "dtype",
         "kernel")]
+
+
+class PaLatentDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_heads", "latent_dim", "value_dim", "block_size",
+        "max_blocks_per_seq", "num_blocks", "dtype")]
 
 
 class PagedKVError(RuntimeError):
@@ -85,6 +99,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_write_kv.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
     lib.pa_copy_blocks.restype = ctypes.c_int
+    LD = ctypes.POINTER(PaLatentDims)
+    lib.pa_latent_workspace_bytes.argtypes = [LD]
+    lib.pa_latent_workspace_bytes.restype = SZ
+    lib.pa_latent_decode.argtypes = [P, P, P, P, F32, P, LD, P, SZ, P]
+    lib.pa_latent_decode.restype = ctypes.c_int
+    lib.pa_latent_write.argtypes = [P, P, I32, P, LD, P]
+    lib.pa_latent_write.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
@@ -311,6 +332,82 @@ def pa_copy_blocks(k_pool, v_pool, block_mapping, *, stream=None):
                                        _stream(stream))
     if st != PA_OK:
         raise PagedKVError("pa_copy_blocks", st)
+
+
+# --------------------------------------------------------------------------
+# latent (MLA-style) decode
+# --------------------------------------------------------------------------
+
+def make_latent_dims(num_seqs, max_blocks_per_seq, num_blocks, dtype=PA_BF16,
+                     num_heads=LATENT_HEADS, latent_dim=LATENT_DIM,
+                     value_dim=LATENT_VALUE_DIM, block_size=LATENT_BLOCK) -> PaLatentDims:
+    return PaLatentDims(int(num_seqs), int(num_heads), int(latent_dim), int(value_dim),
+                        int(block_size), int(max_blocks_per_seq), int(num_blocks), int(dtype))
+
+
+def pa_latent_workspace_bytes(dims: PaLatentDims) -> int:
+    return int(load_library().pa_latent_workspace_bytes(ctypes.byref(dims)))
+
+
+def _latent_pool(kv_pool):
+    _need(kv_pool.dim() == 3 and kv_pool.is_contiguous() and kv_pool.is_cuda,
+          "kv_pool must be a contiguous device tensor [NB, BS, C]")
+    return kv_pool.shape
+
+
+def pa_latent_decode(q, kv_pool, block_tables, seq_lens, scale, out=None, *, workspace=None,
+                     stream=None):
+    """out[b, h] = softmax(scale * q[b, h] . c_t) weighted sum of c_t[:512]
+    over row b's latents c_t (MLA decode with absorbed queries). A
+    caller-provided ``workspace`` (uint8 device tensor of at least
+    pa_latent_workspace_bytes bytes) must be zero-filled before its first
+    use; calls leave it reusable, and two calls that can run at the same
+    time need two workspaces."""
+    torch = _torch()
+    NB, BS, C = _latent_pool(kv_pool)
+    _need(q.dim() == 3 and q.shape[2] == C and q.dtype == kv_pool.dtype and q.is_contiguous()
+          and q.is_cuda, "q must be [B, H, C] like the pool")
+    B, H, _ = q.shape
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == B and block_tables.is_contiguous()
+          and block_tables.is_cuda, "block_tables must be int32 [B, MB] on the device")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,)
+          and seq_lens.is_contiguous() and seq_lens.is_cuda,
+          "seq_lens must be int32 [B] on the device")
+    dims = make_latent_dims(B, block_tables.shape[1], NB, _dtype_code(q), num_heads=H,
+                            latent_dim=C, block_size=BS)
+    if out is None:
+        out = torch.empty((B, H, dims.value_dim), dtype=q.dtype, device=q.device)
+    _need(tuple(out.shape) == (B, H, dims.value_dim) and out.dtype == q.dtype
+          and out.is_contiguous() and out.is_cuda, "out must be [B, H, 512] like q")
+    need = pa_latent_workspace_bytes(dims)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().pa_latent_decode(_ptr(q), _ptr(kv_pool), _ptr(block_tables),
+                                         _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                                         ctypes.byref(dims), _ptr(workspace),
+                                         ctypes.c_size_t(ws_bytes), _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_latent_decode", st)
+    return out
+
+
+def pa_latent_write(kv_new, slot_mapping, kv_pool, *, stream=None):
+    """kv_pool row slot = kv_new[t] for every t with slot_mapping[t] >= 0."""
+    torch = _torch()
+    NB, BS, C = _latent_pool(kv_pool)
+    T = slot_mapping.shape[0]
+    _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1
+          and slot_mapping.is_contiguous() and slot_mapping.is_cuda,
+          "slot_mapping must be int32 [T] on the device")
+    _need(tuple(kv_new.shape) == (T, C) and kv_new.dtype == kv_pool.dtype
+          and kv_new.is_contiguous() and kv_new.is_cuda, "kv_new must be [T, C] like the pool")
+    dims = make_latent_dims(1, 1, NB, _dtype_code(kv_pool), latent_dim=C, block_size=BS)
+    st = load_library().pa_latent_write(_ptr(kv_new), _ptr(slot_mapping), T, _ptr(kv_pool),
+                                        ctypes.byref(dims), _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_latent_write", st)
 
 
 from .validate import validate  # noqa: E402

@@ -262,9 +262,96 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
   return PA_OK;
 }
 
+// Latent decode: one workgroup per compute unit, at most this many; a
+// workgroup's range holds at least kLatentMinTiles 32-token tiles.
+constexpr int kMaxLatentGrid = 256;
+constexpr int kLatentMinTiles = 8;
+
+struct LatentPlan {
+  size_t off_ctl, off_cnt, off_flag, off_rec, ws_bytes;
+};
+
+pa_status plan_latent(const pa_latent_dims* d, LatentPlan* p) {
+  if (!d) return PA_ERR_INVALID_ARG;
+  if (d->num_seqs < 1 || d->num_heads < 1 || d->latent_dim < 1 || d->value_dim < 1 ||
+      d->block_size < 1 || d->max_blocks_per_seq < 1 || d->num_blocks < 1)
+    return PA_ERR_INVALID_ARG;
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (d->value_dim > d->latent_dim) return PA_ERR_INVALID_ARG;
+  if (d->dtype != PA_BF16 || d->num_heads != kLatentHeads || d->latent_dim != kLatentDim ||
+      d->value_dim != kLatentValueDim || d->block_size != kLatentBlockTokens)
+    return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs > kMaxSeqs || d->max_blocks_per_seq > (1 << 20)) return PA_ERR_UNSUPPORTED;
+  const size_t B = (size_t)d->num_seqs;
+  p->off_ctl = 0;
+  p->off_cnt = kAlign;
+  p->off_flag = align_up(p->off_cnt + 2 * B * sizeof(int));
+  p->off_rec = align_up(p->off_flag + B * sizeof(int));
+  p->ws_bytes = p->off_rec + (size_t)2 * kMaxLatentGrid * kLatentRecordFloats * sizeof(float);
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t pa_latent_workspace_bytes(const pa_latent_dims* dims) {
+  LatentPlan p;
+  if (plan_latent(dims, &p) != PA_OK) return 0;
+  return p.ws_bytes;
+}
+
+pa_status pa_latent_decode(const void* q, const void* kv_pool, const int32_t* block_tables,
+                           const int32_t* seq_lens, float scale, void* out,
+                           const pa_latent_dims* dims, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  LatentPlan plan;
+  pa_status st = plan_latent(dims, &plan);
+  if (st != PA_OK) return st;
+  if (!q || !kv_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < plan.ws_bytes) return PA_ERR_INVALID_ARG;
+  size_t lds = 0;
+  hipError_t e = lds_per_workgroup(&lds);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  const size_t smem = latent_decode_smem(dims->num_seqs);
+  if (smem > lds) return PA_ERR_UNSUPPORTED;
+  int resident = 0;
+  e = resident_workgroups(latent_decode_fn(), smem, &resident);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  char* ws = (char*)workspace;
+  LatentArgs a;
+  a.q = q;
+  a.kv_pool = kv_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.ws_rec = (float*)(ws + plan.off_rec);
+  a.ws_cnt = (int*)(ws + plan.off_cnt);
+  a.ws_flag = (int*)(ws + plan.off_flag);
+  a.ws_ctl = (int*)(ws + plan.off_ctl);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = dims->num_seqs;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.grid = resident < kMaxLatentGrid ? resident : kMaxLatentGrid;
+  a.min_tiles = kLatentMinTiles;
+  e = launch_latent_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_latent_write(const void* kv_new, const int32_t* slot_mapping, int32_t num_tokens,
+                          void* kv_pool, const pa_latent_dims* dims, void* stream) {
+  LatentPlan plan;
+  pa_status st = plan_latent(dims, &plan);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!kv_new || !slot_mapping || !kv_pool) return PA_ERR_INVALID_ARG;
+  hipError_t e = launch_latent_write(kv_new, slot_mapping, num_tokens, kv_pool,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 
 size_t pa_decode_workspace_bytes(const pa_dims* dims) {
   Plan p;

@@ -1,4 +1,5 @@
-// KV append (pa_write_kv) and copy-on-write block copy (pa_copy_blocks).
+// KV append (pa_write_kv, pa_latent_write) and copy-on-write block copy
+// (pa_copy_blocks).
 //
 // Both are bit copies. A new token's K row is contiguous in the token-major
 // K region of its block; its V column is strided in the dim-major V tile
@@ -65,7 +66,39 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   for (size_t j = threadIdx.x; j < vecs_per_block; j += blockDim.x) to[j] = stream_load16(from + j);
 }
 
+// One wave per new latent, four per workgroup: 72 16-byte vectors of the
+// 1,152-byte latent row, loaded before the slot is known.
+__global__ __launch_bounds__(256) void latent_write_kernel(const uint4* __restrict__ kv_new,
+                                                           const int32_t* __restrict__ slots,
+                                                           uint4* __restrict__ kv_pool,
+                                                           int num_tokens) {
+  constexpr int kVecs = kLatentDim * 2 / 16;  // 72
+  const int lane = threadIdx.x & 63;
+  const long long stride = (long long)gridDim.x * 4;
+  for (long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); t < num_tokens; t += stride) {
+    const uint4* src = kv_new + (size_t)t * kVecs;
+    const uint4 a = src[lane];
+    uint4 b = make_uint4(0, 0, 0, 0);
+    if (lane < kVecs - 64) b = src[64 + lane];
+    const int s = uniform_load(slots, t);
+    if (s < 0) continue;
+    uint4* dst = kv_pool + (size_t)s * kVecs;
+    dst[lane] = a;
+    if (lane < kVecs - 64) dst[64 + lane] = b;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_latent_write(const void* kv_new, const int32_t* slots, int num_tokens,
+                               void* kv_pool, hipStream_t s) {
+  const long long wgs = ((long long)num_tokens + 3) / 4;
+  dim3 grid((unsigned)(wgs < (1 << 16) ? wgs : (1 << 16))), block(256);
+  const uint4* kn = (const uint4*)kv_new;
+  uint4* kp = (uint4*)kv_pool;
+  void* args[] = {&kn, &slots, &kp, &num_tokens};
+  return hipLaunchKernel((const void*)&latent_write_kernel, grid, block, args, 0, s);
+}
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,
                            int num_tokens, void* k_pool, void* v_pool, int num_kv_heads,

@@ -171,4 +171,26 @@ struct PrefillArgs {
   int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, block_shift;
 };
 
+// Everything the latent (MLA-style) decode kernel needs; passed by value.
+struct LatentArgs {
+  const void* q;               // [B, H, 576] absorbed queries
+  const void* kv_pool;         // [NB, 64, 576] latent blocks
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* out;                   // [B, H, 512]
+  // cut rows: fp32 records of two piece slots per workgroup (O[h][d], then
+  // m[H], then l[H]); per row two counters (pieces arrived, records
+  // written) and an overflow flag; two control counters (workgroups
+  // finished, segments flagged). The counters and flags are zero between
+  // calls.
+  float* ws_rec;
+  int* ws_cnt;   // [B][2]
+  int* ws_flag;  // [B]
+  int* ws_ctl;   // [2]
+  float scale_log2;
+  int num_seqs, max_blocks;
+  int grid;       // workgroups of the launch
+  int min_tiles;  // least 32-token tiles per workgroup range
+};
+
 }  // namespace pagedkv

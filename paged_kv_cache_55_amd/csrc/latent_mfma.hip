@@ -1,0 +1,669 @@
+// Latent (MLA-style) paged decode on the CDNA4 matrix cores (bf16).
+//
+// Every cached token holds one latent of 576 elements (a 512-element
+// compressed KV and a 64-element positional key); each of the 128 query
+// heads of a row scores its absorbed 576-element query against every
+// latent of the row, and its output is the softmax-weighted sum of the
+// latents' first 512 elements [llm-serving.xyz "KV-cache systems", MLA
+// section: the cached latent with its decoupled positional key, the absorbed
+// (MQA) computation mode, the 64-token page]. This is multi-query attention
+// with head dim 576: a token costs 4 x 128 x 576 flops against 1,152 bytes,
+// so on MI355X the two rooflines nearly meet (the bf16 matrix cores must
+// run at about 77% of peak to keep pace with HBM).
+//
+// A workgroup of four waves owns all 128 heads, 32 per wave: a wave's
+// output accumulator O^T (32 heads x 512 dims, fp32) is 256 registers, the
+// accumulation registers of one wave per SIMD. A 32-token latent tile is
+// brought from HBM once per workgroup, straight into LDS (buffer loads with
+// an LDS destination: no staging registers; three tiles in flight), token
+// rows padded to 1,248 bytes, a stride at which both operand reads below
+// run without bank conflicts:
+//   scores  S^T[t][h] = C[t] . q[h]             v_mfma_f32_16x16x32_bf16;
+//           A = 16 tokens x 32 elements, one ds_read_b128 of a token row
+//   values  O^T[d][h] += C^T[d][t] P^T[t][h]    v_mfma_f32_16x16x32_bf16;
+//           A = 16 dims x 32 tokens, two ds_read_b64_tr_b16 (the LDS read
+//           that transposes 16-bit elements across lanes)
+// The probabilities enter the value product as single bf16 numbers (their
+// 2^-9 relative rounding averages out over the weighted sum; a hi/lo pair
+// as in the grouped-query kernels would double the value product's matrix
+// work, which here is the other bound). The softmax keeps a lazy reference
+// max, as the prefill kernel does.
+//
+// Work split: the flat list of (row, 32-token tile) is cut into equal
+// contiguous ranges, one per workgroup of a persistent grid (one workgroup
+// per compute unit). A row cut by range boundaries is finished by the last
+// of its pieces to arrive: each piece first counts itself in; the last one
+// waits until the others, which have all counted already and so are
+// running, have written their fp32 records (O, m, l of 128 heads), folds
+// them into its own registers and writes the row. A cut thus costs one
+// record write and one read (a record is 257 KiB, as much as 229 tokens of
+// latent cache), and no workgroup ever waits for one that has not started.
+#include "launch.h"
+#include "mfma_tile.h"
+#include "worklist.h"
+
+namespace pagedkv {
+
+namespace {
+
+using namespace mfma;
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
+constexpr int kWaves = 4;
+constexpr int kHeads = kLatentHeads;
+constexpr int kHeadsPerWave = kHeads / kWaves;  // 32: two 16-head tiles
+constexpr int kLatent = kLatentDim;
+constexpr int kValue = kLatentValueDim;
+constexpr int kPageTokens = kLatentBlockTokens;
+constexpr int kTileTokens = kLatentTileTokens;
+constexpr int kTokenBytes = kLatent * 2;             // 1,152
+constexpr int kRowBytes = 1248;                       // padded LDS row of one token
+constexpr int kRowChunks = kRowBytes / 16;            // 78 16-byte chunks, 72 of data
+constexpr int kDataChunks = kTokenBytes / 16;         // 72
+constexpr int kTileLoads = kTileTokens * kRowChunks / 64;  // 39 wave loads of 1 KiB
+static_assert(kTileTokens * kRowChunks % 64 == 0, "a tile is whole wave loads");
+static_assert(kTileLoads * 1024 == kLatentStageBytes, "stage size");
+constexpr int kStageBytes = kLatentStageBytes;
+constexpr int kStages = kLatentStages;
+constexpr int kWaveLoads = (kTileLoads + kWaves - 1) / kWaves;  // 10
+constexpr int kFewestLoads = kTileLoads / kWaves;               // 9
+constexpr int kQkSteps = kLatent / 32;  // 18 score steps
+constexpr int kDimTiles = kValue / 16;  // 32 output dim tiles
+constexpr float kOverflowLog2 = 32.f;   // weights up to 2^32 over the reference
+constexpr int kPastRange = 0x7ffffff0;  // buffer offset past any range: the load gives zeros
+constexpr int kRecordFloats = kLatentRecordFloats;
+constexpr int kCoherent = 16;           // buffer cache policy sc1 (device-coherent)
+
+static_assert(kPageTokens % kTileTokens == 0, "tiles never straddle a page");
+static_assert(kTileTokens == 32, "one value step of 32 tokens per tile");
+
+// ---- tile stream ----------------------------------------------------------
+
+// Position of flat tile f: row b, tile j of the row's n tiles.
+struct Cursor {
+  int b, j, n;
+};
+
+__device__ __forceinline__ Cursor locate_tile(const int* prefix, int B, int f) {
+  Cursor c;
+  c.b = __builtin_amdgcn_readfirstlane(find_sequence(prefix, B, f));
+  c.n = __builtin_amdgcn_readfirstlane(prefix[c.b + 1] - prefix[c.b]);
+  c.j = __builtin_amdgcn_readfirstlane(f - prefix[c.b]);
+  return c;
+}
+
+// Moves to the next flat tile; called only when one exists.
+__device__ __forceinline__ void next_tile(Cursor& c, const int* prefix) {
+  if (++c.j < c.n) return;
+  int b = c.b + 1;
+  while (prefix[b + 1] == prefix[b]) ++b;  // rows of length 0 have no tiles
+  c.b = __builtin_amdgcn_readfirstlane(b);
+  c.j = 0;
+  c.n = __builtin_amdgcn_readfirstlane(prefix[b + 1] - prefix[b]);
+}
+
+// Issues this wave's share of the loads of tile c into `stage`: wave load k
+// (k = wave, wave + 4, ...) fills LDS bytes 1024 k .. 1024 k + 1023, lane l
+// the 16 bytes at 1024 k + 16 l, i.e. chunk ch of token t with
+// 78 t + ch = 64 k + l. Pad chunks (ch >= 72) and tokens past the row get
+// an offset past the descriptor's range, which loads zeros.
+__device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, lds_char* stage,
+                                          int wave, int lane) {
+  const int L = uniform_load(a.seq_lens, c.b);
+  const int valid = min(kTileTokens, L - c.j * kTileTokens);
+  const int page = uniform_load(a.block_tables, (size_t)c.b * a.max_blocks +
+                                                    (c.j / (kPageTokens / kTileTokens)));
+  const char* base =
+      (const char*)a.kv_pool +
+      ((size_t)page * kPageTokens + (size_t)(c.j % (kPageTokens / kTileTokens)) * kTileTokens) *
+          kTokenBytes;
+  const __amdgpu_buffer_rsrc_t r = range_rsrc(base, valid * kTokenBytes);
+#pragma unroll
+  for (int i = 0; i < kWaveLoads; ++i) {
+    const int k = wave + kWaves * i;
+    if (k < kTileLoads) {
+      const int slot = 64 * k + lane;
+      const int t = slot / kRowChunks;
+      const int ch = slot - t * kRowChunks;
+      const int off = ch < kDataChunks ? t * kTokenBytes + ch * 16 : kPastRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, stage + 1024 * k, 16, off, 0, 0, kStreamLoad);
+    }
+  }
+}
+
+// Waits until this wave's loads of the current tile have landed in LDS
+// (vector memory operations complete in order, so at most kFewestLoads
+// younger ones, those of the next tile, may remain), then for every wave of
+// the workgroup to get here: the tile is complete, and every wave is done
+// with the tile before it, whose stage the next loads will overwrite.
+template <bool kNextInFlight>
+__device__ __forceinline__ void tile_barrier() {
+  if (kNextInFlight)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kFewestLoads) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A workgroup barrier for LDS traffic only; outstanding loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---- one wave's 32 heads of one row -----------------------------------------
+//
+// The output accumulator fills the accumulation registers, and the compiler
+// keeps it there only if nothing but the matrix instructions writes it:
+// the fast path never rescales, resets or merges it in place. A segment's
+// first tile starts the accumulator from zero (a zero C operand) and fixes
+// the segment's reference max (its tile max); later weights are
+// 2^(s - reference), which stays far from overflow unless a score exceeds
+// the reference by more than kOverflowLog2 (then the row is flagged and
+// recomputed exactly by the slow path below).
+
+struct RowState {
+  float4_t o[2][kDimTiles];  // O^T[d][h]: dims 16 n + 4 kg + r of head h0 + 16 ht + col
+  float m[2];                // reference max (log2 domain) of the lane's head
+  float l[2];                // this lane's share of the head's sum of weights
+  bool overflow;             // a score exceeded the reference by kOverflowLog2
+};
+
+// The B operand of the score product: head h0 + 16 ht + col, elements
+// 32 s + 8 kg .. + 7.
+__device__ __forceinline__ void load_queries(const LatentArgs& a, int b, int h0, int col, int kg,
+                                             bf16x8_t (&qf)[2][kQkSteps]) {
+  const bf16_t* q = (const bf16_t*)a.q + ((size_t)b * kHeads + h0 + col) * kLatent + kg * 8;
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int s = 0; s < kQkSteps; ++s)
+      qf[ht][s] = *(const bf16x8_t*)(q + (size_t)ht * 16 * kLatent + s * 32);
+}
+
+// Scores of the tile, scaled to the log2 domain: x[ht][tt][r] for token
+// 16 tt + 4 kg + r and head h0 + 16 ht + col; -inf past the row's end (the
+// stage holds zeros there).
+__device__ __forceinline__ void score_tile(const lds_char* tile,
+                                           const bf16x8_t (&qf)[2][kQkSteps], int valid,
+                                           float scale_log2, int col, int kg,
+                                           float (&x)[2][2][4]) {
+  float4_t sc[2][2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) sc[tt][ht] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  // one step of fragments in flight: the scheduler may not hoist further
+  // reads, for which the accumulators and the queries leave no registers
+  const lds_char* krow = tile + col * kRowBytes + kg * 16;
+  bf16x8_t k0 = *(lds_bf16x8*)krow;
+  bf16x8_t k1 = *(lds_bf16x8*)(krow + 16 * kRowBytes);
+#pragma unroll
+  for (int s = 0; s < kQkSteps; ++s) {
+    bf16x8_t n0 = k0, n1 = k1;
+    if (s + 1 < kQkSteps) {
+      n0 = *(lds_bf16x8*)(krow + (s + 1) * 64);
+      n1 = *(lds_bf16x8*)(krow + 16 * kRowBytes + (s + 1) * 64);
+    }
+    sc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][s], sc[0][0], 0, 0, 0);
+    sc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][s], sc[0][1], 0, 0, 0);
+    sc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][s], sc[1][0], 0, 0, 0);
+    sc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][s], sc[1][1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    k0 = n0;
+    k1 = n1;
+  }
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        x[ht][tt][r] = 16 * tt + 4 * kg + r < valid ? sc[tt][ht][r] * scale_log2 : -INFINITY;
+}
+
+// Max of the lane's head over the tile (same in the head's four lanes).
+__device__ __forceinline__ float tile_max(const float (&xh)[2][4]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, xh[tt][r]);
+  return max_over_kg(mx);
+}
+
+// Weights 2^(x - m) as bf16, the value product's B operand (k slot
+// 8 kg + 4 tt + r is token 16 tt + 4 kg + r); returns their sum, taken over
+// the rounded weights so that the normalisation matches the product.
+__device__ __forceinline__ float make_weights(const float (&xh)[2][4], float m, bf16x8_t& pf) {
+  float ps = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const __bf16 p = (__bf16)fast_exp2(xh[tt][r] - m);
+      pf[4 * tt + r] = p;
+      ps += (float)p;
+    }
+  return ps;
+}
+
+// O^T += C^T P^T over the tile (kFirst: O^T = C^T P^T). The transposing
+// read gives lane (kg, col) dim 16 n + col of tokens 16 tt + 4 kg .. + 3
+// when lane 16 kg + 4 e + c4 addresses token 16 tt + 4 kg + e at dims
+// 16 n + 4 c4 .. + 3.
+template <bool kFirst>
+__device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t (&pf)[2],
+                                           float4_t (&o)[2][kDimTiles], int col, int kg) {
+  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const lds_char* vrow = tile + (4 * kg + (col >> 2)) * kRowBytes + (col & 3) * 8;
+  short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)vrow);
+  short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + 16 * kRowBytes));
+#pragma unroll
+  for (int n = 0; n < kDimTiles; ++n) {
+    short4_t n0 = v0, n1 = v1;
+    if (n + 1 < kDimTiles) {
+      n0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + (n + 1) * 32));
+      n1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(vrow + 16 * kRowBytes + (n + 1) * 32));
+    }
+    const bf16x8_t vf = __builtin_bit_cast(
+        bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    o[0][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], kFirst ? zero : o[0][n], 0, 0, 0);
+    o[1][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], kFirst ? zero : o[1][n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    v0 = n0;
+    v1 = n1;
+  }
+}
+
+// Folds a tile into the row state. kFirst: the segment's first tile, which
+// sets the reference max; otherwise a score above reference + kOverflowLog2
+// marks the segment.
+template <bool kFirst>
+__device__ __forceinline__ void fold_tile(const lds_char* tile, const bf16x8_t (&qf)[2][kQkSteps],
+                                          RowState& st, int valid, float scale_log2, int col,
+                                          int kg) {
+  float x[2][2][4];
+  score_tile(tile, qf, valid, scale_log2, col, kg, x);
+  bf16x8_t pf[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const float mt = tile_max(x[ht]);
+    if (kFirst) {
+      st.m[ht] = mt;
+      st.l[ht] = 0.f;
+    } else {
+      st.overflow |= mt > st.m[ht] + kOverflowLog2;
+    }
+    st.l[ht] += make_weights(x[ht], st.m[ht], pf[ht]);
+  }
+  value_tile<kFirst>(tile, pf, st.o, col, kg);
+}
+
+// ---- finishing a row ----------------------------------------------------------
+//
+// Every use of the accumulator here only reads it.
+
+// Row b's outputs of this wave's heads: O^T scaled per head, as bf16.
+__device__ __forceinline__ void store_scaled(const LatentArgs& a, const float4_t (&o)[2][kDimTiles],
+                                             const float (&mul)[2], int b, int h0, int col,
+                                             int kg) {
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    bf16_t* out =
+        (bf16_t*)a.out + ((size_t)b * kHeads + h0 + 16 * ht + col) * kValue + 4 * kg;
+#pragma unroll
+    for (int n = 0; n < kDimTiles; ++n) {
+      const float4_t v = o[ht][n] * mul[ht];
+      *(uint2*)(out + 16 * n) = make_uint2(pack_bf16x2(bf16_rne(v[0]), bf16_rne(v[1])),
+                                           pack_bf16x2(bf16_rne(v[2]), bf16_rne(v[3])));
+    }
+  }
+}
+
+// Record of a piece: O[h][d] (unnormalised, relative to m), m[H], l[H].
+__device__ __forceinline__ int record_base(int slot) { return slot * kRecordFloats * 4; }
+__device__ __forceinline__ int record_o(int slot, int h, int d) {
+  return record_base(slot) + (h * kValue + d) * 4;
+}
+__device__ __forceinline__ int record_m(int slot, int h) {
+  return record_base(slot) + (kHeads * kValue + h) * 4;
+}
+__device__ __forceinline__ int record_l(int slot, int h) {
+  return record_base(slot) + (kHeads * kValue + kHeads + h) * 4;
+}
+
+__device__ __forceinline__ float load_coherent(__amdgpu_buffer_rsrc_t rec, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rec, off, 0, kCoherent));
+}
+__device__ __forceinline__ float4_t load_coherent4(__amdgpu_buffer_rsrc_t rec, int off) {
+  return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rec, off, 0, kCoherent));
+}
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t rec, int off, float4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rec, off, 0, kCoherent);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t rec, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rec, off, 0, kCoherent);
+}
+
+__device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slot,
+                                             const RowState& st, const float (&ltot)[2], int h0,
+                                             int col, int kg) {
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int h = h0 + 16 * ht + col;
+#pragma unroll
+    for (int n = 0; n < kDimTiles; ++n) store_coherent4(rec, record_o(slot, h, 16 * n + 4 * kg), st.o[ht][n]);
+    if (kg == 0) {
+      store_coherent(rec, record_m(slot, h), st.m[ht]);
+      store_coherent(rec, record_l(slot, h), ltot[ht]);
+    }
+  }
+}
+
+// Slot of piece i (0 .. n - 1) of a row cut over workgroups v0 .. v0 + n - 1.
+__device__ __forceinline__ int piece_slot(int v0, int first_slot, int i) {
+  return i == 0 ? first_slot : 2 * (v0 + i);
+}
+
+// The last piece of a cut row: combines every piece, its own from the
+// registers and the others from their records, and writes the row. The
+// log-sum-exp merge adds the pieces in piece order whichever arrived last,
+// so the result does not depend on timing: with two pieces straight to the
+// output, with more through this piece's own record slot (fp32), which
+// holds the running sum between passes.
+__device__ __forceinline__ void merge_and_store(const LatentArgs& a, __amdgpu_buffer_rsrc_t rec,
+                                                const RowState& st, const float (&ltot)[2], int b,
+                                                int v0, int n, int first_slot, int my_slot,
+                                                int h0, int col, int kg) {
+  // merged max and sum per head
+  float M[2], L[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int h = h0 + 16 * ht + col;
+    float mx = -INFINITY;
+    for (int i = 0; i < n; ++i) {
+      const int slot = piece_slot(v0, first_slot, i);
+      mx = fmaxf(mx, slot == my_slot ? st.m[ht] : load_coherent(rec, record_m(slot, h)));
+    }
+    float sum = 0.f;
+    for (int i = 0; i < n; ++i) {
+      const int slot = piece_slot(v0, first_slot, i);
+      const float m = slot == my_slot ? st.m[ht] : load_coherent(rec, record_m(slot, h));
+      const float l = slot == my_slot ? ltot[ht] : load_coherent(rec, record_l(slot, h));
+      sum += l * fast_exp2(m - mx);
+    }
+    M[ht] = mx;
+    L[ht] = sum;
+  }
+  // pass p adds piece p to the sum of pieces 0 .. p - 1
+  for (int p = 1; p < n; ++p) {
+    const int s0 = piece_slot(v0, first_slot, 0);
+    const int sp = piece_slot(v0, first_slot, p);
+    const bool last = p == n - 1;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int h = h0 + 16 * ht + col;
+      const float b0 = fast_exp2((s0 == my_slot ? st.m[ht] : load_coherent(rec, record_m(s0, h))) -
+                                 M[ht]);
+      const float bp = fast_exp2((sp == my_slot ? st.m[ht] : load_coherent(rec, record_m(sp, h))) -
+                                 M[ht]);
+      const float inv = 1.f / L[ht];
+      bf16_t* out = (bf16_t*)a.out + ((size_t)b * kHeads + h) * kValue + 4 * kg;
+#pragma unroll
+      for (int nn = 0; nn < kDimTiles; ++nn) {
+        const int d = 16 * nn + 4 * kg;
+        float4_t sum;
+        if (p == 1)
+          sum = (s0 == my_slot ? st.o[ht][nn] : load_coherent4(rec, record_o(s0, h, d))) * b0;
+        else
+          sum = load_coherent4(rec, record_o(my_slot, h, d));
+        sum += (sp == my_slot ? st.o[ht][nn] : load_coherent4(rec, record_o(sp, h, d))) * bp;
+        if (last) {
+          const float4_t w = sum * inv;
+          *(uint2*)(out + 16 * nn) = make_uint2(pack_bf16x2(bf16_rne(w[0]), bf16_rne(w[1])),
+                                                pack_bf16x2(bf16_rne(w[2]), bf16_rne(w[3])));
+        } else {
+          store_coherent4(rec, record_o(my_slot, h, d), sum);
+        }
+      }
+    }
+    // the running sum is read back by the lanes that wrote it
+    if (!last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// A finished segment (flat tiles seg0 .. seg1 - 1 of row c.b). Whole rows
+// are written; a cut row's piece is counted in, then either written as a
+// record (not the last piece) or merged with the others and written (the
+// last). A segment marked for overflow flags its row for the slow path. The
+// protocol is workgroup-uniform.
+__device__ __forceinline__ void finish_segment(const LatentArgs& a, const Cursor& c,
+                                               const RowState& st, int seg0, int seg1, int f0,
+                                               int chunk, const int* prefix,
+                                               __amdgpu_buffer_rsrc_t rec, int* bcast, int wave,
+                                               int h0, int col, int kg) {
+  const float ltot[2] = {sum_over_kg(st.l[0]), sum_over_kg(st.l[1])};
+  // overflow anywhere in the workgroup flags the row
+  if (__builtin_amdgcn_ballot_w64(st.overflow) != 0 && (threadIdx.x & 63) == 0) bcast[1 + wave] = 1;
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    int any = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      any |= bcast[1 + w];
+      bcast[1 + w] = 0;
+    }
+    if (any) {
+      __hip_atomic_store(a.ws_flag + c.b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(a.ws_ctl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const int row0 = prefix[c.b];
+  const int row1 = prefix[c.b + 1];
+  if (seg0 == row0 && seg1 == row1) {
+    const float inv[2] = {1.f / ltot[0], 1.f / ltot[1]};
+    store_scaled(a, st.o, inv, c.b, h0, col, kg);
+    return;
+  }
+  // pieces: workgroups v0 .. v1; the piece of workgroup v is its first
+  // segment (slot 2 v) unless v = v0 began before the row (slot 2 v + 1)
+  const int v0 = row0 / chunk;
+  const int v1 = (row1 - 1) / chunk;
+  const int first_slot = 2 * v0 + (v0 * chunk < row0 ? 1 : 0);
+  const int my_slot = 2 * (int)blockIdx.x + (seg0 == f0 ? 0 : 1);
+  int* done = a.ws_cnt + 2 * c.b;
+  int* written = done + 1;
+  if (threadIdx.x == 0)
+    bcast[0] = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
+  const int arrived = bcast[0];
+  lds_barrier();  // bcast is free again
+  if (arrived == v1 - v0) {
+    // the last piece: every other piece has counted itself in and is
+    // writing (or has written) its record
+    if (threadIdx.x == 0)
+      while (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < v1 - v0)
+        __builtin_amdgcn_s_sleep(2);
+    lds_barrier();
+    merge_and_store(a, rec, st, ltot, c.b, v0, v1 - v0 + 1, first_slot, my_slot, h0, col, kg);
+    if (threadIdx.x == 0) {  // rearm for the next call
+      __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(written, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    write_record(rec, my_slot, st, ltot, h0, col, kg);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+    lds_barrier();                                     // ... and every wave's
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(written, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---- slow path: rows whose scores outran their reference --------------------
+//
+// Exact two-pass recompute of row b by one workgroup: the first pass finds
+// every head's maximum score, the second folds the row with it as the
+// reference (all weights <= 1). Runs only after the streaming loop, when
+// the accumulator registers are free.
+__device__ __forceinline__ void recompute_row(const LatentArgs& a, const int* prefix, int b,
+                                              lds_char* stage, int wave, int lane, int h0,
+                                              int col, int kg) {
+  Cursor c;
+  c.b = b;
+  c.n = prefix[b + 1] - prefix[b];
+  const int L = uniform_load(a.seq_lens, b);
+  bf16x8_t qf[2][kQkSteps];
+  load_queries(a, b, h0, col, kg, qf);
+  float mx[2] = {-INFINITY, -INFINITY};
+  for (c.j = 0; c.j < c.n; ++c.j) {
+    load_tile(a, c, stage, wave, lane);
+    tile_barrier<false>();
+    float x[2][2][4];
+    score_tile(stage, qf, min(kTileTokens, L - c.j * kTileTokens), a.scale_log2, col, kg, x);
+    mx[0] = fmaxf(mx[0], tile_max(x[0]));
+    mx[1] = fmaxf(mx[1], tile_max(x[1]));
+    lds_barrier();  // everyone is done with the stage
+  }
+  RowState st;
+  for (c.j = 0; c.j < c.n; ++c.j) {
+    load_tile(a, c, stage, wave, lane);
+    tile_barrier<false>();
+    float x[2][2][4];
+    score_tile(stage, qf, min(kTileTokens, L - c.j * kTileTokens), a.scale_log2, col, kg, x);
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const float w = make_weights(x[ht], mx[ht], pf[ht]);
+      st.l[ht] = c.j == 0 ? w : st.l[ht] + w;
+    }
+    if (c.j == 0)
+      value_tile<true>(stage, pf, st.o, col, kg);
+    else
+      value_tile<false>(stage, pf, st.o, col, kg);
+    lds_barrier();
+  }
+  const float inv[2] = {1.f / sum_over_kg(st.l[0]), 1.f / sum_over_kg(st.l[1])};
+  store_scaled(a, st.o, inv, b, h0, col, kg);
+}
+
+__global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
+  // dynamic LDS: kStages tile stages, then the work-list prefix [B + 1]
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int scan_scratch[kWaves];
+  __shared__ int bcast[1 + kWaves];
+  lds_char* stages = (lds_char*)smem;
+  int* prefix = (int*)(smem + kStages * kStageBytes);
+
+  const int B = a.num_seqs;
+  if (threadIdx.x < 1 + kWaves) bcast[threadIdx.x] = 0;
+  build_partition_prefix(a.seq_lens, B, kTileTokens, prefix, scan_scratch);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int h0 = wave * kHeadsPerWave;
+
+  // rows of length 0 are zeros: workgroup g writes rows g, g + grid, ...
+  for (int b = blockIdx.x; b < B; b += a.grid) {
+    if (prefix[b + 1] != prefix[b]) continue;
+    uint4* o = (uint4*)((bf16_t*)a.out + (size_t)b * kHeads * kValue);
+    for (int i = threadIdx.x; i < kHeads * kValue / 8; i += 256) o[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  const int total = prefix[B];
+  const int chunk = max((total + a.grid - 1) / a.grid, a.min_tiles);
+  const int f0 = blockIdx.x * chunk;
+  const int f1 = min(f0 + chunk, total);
+  const __amdgpu_buffer_rsrc_t rec = range_rsrc(a.ws_rec, 2 * a.grid * kRecordFloats * 4);
+
+  if (f0 < f1) {
+    Cursor cc = locate_tile(prefix, B, f0);
+    Cursor lc = cc;
+    load_tile(a, lc, stages, wave, lane);
+    if (f0 + 1 < f1) {
+      next_tile(lc, prefix);
+      load_tile(a, lc, stages + kStageBytes, wave, lane);
+    }
+    // tile f of the range sits in stage (f - f0) % kStages; segments: the
+    // range's part of one row each, inside which the queries and the row
+    // state live
+    for (int f = f0; f < f1;) {
+      const int seg0 = f;
+      const int seg1 = min(f1, prefix[cc.b + 1]);
+      const int L = uniform_load(a.seq_lens, cc.b);
+      bf16x8_t qf[2][kQkSteps];
+      load_queries(a, cc.b, h0, col, kg, qf);
+      RowState st;
+      st.overflow = false;
+      for (; f < seg1; ++f) {
+        if (f + 1 < f1)
+          tile_barrier<true>();
+        else
+          tile_barrier<false>();
+        if (f + 2 < f1) {
+          next_tile(lc, prefix);
+          load_tile(a, lc, stages + ((f + 2 - f0) % kStages) * kStageBytes, wave, lane);
+        }
+        const int valid = min(kTileTokens, L - (cc.j + f - seg0) * kTileTokens);
+        const lds_char* tile = stages + ((f - f0) % kStages) * kStageBytes;
+        if (f == seg0)
+          fold_tile<true>(tile, qf, st, valid, a.scale_log2, col, kg);
+        else
+          fold_tile<false>(tile, qf, st, valid, a.scale_log2, col, kg);
+      }
+      finish_segment(a, cc, st, seg0, seg1, f0, chunk, prefix, rec, bcast, wave, h0, col, kg);
+      if (f < f1) {  // the next row with tiles
+        int b = cc.b + 1;
+        while (prefix[b + 1] == prefix[b]) ++b;
+        cc.b = __builtin_amdgcn_readfirstlane(b);
+        cc.j = 0;
+        cc.n = __builtin_amdgcn_readfirstlane(prefix[b + 1] - prefix[b]);
+      }
+    }
+  }
+
+  // every workgroup counts itself out; the last one recomputes flagged rows
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (threadIdx.x == 0)
+    bcast[0] = __hip_atomic_fetch_add(a.ws_ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
+  if (bcast[0] != a.grid - 1) return;
+  if (__hip_atomic_load(a.ws_ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > 0) {
+    for (int b = 0; b < B; ++b) {
+      if (__hip_atomic_load(a.ws_flag + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        continue;
+      recompute_row(a, prefix, b, stages, wave, lane, h0, col, kg);
+      lds_barrier();
+      if (threadIdx.x == 0)
+        __hip_atomic_store(a.ws_flag + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (threadIdx.x == 0) {  // rearm for the next call
+    __hip_atomic_store(a.ws_ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.ws_ctl + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace
+
+const void* latent_decode_fn() { return (const void*)latent_decode_kernel; }
+
+size_t latent_decode_smem(int num_seqs) {
+  return (size_t)kStages * kStageBytes + (size_t)(num_seqs + 1) * sizeof(int);
+}
+
+hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(latent_decode_kernel, dim3(a.grid), dim3(256), latent_decode_smem(a.num_seqs),
+                     s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pagedkv

@@ -52,6 +52,25 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
 const void* prefill_mfma_fn(int head_dim);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int head_dim, int grid, hipStream_t s);
 
+// Latent (MLA-style) decode, fixed shape: 128 heads over one 576-element
+// latent per token (512 value elements), 64-token blocks, 32-token tiles in
+// three LDS stages of 39 KiB, one workgroup of 256 threads per compute unit.
+constexpr int kLatentHeads = 128;
+constexpr int kLatentDim = 576;
+constexpr int kLatentValueDim = 512;
+constexpr int kLatentBlockTokens = 64;
+constexpr int kLatentTileTokens = 32;
+constexpr int kLatentStageBytes = 39 * 1024;
+constexpr int kLatentStages = 3;
+// fp32 record of one piece of a cut row: O[H][512], then m[H], then l[H]
+constexpr int kLatentRecordFloats = kLatentHeads * kLatentValueDim + 2 * kLatentHeads;
+const void* latent_decode_fn();
+size_t latent_decode_smem(int num_seqs);
+hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t s);
+// Latent append: kv_pool row slot_mapping[t] <- kv_new[t] (576 elements).
+hipError_t launch_latent_write(const void* kv_new, const int32_t* slots, int num_tokens,
+                               void* kv_pool, hipStream_t s);
+
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* slots,
                            int num_tokens, void* k_pool, void* v_pool, int num_kv_heads,
                            int head_dim, int block_shift, int elem_bytes, hipStream_t s);

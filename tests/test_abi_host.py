@@ -226,3 +226,68 @@ def test_validator_rejects(case):
         kw["block_mapping"] = np.array([[0, 3], [1, 3]], dtype=np.int32)
     with pytest.raises(ValueError):
         pk.validate(**kw)
+
+
+# --------------------------------------------------------------------------
+# latent (MLA-style) decode
+# --------------------------------------------------------------------------
+
+def latent_dims(**kw):
+    base = dict(num_seqs=256, max_blocks_per_seq=128, num_blocks=7000)
+    base.update(kw)
+    return pk.make_latent_dims(**base)
+
+
+def test_latent_workspace_size(lib):
+    align = lambda x: (x + 255) // 256 * 256
+    B = 256
+    rec = 128 * 512 + 2 * 128
+    off_flag = align(256 + 2 * B * 4)
+    off_rec = align(off_flag + B * 4)
+    assert pk.pa_latent_workspace_bytes(latent_dims()) == off_rec + 2 * 256 * rec * 4
+    assert pk.pa_latent_workspace_bytes(latent_dims(num_heads=64)) == 0
+    assert pk.pa_latent_workspace_bytes(latent_dims(num_seqs=0)) == 0
+
+
+def latent_status(lib, d, q=FAKE, ws=FAKE, wsb=None, scale=0.05):
+    if wsb is None:
+        wsb = pk.pa_latent_workspace_bytes(d) or (1 << 30)
+    return lib.pa_latent_decode(q, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE,
+                                ctypes.byref(d), ws, ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=0), pk.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), pk.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), pk.PA_ERR_INVALID_ARG),
+    (dict(value_dim=600), pk.PA_ERR_INVALID_ARG),
+    (dict(dtype=7), pk.PA_ERR_INVALID_ARG),
+    (dict(dtype=pk.PA_F32), pk.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=64), pk.PA_ERR_UNSUPPORTED),
+    (dict(latent_dim=512, value_dim=512), pk.PA_ERR_UNSUPPORTED),
+    (dict(value_dim=576), pk.PA_ERR_UNSUPPORTED),
+    (dict(block_size=16), pk.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=5000), pk.PA_ERR_UNSUPPORTED),
+])
+def test_latent_rejects_bad_dims(lib, kw, status):
+    assert latent_status(lib, latent_dims(**kw)) == status
+
+
+def test_latent_rejects_null_and_small_workspace(lib):
+    d = latent_dims()
+    need = pk.pa_latent_workspace_bytes(d)
+    assert latent_status(lib, d, q=None) == pk.PA_ERR_INVALID_ARG
+    assert latent_status(lib, d, ws=None) == pk.PA_ERR_INVALID_ARG
+    assert latent_status(lib, d, wsb=need - 1) == pk.PA_ERR_INVALID_ARG
+    assert latent_status(lib, d, scale=float("inf")) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_latent_decode(FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, None, FAKE,
+                                ctypes.c_size_t(need), None) == pk.PA_ERR_INVALID_ARG
+
+
+def test_latent_write_rejects_bad_args(lib):
+    d = latent_dims()
+    assert lib.pa_latent_write(FAKE, FAKE, -1, FAKE, ctypes.byref(d), None) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_latent_write(None, FAKE, 3, FAKE, ctypes.byref(d), None) == pk.PA_ERR_INVALID_ARG
+    assert lib.pa_latent_write(None, None, 0, None, ctypes.byref(d), None) == pk.PA_OK
+    bad = latent_dims(block_size=32)
+    assert lib.pa_latent_write(FAKE, FAKE, 3, FAKE, ctypes.byref(bad), None) == pk.PA_ERR_UNSUPPORTED

@@ -1,0 +1,178 @@
+"""pa_latent_decode (MLA-style latent decode) and pa_latent_write on the GPU
+against the float64 oracle on the same seeded inputs, to the bf16 bar
+(per-row RMS). Poisoned memory (unused blocks, tail slots) must never leak
+into a result; rows cut across workgroups (one cut, many cuts, rows spread
+over dozens of workgroups) must merge exactly like whole rows; repeated
+calls must reuse the workspace and give bit-identical results; a row whose
+scores outrun the reference of its first tile must take the exact slow
+path."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_55_amd as pk
+import workloads as wl
+from parity import bits_equal, compare, gpu_out_f64
+from workloads import to_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_latent(c, rows=None):
+    return oracle.latent_decode(to_numpy(c.q), to_numpy(c.kv_pool), to_numpy(c.block_tables),
+                                to_numpy(c.seq_lens), c.scale, c.dtype, rows=rows)
+
+
+def gpu_latent(c, workspace=None):
+    d = c.to("cuda")
+    out = pk.pa_latent_decode(d.q, d.kv_pool, d.block_tables, d.seq_lens, c.scale,
+                              workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(c, rows=None):
+    print(f"latent case B={c.q.shape[0]} lens[:8]={c.seq_lens[:8].tolist()}", flush=True)
+    out = gpu_latent(c)
+    ref = oracle_latent(c, rows)
+    sel = range(c.q.shape[0]) if rows is None else rows
+    got = gpu_out_f64(out, None if rows is None else rows)
+    return compare(got, ref, c.seq_lens.numpy()[list(sel)], "bf16")
+
+
+def test_latent_edge_lengths():
+    lens = [0, 1, 31, 32, 33, 63, 64, 65, 127, 200, 1000, 0, 2]
+    check(wl.latent_case(1001, lens))
+
+
+def test_latent_many_cuts():
+    """Short rows, so every workgroup range (8 tiles at least) cuts rows;
+    some rows span three or more workgroups."""
+    rng = np.random.default_rng(1002)
+    check(wl.latent_case(1002, rng.integers(1, 3000, size=40)))
+
+
+@pytest.mark.parametrize("lens", [[20000], [20000, 5, 7000, 0]])
+def test_latent_long_rows_over_many_workgroups(lens):
+    """A 20,000-token row is 625 tiles, spread over dozens of workgroups."""
+    check(wl.latent_case(1003 + len(lens), lens))
+
+
+def test_latent_decode_batch_full_size_sampled():
+    """The measured workload (B = 256, the 70B serving batch's length mix):
+    the kernel runs over the whole batch; the oracle checks 16 rows, the
+    longest and shortest among them."""
+    c = wl.latent_decode_batch()
+    lens = c.seq_lens.numpy()
+    order = np.argsort(lens)
+    rows = sorted(set(order[:4].tolist() + order[-4:].tolist() +
+                      np.random.default_rng(7).choice(len(lens), 8, replace=False).tolist()))
+    worst = check(c, rows)
+    print(f"latent full-size worst ratio {worst:.3f}")
+
+
+def test_latent_repeat_calls_are_identical():
+    """Two calls on one workspace: the counters rearm, and the merge order
+    does not depend on which piece arrives last."""
+    rng = np.random.default_rng(1005)
+    c = wl.latent_case(1005, rng.integers(1, 4000, size=30))
+    d = c.to("cuda")
+    ws = torch.zeros(pk.pa_latent_workspace_bytes(
+        pk.make_latent_dims(30, c.block_tables.shape[1], c.kv_pool.shape[0])),
+        dtype=torch.uint8, device="cuda")
+    a = pk.pa_latent_decode(d.q, d.kv_pool, d.block_tables, d.seq_lens, c.scale, workspace=ws)
+    b = pk.pa_latent_decode(d.q, d.kv_pool, d.block_tables, d.seq_lens, c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    compare(gpu_out_f64(a), oracle_latent(c), c.seq_lens.numpy(), "bf16")
+
+
+def spiked_case(seed, gain):
+    """Row 2 (5,000 tokens, cut across many workgroups) holds one latent at
+    position 3,100 equal to `gain` times the query of head 0, whose score
+    then exceeds every score of its piece's first tile by about
+    gain * 576 / 24 natural-log units: far beyond the 2^32 weight margin, so
+    the row must be recomputed by the exact path. At gain 1.5 the fast path
+    would still be finite (weights near 2^49); at gain 5 its weights
+    overflow fp32, so only the exact path can give a finite result."""
+    c = wl.latent_case(seed, [2000, 300, 5000, 40])
+    b, t = 2, 3100
+    bs = c.kv_pool.shape[1]
+    blk = int(c.block_tables[b, t // bs])
+    q0 = c.q[b, 0].float()
+    c.kv_pool[blk, t % bs] = (gain * q0).to(c.kv_pool.dtype)
+    return c
+
+
+@pytest.mark.parametrize("gain", [1.5, 5.0])
+def test_latent_overflow_takes_the_exact_path(gain):
+    c = spiked_case(1006, gain)
+    check(c)
+    # a normal call afterwards on a fresh workspace
+    check(wl.latent_case(1007, [100, 2000]))
+
+
+def test_latent_overflow_then_normal_on_one_workspace():
+    """The flags and control counters are rearmed by the call that used them."""
+    c = spiked_case(1008, 5.0)
+    d = c.to("cuda")
+    dims = pk.make_latent_dims(4, c.block_tables.shape[1], c.kv_pool.shape[0])
+    ws = torch.zeros(pk.pa_latent_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = pk.pa_latent_decode(d.q, d.kv_pool, d.block_tables, d.seq_lens, c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    compare(gpu_out_f64(out), oracle_latent(c), c.seq_lens.numpy(), "bf16")
+    c2 = wl.latent_case(1009, [2000, 300, 5000, 40])
+    d2 = c2.to("cuda")
+    out2 = pk.pa_latent_decode(d2.q, d2.kv_pool, d2.block_tables, d2.seq_lens, c2.scale,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    compare(gpu_out_f64(out2), oracle_latent(c2), c2.seq_lens.numpy(), "bf16")
+    # all control words are back to zero
+    head = ws[:256].view(torch.int32).cpu()
+    assert int(head[0]) == 0 and int(head[1]) == 0
+
+
+def test_latent_write_bit_exact():
+    rng = np.random.default_rng(1010)
+    gen = torch.Generator().manual_seed(1010)
+    nb, T = 9, 70
+    pool = torch.full((nb, 64, 576), float("nan"), dtype=torch.bfloat16)
+    new = torch.randn((T, 576), generator=gen).to(torch.bfloat16)
+    slots = rng.choice(nb * 64, size=T, replace=False).astype(np.int32)
+    slots[::7] = -1
+    ref = to_numpy(pool).copy()
+    for t, s in enumerate(slots.tolist()):
+        if s >= 0:
+            ref[s // 64, s % 64] = to_numpy(new)[t]
+    g = pool.cuda()
+    pk.pa_latent_write(new.cuda(), torch.from_numpy(slots).cuda(), g)
+    torch.cuda.synchronize()
+    assert bits_equal(g, ref)
+
+
+def test_latent_write_then_decode():
+    """The decode step: each row's newest latent is appended, then the row
+    attends over its cache including it."""
+    lens = [1, 64, 65, 500]
+    c = wl.latent_case(1011, lens)
+    gen = torch.Generator().manual_seed(1011)
+    new = torch.randn((len(lens), 576), generator=gen).to(torch.bfloat16)
+    slots = np.array([int(c.block_tables[b, (L - 1) // 64]) * 64 + (L - 1) % 64
+                      for b, L in enumerate(lens)], dtype=np.int32)
+    d = c.to("cuda")
+    pk.pa_latent_write(new.cuda(), torch.from_numpy(slots).cuda(), d.kv_pool)
+    out = pk.pa_latent_decode(d.q, d.kv_pool, d.block_tables, d.seq_lens, c.scale)
+    torch.cuda.synchronize()
+    host = c.kv_pool.clone()
+    for b, s in enumerate(slots.tolist()):
+        host[s // 64, s % 64] = new[b]
+    c2 = wl.LatentCase(c.q, host, c.block_tables, c.seq_lens, c.scale, c.dtype)
+    compare(gpu_out_f64(out), oracle_latent(c2), np.array(lens), "bf16")
+
+
+def test_latent_rejects_unsupported():
+    c = wl.latent_case(1012, [10, 20], num_heads=64).to("cuda")
+    with pytest.raises(pk.PagedKVError):
+        pk.pa_latent_decode(c.q, c.kv_pool, c.block_tables, c.seq_lens, c.scale)
