@@ -287,7 +287,7 @@ pa_status plan_latent(const pa_latent_dims* d, LatentPlan* p) {
   p->off_cnt = kAlign;
   p->off_flag = align_up(p->off_cnt + 2 * B * sizeof(int));
   p->off_rec = align_up(p->off_flag + B * sizeof(int));
-  p->ws_bytes = p->off_rec + (size_t)2 * kMaxLatentGrid * kLatentRecordFloats * sizeof(float);
+  p->ws_bytes = p->off_rec + (size_t)2 * kMaxLatentGrid * kLatentRecordBytes;
   return PA_OK;
 }
 

@@ -34,10 +34,13 @@
 // per compute unit). A row cut by range boundaries is finished by the last
 // of its pieces to arrive: each piece first counts itself in; the last one
 // waits until the others, which have all counted already and so are
-// running, have written their fp32 records (O, m, l of 128 heads), folds
-// them into its own registers and writes the row. A cut thus costs one
-// record write and one read (a record is 257 KiB, as much as 229 tokens of
-// latent cache), and no workgroup ever waits for one that has not started.
+// running, have written their records (output normalised by the piece's
+// sum as bf16, max and sum as fp32: 129 KiB, as much as 115 tokens of
+// latent cache), merges them with its own piece and writes the row. A cut
+// thus costs one record write and one read, and no workgroup ever waits
+// for one that has not started.
+#include <type_traits>
+
 #include "launch.h"
 #include "mfma_tile.h"
 #include "worklist.h"
@@ -51,6 +54,7 @@ using namespace mfma;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kHeads = kLatentHeads;
@@ -74,7 +78,8 @@ constexpr int kQkSteps = kLatent / 32;  // 18 score steps
 constexpr int kDimTiles = kValue / 16;  // 32 output dim tiles
 constexpr float kOverflowLog2 = 32.f;   // weights up to 2^32 over the reference
 constexpr int kPastRange = 0x7ffffff0;  // buffer offset past any range: the load gives zeros
-constexpr int kRecordFloats = kLatentRecordFloats;
+constexpr int kRecordBytes = kLatentRecordBytes;
+constexpr int kMergeBatch = 8;          // pieces whose loads a merge round issues together
 constexpr int kCoherent = 16;           // buffer cache policy sc1 (device-coherent)
 
 static_assert(kPageTokens % kTileTokens == 0, "tiles never straddle a page");
@@ -105,6 +110,34 @@ __device__ __forceinline__ void next_tile(Cursor& c, const int* prefix) {
   c.n = __builtin_amdgcn_readfirstlane(prefix[b + 1] - prefix[b]);
 }
 
+// A raw buffer descriptor of `bytes` bytes at `base` (32-bit data format,
+// unswizzled; reads past the range give zero).
+__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)base;
+  return (u32x4_t){(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer at byte offset `off` into LDS at
+// `dst` + 16 * lane (buffer_load_dwordx4 with the LDS destination in M0,
+// streaming cache policy). Written as assembly so that the compiler does
+// not track these LDS writes: it cannot tell the tile stages apart and
+// would otherwise make every later LDS read wait for all of them, the
+// prefetch included. Completion is awaited explicitly (tile_barrier). M0
+// belongs to the compiler, so the sequence restores it.
+__device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(off), "s"(rsrc)
+      : "memory");
+}
+
 // Issues this wave's share of the loads of tile c into `stage`: wave load k
 // (k = wave, wave + 4, ...) fills LDS bytes 1024 k .. 1024 k + 1023, lane l
 // the 16 bytes at 1024 k + 16 l, i.e. chunk ch of token t with
@@ -120,7 +153,7 @@ __device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, 
       (const char*)a.kv_pool +
       ((size_t)page * kPageTokens + (size_t)(c.j % (kPageTokens / kTileTokens)) * kTileTokens) *
           kTokenBytes;
-  const __amdgpu_buffer_rsrc_t r = range_rsrc(base, valid * kTokenBytes);
+  const u32x4_t r = raw_rsrc(base, valid * kTokenBytes);
 #pragma unroll
   for (int i = 0; i < kWaveLoads; ++i) {
     const int k = wave + kWaves * i;
@@ -129,7 +162,7 @@ __device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, 
       const int t = slot / kRowChunks;
       const int ch = slot - t * kRowChunks;
       const int off = ch < kDataChunks ? t * kTokenBytes + ch * 16 : kPastRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, stage + 1024 * k, 16, off, 0, 0, kStreamLoad);
+      load_to_lds(r, stage + 1024 * k, off);
     }
   }
 }
@@ -327,29 +360,50 @@ __device__ __forceinline__ void store_scaled(const LatentArgs& a, const float4_t
   }
 }
 
-// Record of a piece: O[h][d] (unnormalised, relative to m), m[H], l[H].
-__device__ __forceinline__ int record_base(int slot) { return slot * kRecordFloats * 4; }
-__device__ __forceinline__ int record_o(int slot, int h, int d) {
-  return record_base(slot) + (h * kValue + d) * 4;
+// Record of a piece: x[h][d] = bf16(O / l), then m[H], then l[H] (fp32).
+__device__ __forceinline__ int record_base(int slot) { return slot * kRecordBytes; }
+__device__ __forceinline__ int record_x(int slot, int h, int d) {
+  return record_base(slot) + (h * kValue + d) * 2;
 }
 __device__ __forceinline__ int record_m(int slot, int h) {
-  return record_base(slot) + (kHeads * kValue + h) * 4;
+  return record_base(slot) + kHeads * kValue * 2 + h * 4;
 }
 __device__ __forceinline__ int record_l(int slot, int h) {
-  return record_base(slot) + (kHeads * kValue + kHeads + h) * 4;
+  return record_base(slot) + kHeads * kValue * 2 + kHeads * 4 + h * 4;
 }
 
 __device__ __forceinline__ float load_coherent(__amdgpu_buffer_rsrc_t rec, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rec, off, 0, kCoherent));
 }
-__device__ __forceinline__ float4_t load_coherent4(__amdgpu_buffer_rsrc_t rec, int off) {
-  return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rec, off, 0, kCoherent));
+__device__ __forceinline__ uint2 load_coherent8(__amdgpu_buffer_rsrc_t rec, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rec, off, 0, kCoherent));
 }
-__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t rec, int off, float4_t v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rec, off, 0, kCoherent);
+__device__ __forceinline__ void store_coherent8(__amdgpu_buffer_rsrc_t rec, int off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rec, off, 0, kCoherent);
 }
 __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t rec, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rec, off, 0, kCoherent);
+}
+
+// A piece's normalised output chunk (4 dims of one head) as 4 bf16: what
+// its record holds, computed the same way for a piece kept in registers.
+__device__ __forceinline__ uint2 normalised_chunk(float4_t o, float inv) {
+  const float4_t v = o * inv;
+  return make_uint2(pack_bf16x2(bf16_rne(v[0]), bf16_rne(v[1])),
+                    pack_bf16x2(bf16_rne(v[2]), bf16_rne(v[3])));
+}
+
+__device__ __forceinline__ float4_t zero4() { return (float4_t){0.f, 0.f, 0.f, 0.f}; }
+
+// x * w + acc elementwise, one rounding each (the merge's only operation,
+// so that its result depends on the pieces' order alone)
+__device__ __forceinline__ float4_t fma4(float4_t x, float w, float4_t acc) {
+  return (float4_t){__builtin_fmaf(x[0], w, acc[0]), __builtin_fmaf(x[1], w, acc[1]),
+                    __builtin_fmaf(x[2], w, acc[2]), __builtin_fmaf(x[3], w, acc[3])};
+}
+
+__device__ __forceinline__ float4_t widen(uint2 x) {
+  return (float4_t){bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
 }
 
 __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slot,
@@ -358,8 +412,10 @@ __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slo
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int h = h0 + 16 * ht + col;
+    const float inv = 1.f / ltot[ht];
 #pragma unroll
-    for (int n = 0; n < kDimTiles; ++n) store_coherent4(rec, record_o(slot, h, 16 * n + 4 * kg), st.o[ht][n]);
+    for (int n = 0; n < kDimTiles; ++n)
+      store_coherent8(rec, record_x(slot, h, 16 * n + 4 * kg), normalised_chunk(st.o[ht][n], inv));
     if (kg == 0) {
       store_coherent(rec, record_m(slot, h), st.m[ht]);
       store_coherent(rec, record_l(slot, h), ltot[ht]);
@@ -372,70 +428,120 @@ __device__ __forceinline__ int piece_slot(int v0, int first_slot, int i) {
   return i == 0 ? first_slot : 2 * (v0 + i);
 }
 
-// The last piece of a cut row: combines every piece, its own from the
-// registers and the others from their records, and writes the row. The
-// log-sum-exp merge adds the pieces in piece order whichever arrived last,
-// so the result does not depend on timing: with two pieces straight to the
-// output, with more through this piece's own record slot (fp32), which
-// holds the running sum between passes.
+// The last piece of a cut row writes the row: out = sum_i w_i x_i over the
+// pieces in piece order, x_i the piece's normalised output rounded to bf16
+// (its own computed from the registers exactly as its record would hold
+// it), w_i = l_i 2^(m_i - M) / L (log-sum-exp merge). The result is thus the
+// same whichever piece arrives last. Loads are issued a batch at a time: a
+// two-piece row (the common cut) takes one round trip for the other
+// piece's (m, l) and one for its data.
 __device__ __forceinline__ void merge_and_store(const LatentArgs& a, __amdgpu_buffer_rsrc_t rec,
                                                 const RowState& st, const float (&ltot)[2], int b,
                                                 int v0, int n, int first_slot, int my_slot,
                                                 int h0, int col, int kg) {
-  // merged max and sum per head
-  float M[2], L[2];
+  float M[2], L[2], inv_mine[2];
+  // merged max and sum per head, kMergeBatch pieces per round
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const int h = h0 + 16 * ht + col;
-    float mx = -INFINITY;
-    for (int i = 0; i < n; ++i) {
-      const int slot = piece_slot(v0, first_slot, i);
-      mx = fmaxf(mx, slot == my_slot ? st.m[ht] : load_coherent(rec, record_m(slot, h)));
-    }
-    float sum = 0.f;
-    for (int i = 0; i < n; ++i) {
-      const int slot = piece_slot(v0, first_slot, i);
-      const float m = slot == my_slot ? st.m[ht] : load_coherent(rec, record_m(slot, h));
-      const float l = slot == my_slot ? ltot[ht] : load_coherent(rec, record_l(slot, h));
-      sum += l * fast_exp2(m - mx);
-    }
-    M[ht] = mx;
-    L[ht] = sum;
+    M[ht] = st.m[ht];
+    L[ht] = 0.f;  // accumulated in piece order below
+    inv_mine[ht] = 1.f / ltot[ht];
   }
-  // pass p adds piece p to the sum of pieces 0 .. p - 1
-  for (int p = 1; p < n; ++p) {
-    const int s0 = piece_slot(v0, first_slot, 0);
-    const int sp = piece_slot(v0, first_slot, p);
-    const bool last = p == n - 1;
+  for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       const int h = h0 + 16 * ht + col;
-      const float b0 = fast_exp2((s0 == my_slot ? st.m[ht] : load_coherent(rec, record_m(s0, h))) -
-                                 M[ht]);
-      const float bp = fast_exp2((sp == my_slot ? st.m[ht] : load_coherent(rec, record_m(sp, h))) -
-                                 M[ht]);
-      const float inv = 1.f / L[ht];
-      bf16_t* out = (bf16_t*)a.out + ((size_t)b * kHeads + h) * kValue + 4 * kg;
+      float mv[kMergeBatch];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int slot = piece_slot(v0, first_slot, i0 + j);
+        const bool other = i0 + j < n && slot != my_slot;
+        mv[j] = other ? load_coherent(rec, record_m(slot, h)) : -INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) M[ht] = fmaxf(M[ht], mv[j]);
+    }
+  }
+  for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int h = h0 + 16 * ht + col;
+      float mv[kMergeBatch], lv[kMergeBatch];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int slot = piece_slot(v0, first_slot, i0 + j);
+        const bool mine = slot == my_slot;
+        const bool other = i0 + j < n && !mine;
+        mv[j] = other ? load_coherent(rec, record_m(slot, h)) : (mine ? st.m[ht] : -INFINITY);
+        lv[j] = other ? load_coherent(rec, record_l(slot, h)) : (mine ? ltot[ht] : 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j)
+        if (i0 + j < n) L[ht] += lv[j] * fast_exp2(mv[j] - M[ht]);
+    }
+  }
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int h = h0 + 16 * ht + col;
+    bf16_t* out = (bf16_t*)a.out + ((size_t)b * kHeads + h) * kValue + 4 * kg;
+    const float invL = 1.f / L[ht];
+    if (n == 2) {
+      const int other = piece_slot(v0, first_slot, first_slot == my_slot ? 1 : 0);
+      const float mo = load_coherent(rec, record_m(other, h));
+      const float lo = load_coherent(rec, record_l(other, h));
+      const float w_mine = ltot[ht] * fast_exp2(st.m[ht] - M[ht]) * invL;
+      const float w_other = lo * fast_exp2(mo - M[ht]) * invL;
+      const bool mine_first = first_slot == my_slot;
+      const float w0 = mine_first ? w_mine : w_other;
+      const float w1 = mine_first ? w_other : w_mine;
+      uint2 xo[kDimTiles];
+#pragma unroll
+      for (int nn = 0; nn < kDimTiles; ++nn)
+        xo[nn] = load_coherent8(rec, record_x(other, h, 16 * nn + 4 * kg));
 #pragma unroll
       for (int nn = 0; nn < kDimTiles; ++nn) {
-        const int d = 16 * nn + 4 * kg;
-        float4_t sum;
-        if (p == 1)
-          sum = (s0 == my_slot ? st.o[ht][nn] : load_coherent4(rec, record_o(s0, h, d))) * b0;
-        else
-          sum = load_coherent4(rec, record_o(my_slot, h, d));
-        sum += (sp == my_slot ? st.o[ht][nn] : load_coherent4(rec, record_o(sp, h, d))) * bp;
-        if (last) {
-          const float4_t w = sum * inv;
-          *(uint2*)(out + 16 * nn) = make_uint2(pack_bf16x2(bf16_rne(w[0]), bf16_rne(w[1])),
-                                                pack_bf16x2(bf16_rne(w[2]), bf16_rne(w[3])));
-        } else {
-          store_coherent4(rec, record_o(my_slot, h, d), sum);
-        }
+        const float4_t xm = widen(normalised_chunk(st.o[ht][nn], inv_mine[ht]));
+        const float4_t xp = widen(xo[nn]);
+        // piece 0, then piece 1, as the general path sums
+        const float4_t v = fma4(mine_first ? xp : xm, w1, fma4(mine_first ? xm : xp, w0, zero4()));
+        *(uint2*)(out + 16 * nn) = make_uint2(pack_bf16x2(bf16_rne(v[0]), bf16_rne(v[1])),
+                                              pack_bf16x2(bf16_rne(v[2]), bf16_rne(v[3])));
       }
+      continue;
     }
-    // the running sum is read back by the lanes that wrote it
-    if (!last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // more pieces: 8 dims tiles at a time, kMergeBatch pieces per round
+#pragma unroll
+    for (int g = 0; g < kDimTiles; g += 8) {
+      float4_t acc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = zero4();
+      for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+        float w[kMergeBatch];
+        uint2 x[kMergeBatch][8];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const int slot = piece_slot(v0, first_slot, i0 + j);
+          const bool other = i0 + j < n && slot != my_slot;
+          const float mj = other ? load_coherent(rec, record_m(slot, h)) : st.m[ht];
+          const float lj = other ? load_coherent(rec, record_l(slot, h)) : ltot[ht];
+          w[j] = i0 + j < n ? lj * fast_exp2(mj - M[ht]) * invL : 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            x[j][u] = other ? load_coherent8(rec, record_x(slot, h, 16 * (g + u) + 4 * kg))
+                            : normalised_chunk(st.o[ht][g + u], inv_mine[ht]);
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (i0 + j < n) acc[u] = fma4(widen(x[j][u]), w[j], acc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        *(uint2*)(out + 16 * (g + u)) =
+            make_uint2(pack_bf16x2(bf16_rne(acc[u][0]), bf16_rne(acc[u][1])),
+                       pack_bf16x2(bf16_rne(acc[u][2]), bf16_rne(acc[u][3])));
+    }
   }
 }
 
@@ -581,7 +687,7 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
   const int chunk = max((total + a.grid - 1) / a.grid, a.min_tiles);
   const int f0 = blockIdx.x * chunk;
   const int f1 = min(f0 + chunk, total);
-  const __amdgpu_buffer_rsrc_t rec = range_rsrc(a.ws_rec, 2 * a.grid * kRecordFloats * 4);
+  const __amdgpu_buffer_rsrc_t rec = range_rsrc(a.ws_rec, 2 * a.grid * kRecordBytes);
 
   if (f0 < f1) {
     Cursor cc = locate_tile(prefix, B, f0);
@@ -602,7 +708,8 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
       load_queries(a, cc.b, h0, col, kg, qf);
       RowState st;
       st.overflow = false;
-      for (; f < seg1; ++f) {
+      // one tile: wait for it, start the tile two ahead, fold
+      auto tile_step = [&](auto first) {
         if (f + 1 < f1)
           tile_barrier<true>();
         else
@@ -613,11 +720,14 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
         }
         const int valid = min(kTileTokens, L - (cc.j + f - seg0) * kTileTokens);
         const lds_char* tile = stages + ((f - f0) % kStages) * kStageBytes;
-        if (f == seg0)
-          fold_tile<true>(tile, qf, st, valid, a.scale_log2, col, kg);
-        else
-          fold_tile<false>(tile, qf, st, valid, a.scale_log2, col, kg);
-      }
+        fold_tile<decltype(first)::value>(tile, qf, st, valid, a.scale_log2, col, kg);
+        ++f;
+      };
+      // the first tile is peeled: it consumes the queries, so the
+      // compiler's wait for their loads stays out of the tile loop (where
+      // it would also drain the tile prefetch)
+      tile_step(std::true_type{});
+      while (f < seg1) tile_step(std::false_type{});
       finish_segment(a, cc, st, seg0, seg1, f0, chunk, prefix, rec, bcast, wave, h0, col, kg);
       if (f < f1) {  // the next row with tiles
         int b = cc.b + 1;
