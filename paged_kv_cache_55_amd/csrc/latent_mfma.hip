@@ -80,6 +80,14 @@ constexpr float kOverflowLog2 = 32.f;   // weights up to 2^32 over the reference
 constexpr int kPastRange = 0x7ffffff0;  // buffer offset past any range: the load gives zeros
 constexpr int kRecordBytes = kLatentRecordBytes;
 constexpr int kMergeBatch = 8;          // pieces whose loads a merge round issues together
+#ifndef LATENT_K_AHEAD
+#define LATENT_K_AHEAD 2
+#endif
+#ifndef LATENT_V_AHEAD
+#define LATENT_V_AHEAD 8
+#endif
+constexpr int kKAhead = LATENT_K_AHEAD;  // score steps of LDS reads in flight
+constexpr int kVAhead = LATENT_V_AHEAD;  // value steps of LDS reads in flight
 constexpr int kCoherent = 16;           // buffer cache policy sc1 (device-coherent)
 
 static_assert(kPageTokens % kTileTokens == 0, "tiles never straddle a page");
@@ -231,25 +239,27 @@ __device__ __forceinline__ void score_tile(const lds_char* tile,
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) sc[tt][ht] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  // one step of fragments in flight: the scheduler may not hoist further
-  // reads, for which the accumulators and the queries leave no registers
+  // kKAhead steps of fragments in flight (LDS latency exceeds a step's
+  // four products); the schedule barriers keep the compiler from hoisting
+  // more, for which the accumulators and the queries leave no registers
   const lds_char* krow = tile + col * kRowBytes + kg * 16;
-  bf16x8_t k0 = *(lds_bf16x8*)krow;
-  bf16x8_t k1 = *(lds_bf16x8*)(krow + 16 * kRowBytes);
+  bf16x8_t k0[kQkSteps], k1[kQkSteps];
+#pragma unroll
+  for (int s = 0; s < kKAhead; ++s) {
+    k0[s] = *(lds_bf16x8*)(krow + s * 64);
+    k1[s] = *(lds_bf16x8*)(krow + 16 * kRowBytes + s * 64);
+  }
 #pragma unroll
   for (int s = 0; s < kQkSteps; ++s) {
-    bf16x8_t n0 = k0, n1 = k1;
-    if (s + 1 < kQkSteps) {
-      n0 = *(lds_bf16x8*)(krow + (s + 1) * 64);
-      n1 = *(lds_bf16x8*)(krow + 16 * kRowBytes + (s + 1) * 64);
+    if (s + kKAhead < kQkSteps) {
+      k0[s + kKAhead] = *(lds_bf16x8*)(krow + (s + kKAhead) * 64);
+      k1[s + kKAhead] = *(lds_bf16x8*)(krow + 16 * kRowBytes + (s + kKAhead) * 64);
     }
-    sc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][s], sc[0][0], 0, 0, 0);
-    sc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][s], sc[0][1], 0, 0, 0);
-    sc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][s], sc[1][0], 0, 0, 0);
-    sc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][s], sc[1][1], 0, 0, 0);
+    sc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[s], qf[0][s], sc[0][0], 0, 0, 0);
+    sc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[s], qf[1][s], sc[0][1], 0, 0, 0);
+    sc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qf[0][s], sc[1][0], 0, 0, 0);
+    sc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qf[1][s], sc[1][1], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    k0 = n0;
-    k1 = n1;
   }
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
@@ -295,23 +305,26 @@ __device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t 
                                            float4_t (&o)[2][kDimTiles], int col, int kg) {
   const float4_t zero = {0.f, 0.f, 0.f, 0.f};
   const lds_char* vrow = tile + (4 * kg + (col >> 2)) * kRowBytes + (col & 3) * 8;
-  short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)vrow);
-  short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + 16 * kRowBytes));
+  // kVAhead steps of fragments in flight: a step is only two products
+  short4_t v0[kDimTiles], v1[kDimTiles];
+#pragma unroll
+  for (int n = 0; n < kVAhead; ++n) {
+    v0[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + n * 32));
+    v1[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + 16 * kRowBytes + n * 32));
+  }
 #pragma unroll
   for (int n = 0; n < kDimTiles; ++n) {
-    short4_t n0 = v0, n1 = v1;
-    if (n + 1 < kDimTiles) {
-      n0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + (n + 1) * 32));
-      n1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4*)(vrow + 16 * kRowBytes + (n + 1) * 32));
+    if (n + kVAhead < kDimTiles) {
+      v0[n + kVAhead] =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + (n + kVAhead) * 32));
+      v1[n + kVAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(vrow + 16 * kRowBytes + (n + kVAhead) * 32));
     }
     const bf16x8_t vf = __builtin_bit_cast(
-        bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        bf16x8_t, __builtin_shufflevector(v0[n], v1[n], 0, 1, 2, 3, 4, 5, 6, 7));
     o[0][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], kFirst ? zero : o[0][n], 0, 0, 0);
     o[1][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], kFirst ? zero : o[1][n], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    v0 = n0;
-    v1 = n1;
   }
 }
 
