@@ -19,9 +19,13 @@ def fact(name):
     return FACTS[name]["value"], FACTS[name]["inputs"]
 
 
+PAGES = ("cs2680 Lecture 10", "inferenceinterviews.com", "llm-serving.xyz", "The inference server",
+         "same page", "same paragraph", "same section")
+
+
 def test_every_fact_has_a_source():
     for f in FACTS.values():
-        assert f["source"] and "PAPER" not in f["source"]
+        assert any(p in f["source"] for p in PAGES), f["name"]
 
 
 def test_bytes_per_token_and_pool():
