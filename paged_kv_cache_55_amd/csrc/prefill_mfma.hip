@@ -17,10 +17,10 @@
 //
 // A wave owns kColTiles column tiles of 16 (64 columns): each K/V tile it
 // loads feeds all of them, and it streams the tiles 0 .. up to the last
-// position any of its columns sees. As in decode, the probabilities enter
-// the value product as the sum of two bf16 numbers (about 2^-17 relative):
-// a single bf16 (2^-9) measured just above the parity bar on some rows,
-// where the output's own bf16 rounding already takes most of it.
+// position any of its columns sees. The probabilities enter the value
+// product as single bf16 numbers: their 2^-9 relative rounding averages out
+// over the weighted sum (the measured 8 x 512 step uses 78% of the parity
+// bar), and a hi/lo pair would double the value product's matrix work.
 //
 // Work items are (sequence, KV head, 64-column block); every workgroup
 // counts the items per sequence into an LDS prefix, and the waves of a
@@ -44,7 +44,7 @@ constexpr int kWaves = 4;
 constexpr int kColTiles = 4;
 constexpr int kCols = kColTiles * kTile;  // columns per work item
 constexpr float kLazyLog2 = 8.f;          // reference-max slack, log2 units
-constexpr bool kSplitP = true;            // probabilities as bf16 hi + lo
+constexpr bool kSplitP = false;           // true: probabilities as bf16 hi + lo
 
 template <int D>
 struct ColState {
