@@ -56,7 +56,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
     "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
-    "latent": ["latent_mfma.hip", "mfma_tile.h", "device_common.h", "worklist.h", "launch.h"],
+    "latent": ["latent_mfma.hip", "lds_stream.h", "mfma_tile.h", "device_common.h", "worklist.h",
+               "launch.h"],
 }
 
 

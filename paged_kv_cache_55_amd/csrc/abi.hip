@@ -410,9 +410,13 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.group = dims->num_q_heads / dims->num_kv_heads;
   a.max_blocks = dims->max_blocks_per_seq;
   a.block_shift = block_shift(dims->block_size);
+  size_t lds = 0;
+  hipError_t e = lds_per_workgroup(&lds);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  const size_t smem = prefill_mfma_smem(dims->num_seqs, dims->head_dim);
+  if (smem > lds) return PA_ERR_UNSUPPORTED;
   int resident = 0;
-  hipError_t e = resident_workgroups(prefill_mfma_fn(dims->head_dim),
-                                     (size_t)(dims->num_seqs + 1) * sizeof(int), &resident);
+  e = resident_workgroups(prefill_mfma_fn(dims->head_dim), smem, &resident);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
   const int grid = resident < kMaxPrefillGrid ? resident : kMaxPrefillGrid;
   e = launch_prefill_mfma(a, dims->head_dim, grid, (hipStream_t)stream);

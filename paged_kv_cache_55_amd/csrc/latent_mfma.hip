@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "launch.h"
+#include "lds_stream.h"
 #include "mfma_tile.h"
 #include "worklist.h"
 
@@ -51,7 +52,10 @@ namespace {
 
 using namespace mfma;
 
-typedef __attribute__((address_space(3))) char lds_char;
+using lds_stream::lds_char;
+using lds_stream::kPastRange;
+using lds_stream::load_to_lds;
+using lds_stream::raw_rsrc;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -77,7 +81,6 @@ constexpr int kFewestLoads = kTileLoads / kWaves;               // 9
 constexpr int kQkSteps = kLatent / 32;  // 18 score steps
 constexpr int kDimTiles = kValue / 16;  // 32 output dim tiles
 constexpr float kOverflowLog2 = 32.f;   // weights up to 2^32 over the reference
-constexpr int kPastRange = 0x7ffffff0;  // buffer offset past any range: the load gives zeros
 constexpr int kRecordBytes = kLatentRecordBytes;
 constexpr int kMergeBatch = 8;          // pieces whose loads a merge round issues together
 #ifndef LATENT_K_AHEAD
@@ -118,34 +121,6 @@ __device__ __forceinline__ void next_tile(Cursor& c, const int* prefix) {
   c.n = __builtin_amdgcn_readfirstlane(prefix[b + 1] - prefix[b]);
 }
 
-// A raw buffer descriptor of `bytes` bytes at `base` (32-bit data format,
-// unswizzled; reads past the range give zero).
-__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
-  const uint64_t p = (uint64_t)base;
-  return (u32x4_t){(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
-}
-
-// 16 bytes per lane from the buffer at byte offset `off` into LDS at
-// `dst` + 16 * lane (buffer_load_dwordx4 with the LDS destination in M0,
-// streaming cache policy). Written as assembly so that the compiler does
-// not track these LDS writes: it cannot tell the tile stages apart and
-// would otherwise make every later LDS read wait for all of them, the
-// prefetch included. Completion is awaited explicitly (tile_barrier). M0
-// belongs to the compiler, so the sequence restores it.
-__device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(off), "s"(rsrc)
-      : "memory");
-}
-
 // Issues this wave's share of the loads of tile c into `stage`: wave load k
 // (k = wave, wave + 4, ...) fills LDS bytes 1024 k .. 1024 k + 1023, lane l
 // the 16 bytes at 1024 k + 16 l, i.e. chunk ch of token t with
@@ -175,27 +150,18 @@ __device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, 
   }
 }
 
-// Waits until this wave's loads of the current tile have landed in LDS
-// (vector memory operations complete in order, so at most kFewestLoads
-// younger ones, those of the next tile, may remain), then for every wave of
-// the workgroup to get here: the tile is complete, and every wave is done
-// with the tile before it, whose stage the next loads will overwrite.
+// Waits until this wave's loads of the current tile have landed in LDS (at
+// most kFewestLoads younger ones, those of the next tile, may remain; none
+// when no tile follows), then for every wave of the workgroup.
 template <bool kNextInFlight>
 __device__ __forceinline__ void tile_barrier() {
   if (kNextInFlight)
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kFewestLoads) : "memory");
+    lds_stream::tile_barrier<kFewestLoads>();
   else
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+    lds_stream::tile_barrier<0>();
 }
 
-// A workgroup barrier for LDS traffic only; outstanding loads stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+using lds_stream::lds_barrier;
 
 // ---- one wave's 32 heads of one row -----------------------------------------
 //

@@ -48,8 +48,10 @@ inline int balanced_stage_slots(int num_seqs, int group, int head_dim, size_t ld
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s);
 
 // Chunked-prefill attention (bf16, blocks of 16 or more tokens): persistent
-// grid of `grid` workgroups, dynamic LDS of (num_seqs + 1) ints.
+// grid of `grid` workgroups; dynamic LDS: the tile stages and (num_seqs + 1)
+// ints.
 const void* prefill_mfma_fn(int head_dim);
+size_t prefill_mfma_smem(int num_seqs, int head_dim);  // dynamic LDS bytes of a launch
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int head_dim, int grid, hipStream_t s);
 
 // Latent (MLA-style) decode, fixed shape: 128 heads over one 576-element

@@ -1,0 +1,66 @@
+// Streaming tiles from HBM into LDS with buffer loads that carry an LDS
+// destination (gfx950 buffer_load_dwordx4 ... lds): lane l of a wave load
+// writes 16 bytes at M0 + 16 l, from any byte offset of a buffer descriptor
+// (offsets past the descriptor's range load zeros). Shared by the kernels
+// whose workgroups share each tile among their waves.
+#pragma once
+
+#include "device_common.h"
+
+namespace pagedkv {
+namespace lds_stream {
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPastRange = 0x7ffffff0;  // buffer offset past any range: the load gives zeros
+
+// A raw buffer descriptor of `bytes` bytes at `base` (32-bit data format,
+// unswizzled; reads past the range give zero).
+__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)base;
+  return (u32x4_t){(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer at byte offset `off` into LDS at
+// `dst` + 16 * lane (buffer_load_dwordx4 with the LDS destination in M0,
+// streaming cache policy). Written as assembly so that the compiler does
+// not track these LDS writes: it cannot tell the stages apart and would
+// otherwise make every later LDS read wait for all of them, the prefetch
+// included. Completion is awaited explicitly (tile_barrier). M0 belongs to
+// the compiler, so the sequence restores it.
+__device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(off), "s"(rsrc)
+      : "memory");
+}
+
+// Waits until at most kYounger of this wave's vector memory operations are
+// outstanding (they complete in order: everything older has landed), then
+// for every wave of the workgroup to get here. With kYounger no larger than
+// the loads each wave issued after a tile's, the tile is complete in LDS
+// for every wave, and every wave is done with the stages read before.
+template <int kYounger>
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kYounger) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A workgroup barrier for LDS traffic only; outstanding loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace lds_stream
+}  // namespace pagedkv

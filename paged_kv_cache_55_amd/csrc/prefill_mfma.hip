@@ -9,28 +9,34 @@
 // every query token form the columns c = i G + g of the decode kernel's two
 // products:
 //   scores  S^T[t][c] = K[t] . q[c]             v_mfma_f32_16x16x32_bf16
-//   values  O^T[d][c] += V^T[d][t] P^T[t][c]   v_mfma_f32_16x16x16_bf16
+//   values  O^T[d][c] += V^T[d][t] P^T[t][c]   v_mfma_f32_16x16x32_bf16
 // with the causal test t <= p(c) applied to the scores by select. The
 // accumulator layout gives every lane one column and 4 tokens, so the
 // causal test and the online softmax are lane-local, with two cross-lane
 // steps per tile for the column's max and sum.
 //
-// A wave owns kColTiles column tiles of 16 (64 columns): each K/V tile it
-// loads feeds all of them, and it streams the tiles 0 .. up to the last
-// position any of its columns sees. The probabilities enter the value
-// product as single bf16 numbers: their 2^-9 relative rounding averages out
-// over the weighted sum (the measured 8 x 512 step uses 78% of the parity
-// bar), and a hi/lo pair would double the value product's matrix work.
+// A work item is 256 columns of one (sequence, KV head): its workgroup's
+// four waves own 64 columns each, and all of them read the same K/V tiles.
+// The 16-token tiles are staged once per workgroup in LDS by buffer loads
+// with an LDS destination (no staging registers), eight stages deep, six
+// tiles ahead of the two being folded, with K token rows padded to 2 D + 16
+// bytes and V^T dim rows to 48 bytes so that the operand reads run without
+// bank conflicts. Tiles are folded in pairs: the value product's k = 32 is
+// the pair's 32 tokens (4 of each tile per lane, the same k slots as the
+// two score accumulators give the probabilities). The probabilities enter
+// it as single bf16 numbers: their 2^-9 relative rounding averages out over
+// the weighted sum, and a hi/lo pair would double the value product's
+// matrix work. A lazy reference max keeps the rescale of the accumulators
+// off the common path.
 //
-// Work items are (sequence, KV head, 64-column block); every workgroup
-// counts the items per sequence into an LDS prefix, and the waves of a
-// persistent grid take items in serpentine order (w, 2W - 1 - w, 2W + w,
-// ...), which pairs long items with short ones when their cost grows with
-// the item index. The four waves of a workgroup get neighbouring column
-// blocks of one (sequence, KV head) and read the same K/V tiles at about the
-// same time, so the tiles are loaded with the default cache policy (they
-// are shared through the caches, unlike decode's read-once tiles).
+// Every workgroup counts the items per sequence into an LDS prefix, and the
+// workgroups of a persistent grid take items in serpentine order (w,
+// 2W - 1 - w, 2W + w, ...), which pairs long items with short ones when
+// their cost grows with the item index.
+#include <type_traits>
+
 #include "launch.h"
+#include "lds_stream.h"
 #include "mfma_tile.h"
 #include "worklist.h"
 
@@ -39,117 +45,204 @@ namespace pagedkv {
 namespace {
 
 using namespace mfma;
+using lds_stream::kPastRange;
+using lds_stream::lds_barrier;
+using lds_stream::lds_char;
+using lds_stream::load_to_lds;
+using lds_stream::raw_rsrc;
+
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) const short4_t lds_short4;
 
 constexpr int kWaves = 4;
 constexpr int kColTiles = 4;
-constexpr int kCols = kColTiles * kTile;  // columns per work item
-constexpr float kLazyLog2 = 8.f;          // reference-max slack, log2 units
-constexpr bool kSplitP = false;           // true: probabilities as bf16 hi + lo
+constexpr int kCols = kColTiles * kTile;     // columns per wave
+constexpr int kItemCols = kWaves * kCols;    // columns per work item
+constexpr float kLazyLog2 = 8.f;             // reference-max slack, log2 units
+constexpr int kStages = 8;                   // LDS tile stages
+constexpr int kAhead = 6;                    // tiles in flight beyond the pair being folded
+static_assert(kAhead + 2 == kStages, "a pair's stages are refilled after it is folded");
+
+// LDS stage of one 16-token tile: K rows [16][2 D + 16 bytes], then V^T
+// rows [D][48 bytes], each region whole wave loads of 1 KiB (lane l of
+// load k fills bytes 1024 k + 16 l).
+template <int D>
+struct Stage {
+  static constexpr int kKRow = 2 * D + 16;
+  static constexpr int kKRowChunks = kKRow / 16;
+  static constexpr int kKDataChunks = 2 * D / 16;
+  static constexpr int kKLoads = (kTile * kKRowChunks + 63) / 64;
+  static constexpr int kVRow = 48;
+  static constexpr int kVRowChunks = kVRow / 16;
+  static constexpr int kVLoads = (D * kVRowChunks + 63) / 64;
+  static constexpr int kVBase = kKLoads * 1024;
+  static constexpr int kLoads = kKLoads + kVLoads;
+  static constexpr int kBytes = kLoads * 1024;
+  static constexpr int kFewest = kLoads / kWaves;  // loads of one tile a wave issues, at least
+};
 
 template <int D>
 struct ColState {
   float4_t acc[D / 16];  // O^T[d][c]: dims 16 n + 4 kg + r of this lane's column
-  float m;               // running max (log2 domain) of the column
-  float l;               // this lane's 4-token share of the column's sum
+  float m;               // running reference max (log2 domain) of the column
+  float l;               // this lane's share of the column's sum
 };
 
-// Folds one 16-token tile (tokens tok0 .. tok0 + 15, the first nvalid of
-// them inside the sequence) into the kColTiles column states.
+// Issues this wave's share of the loads of one tile: K rows from `kt`
+// (16 x D, contiguous), V^T rows from `vt` (D x 16, contiguous); an empty
+// tile (bytes = 0) fills the stage with zeros.
 template <int D>
-__device__ __forceinline__ void fold_tile(Tile<D>& t, const bf16x8_t (&qb)[kColTiles][D / 32],
-                                          ColState<D> (&st)[kColTiles],
-                                          const int (&pos)[kColTiles], int tok0, int nvalid,
-                                          float scale_log2, int kg) {
-  constexpr int NQK = D / 32;
-  constexpr int NDT = D / 16;
-  if (nvalid < kTile) {
-    // slots past the sequence may hold anything (NaN included): zero their
-    // V so that p = 0 there contributes nothing
-    const uint32_t m0 = (kg * 4 + 0 < nvalid ? 0x0000ffffu : 0u) |
-                        (kg * 4 + 1 < nvalid ? 0xffff0000u : 0u);
-    const uint32_t m1 = (kg * 4 + 2 < nvalid ? 0x0000ffffu : 0u) |
-                        (kg * 4 + 3 < nvalid ? 0xffff0000u : 0u);
+__device__ __forceinline__ void load_tile(lds_char* stage, const bf16_t* kt, const bf16_t* vt,
+                                          int bytes, int wave, int lane) {
+  using S = Stage<D>;
+  const u32x4_t kr = raw_rsrc(kt, bytes);
+  const u32x4_t vr = raw_rsrc(vt, bytes);
 #pragma unroll
-    for (int n = 0; n < NDT; ++n) {
-      uint2 raw = __builtin_bit_cast(uint2, t.v[n]);
-      raw.x &= m0;
-      raw.y &= m1;
-      t.v[n] = __builtin_bit_cast(short4_t, raw);
+  for (int i = 0; i < (S::kLoads + kWaves - 1) / kWaves; ++i) {
+    const int k = wave + kWaves * i;
+    if (k >= S::kLoads) break;
+    if (k < S::kKLoads) {
+      const int slot = 64 * k + lane;
+      const int t = slot / S::kKRowChunks;
+      const int ch = slot - t * S::kKRowChunks;
+      const int off = t < kTile && ch < S::kKDataChunks ? t * 2 * D + ch * 16 : kPastRange;
+      load_to_lds(kr, stage + 1024 * k, off);
+    } else {
+      const int slot = 64 * (k - S::kKLoads) + lane;
+      const int d = slot / S::kVRowChunks;
+      const int ch = slot - d * S::kVRowChunks;
+      const int off = d < D && ch < 2 ? d * 2 * kTile + ch * 16 : kPastRange;
+      load_to_lds(vr, stage + 1024 * k, off);
     }
   }
+}
+
+// Folds tiles (tok0 .. tok0 + 15) in stage a and (tok0 + 16 .. tok0 + 31) in
+// stage b into the column states. Tokens past the sequence (L) or past a
+// column's position are masked; V^T slots past L may hold anything (NaN
+// included), so the pair holding the sequence's end zeroes them.
+template <int D>
+__device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb,
+                                          const bf16x8_t (&qb)[kColTiles][D / 32],
+                                          ColState<D> (&st)[kColTiles],
+                                          const int (&pos)[kColTiles], int tok0, int L,
+                                          float scale_log2, int row, int kg) {
+  using S = Stage<D>;
+  constexpr int NQK = D / 32;
+  constexpr int NDT = D / 16;
+  // score operands of both tiles: token `row`, elements 32 c + 8 kg .. + 7
+  bf16x8_t ka[NQK], kb[NQK];
+#pragma unroll
+  for (int c = 0; c < NQK; ++c) {
+    ka[c] = *(lds_bf16x8*)(sa + row * S::kKRow + c * 64 + kg * 16);
+    kb[c] = *(lds_bf16x8*)(sb + row * S::kKRow + c * 64 + kg * 16);
+  }
+  // scores of all column tiles first (one stretch of matrix instructions),
+  // then the softmax, then the value product
+  float4_t s0[kColTiles], s1[kColTiles];
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
-    float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
+    s0[ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    s1[ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NQK; ++c)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[c], qb[ct][c], s, 0, 0, 0);
-    float sv[4];
+    for (int c = 0; c < NQK; ++c) {
+      s0[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qb[ct][c], s0[ct], 0, 0, 0);
+      s1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c], qb[ct][c], s1[ct], 0, 0, 0);
+    }
+  }
+  // masked, scaled scores in place; the columns' tile maxima
+  float mcol[kColTiles];
+  bool grow = false;
+#pragma unroll
+  for (int ct = 0; ct < kColTiles; ++ct) {
     float mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = tok0 + kg * 4 + r <= pos[ct] ? s[r] * scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, sv[r]);
+      s0[ct][r] = tok0 + kg * 4 + r <= pos[ct] ? s0[ct][r] * scale_log2 : -INFINITY;
+      s1[ct][r] = tok0 + kTile + kg * 4 + r <= pos[ct] ? s1[ct][r] * scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, fmaxf(s0[ct][r], s1[ct][r]));
     }
-    // lazy reference max: the column keeps its reference m until a score
-    // exceeds it by 2^kLazyLog2 (its first tile always does: m starts at
-    // -inf, and token 0 is seen by every column); p = 2^(s - m) then stays
-    // <= 2^kLazyLog2, and the rescale of O and l runs only when some column
-    // of the wave moves its reference
-    const float mcol = max_over_kg(mloc);
-    const bool grow = mcol > st[ct].m + kLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mcol : st[ct].m;
+    mcol[ct] = max_over_kg(mloc);
+    grow |= mcol[ct] > st[ct].m + kLazyLog2;
+  }
+  // lazy reference max: a column keeps its reference m until a score
+  // exceeds it by 2^kLazyLog2 (its first tile always does: m starts at
+  // -inf, and token 0 is seen by every column); p = 2^(s - m) then stays
+  // <= 2^kLazyLog2, and the rescale of O and l runs only when some column
+  // of the wave moves its reference
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int ct = 0; ct < kColTiles; ++ct) {
+      const float m_new = mcol[ct] > st[ct].m + kLazyLog2 ? mcol[ct] : st[ct].m;
       const float alpha = fast_exp2(st[ct].m - m_new);  // 1 for columns that keep m
       st[ct].m = m_new;
       st[ct].l *= alpha;
 #pragma unroll
       for (int n = 0; n < NDT; ++n) st[ct].acc[n] *= alpha;
     }
+  }
+  bf16x8_t pf[kColTiles];
+#pragma unroll
+  for (int ct = 0; ct < kColTiles; ++ct) {
     float psum = 0.f;
-    uint16_t ph[4], pl[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(sv[r] - st[ct].m);
-      psum += p;
-      ph[r] = bf16_rne(p);
-      pl[r] = bf16_rne(p - __uint_as_float((uint32_t)ph[r] << 16));
+      const float pa = fast_exp2(s0[ct][r] - st[ct].m);
+      const float pb = fast_exp2(s1[ct][r] - st[ct].m);
+      psum += pa + pb;
+      pf[ct][r] = (__bf16)pa;      // k slot 8 kg + r: token 4 kg + r of tile a
+      pf[ct][4 + r] = (__bf16)pb;  // k slot 8 kg + 4 + r: token 4 kg + r of tile b
     }
     st[ct].l += psum;
-    const short4_t bhi = __builtin_bit_cast(
-        short4_t, make_uint2(pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])));
-    const short4_t blo = __builtin_bit_cast(
-        short4_t, make_uint2(pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3])));
+  }
+  // value operand: dim 16 n + row, tokens 4 kg .. + 3 of each tile; slots
+  // past L (only in the pair that holds the sequence's end) are zeroed
+  const int ta = tok0 + 4 * kg, tb = ta + kTile;
+  const uint32_t m0 = (ta + 0 < L ? 0x0000ffffu : 0u) | (ta + 1 < L ? 0xffff0000u : 0u);
+  const uint32_t m1 = (ta + 2 < L ? 0x0000ffffu : 0u) | (ta + 3 < L ? 0xffff0000u : 0u);
+  const uint32_t m2 = (tb + 0 < L ? 0x0000ffffu : 0u) | (tb + 1 < L ? 0xffff0000u : 0u);
+  const uint32_t m3 = (tb + 2 < L ? 0x0000ffffu : 0u) | (tb + 3 < L ? 0xffff0000u : 0u);
 #pragma unroll
-    for (int n = 0; n < NDT; ++n) {
-      float4_t o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[n], bhi, st[ct].acc[n], 0, 0, 0);
-      if (kSplitP) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[n], blo, o, 0, 0, 0);
-      st[ct].acc[n] = o;
-    }
+  for (int n = 0; n < NDT; ++n) {
+    const int voff = S::kVBase + (16 * n + row) * S::kVRow + kg * 8;
+    const uint2 va = __builtin_bit_cast(uint2, *(lds_short4*)(sa + voff));
+    const uint2 vb = __builtin_bit_cast(uint2, *(lds_short4*)(sb + voff));
+    const bf16x8_t vf =
+        __builtin_bit_cast(bf16x8_t, make_uint4(va.x & m0, va.y & m1, vb.x & m2, vb.y & m3));
+#pragma unroll
+    for (int ct = 0; ct < kColTiles; ++ct)
+      st[ct].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ct], st[ct].acc[n], 0, 0, 0);
   }
 }
 
-// One work item: columns cb * 64 .. cb * 64 + 63 of (sequence s, KV head).
+// One work item: columns grp * 256 .. + 255 of (sequence s, KV head); wave
+// w owns columns grp * 256 + 64 w .. + 63.
 template <int D>
-__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int kvh, int cb,
-                                             int row, int kg) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* stages, int s,
+                                             int kvh, int grp, int wave, int lane) {
+  using S = Stage<D>;
   constexpr int NQK = D / 32;
   constexpr int NDT = D / 16;
+  const int row = lane & 15;
+  const int kg = lane >> 4;
   const int G = a.group;
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int r0 = uniform_load(a.query_start, s);
   const int n = uniform_load(a.query_start, s + 1) - r0;
   const int L = uniform_load(a.seq_lens, s);
-  const int p0 = L - n;          // position of query token 0
+  const int p0 = L - n;  // position of query token 0
   const int ncols = n * G;
+  const int c0 = grp * kItemCols + wave * kCols;  // this wave's first column
+  const bool active = c0 < ncols;
 
   // this lane's column in each column tile; padded columns repeat the
-  // block's last real column (computed, never written)
+  // wave's last real column (computed, never written)
   int pos[kColTiles];
   bf16x8_t qb[kColTiles][NQK];
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
-    const int c = min(cb * kCols + ct * kTile + row, ncols - 1);
+    const int c = max(0, min(c0 + ct * kTile + row, ncols - 1));
     const int i = c / G;
     const int g = c - i * G;
     pos[ct] = p0 + i;
@@ -157,8 +250,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int kv
 #pragma unroll
     for (int k = 0; k < NQK; ++k) qb[ct][k] = *(const bf16x8_t*)(qp + k * 32 + kg * 8);
   }
-  const int clast = min(cb * kCols + kCols - 1, ncols - 1);
-  const int ntiles = (p0 + clast / G) / kTile + 1;
+  // tiles this wave folds, and the item's (the last active wave's)
+  const int wave_tiles = (p0 + min(c0 + kCols - 1, ncols - 1) / G) / kTile + 1;
+  const int item_tiles = (p0 + min(grp * kItemCols + kItemCols - 1, ncols - 1) / G) / kTile + 1;
+  const int pairs = (item_tiles + 1) / 2;
+  const int padded = 2 * pairs;
 
   ColState<D> st[kColTiles];
 #pragma unroll
@@ -168,53 +264,49 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int kv
     st[ct].m = -INFINITY;
     st[ct].l = 0.f;
   }
+  // the queries are in registers before any tile load is issued: the
+  // compiler's wait for them stays out of the tile loop
+  __builtin_amdgcn_s_waitcnt(0);
 
-  const bf16_t* kbase = (const bf16_t*)a.k_pool;
-  const bf16_t* vbase = (const bf16_t*)a.v_pool;
+  const bf16_t* kpool = (const bf16_t*)a.k_pool;
+  const bf16_t* vpool = (const bf16_t*)a.v_pool;
   const int sub_shift = a.block_shift - 4;
   const int sub_mask = (1 << sub_shift) - 1;
   const size_t trow = (size_t)s * a.max_blocks;
-  const LaneOffsets<D> lo(row, kg);
-  auto table = [&](int j) { return uniform_load(a.block_tables, trow + (j >> sub_shift)); };
-  auto load = [&](Tile<D>& dst, int j, int32_t phys) {
+  auto issue = [&](int j) {  // tile j of the stream into its stage
+    lds_char* stage = stages + (j % kStages) * S::kBytes;
+    if (j >= item_tiles) {  // padding of the last pair: zeros
+      load_tile<D>(stage, kpool, vpool, 0, wave, lane);
+      return;
+    }
+    const int32_t phys = uniform_load(a.block_tables, trow + (j >> sub_shift));
     const size_t base =
         ((((size_t)phys * Hkv + kvh) << a.block_shift) + (size_t)(j & sub_mask) * kTile) * D;
-    load_tile<D, 0>(dst, kbase + base, vbase + base, lo);
+    load_tile<D>(stage, kpool + base, vpool + base, kTile * D * 2, wave, lane);
   };
-
-  // two register tiles alternate; the table entry of tile j + 2 is read
-  // while tile j is folded in, so no tile address waits for its table read
-  Tile<D> ta, tb;
-  int32_t ph_cur = table(0);
-  int32_t ph_nx = table(ntiles > 1 ? 1 : 0);
-  load(ta, 0, ph_cur);
-  int j = 0;
-  auto prefetch = [&](Tile<D>& dst, bool more) {
-    load(dst, more ? j + 1 : j, more ? ph_nx : ph_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    const int32_t ph_nn = table(j + 2 < ntiles ? j + 2 : (more ? j + 1 : j));
-    if (more) {
-      ph_cur = ph_nx;
-      ph_nx = ph_nn;
-    }
-  };
-  while (true) {
-    bool more = j + 1 < ntiles;
-    prefetch(tb, more);
-    fold_tile<D>(ta, qb, st, pos, j * kTile, min(kTile, L - j * kTile), a.scale_log2, kg);
-    if (!more) break;
-    ++j;
-    more = j + 1 < ntiles;
-    prefetch(ta, more);
-    fold_tile<D>(tb, qb, st, pos, j * kTile, min(kTile, L - j * kTile), a.scale_log2, kg);
-    if (!more) break;
-    ++j;
+  for (int j = 0; j < kAhead && j < padded; ++j) issue(j);
+  for (int p = 0; p < pairs; ++p) {
+    // tiles 2p, 2p + 1 landed: the kAhead - 2 tiles issued after them may
+    // still be in flight while whole; at the stream's end nothing may
+    if (2 * p + kAhead <= padded)
+      lds_stream::tile_barrier<S::kFewest * (kAhead - 2)>();
+    else
+      lds_stream::tile_barrier<0>();
+    // refill the stages of the pair folded last (every wave is past it)
+    if (2 * p + kAhead < padded) issue(2 * p + kAhead);
+    if (2 * p + kAhead + 1 < padded) issue(2 * p + kAhead + 1);
+    if (active && 2 * p < wave_tiles)
+      fold_pair<D>(stages + ((2 * p) % kStages) * S::kBytes,
+                   stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos, 2 * p * kTile, L,
+                   a.scale_log2, row, kg);
   }
+  lds_barrier();  // every wave is done with the stages before the next item
 
+  if (!active) return;
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
     const float l = sum_over_kg(st[ct].l);  // every lane takes part
-    const int c = cb * kCols + ct * kTile + row;
+    const int c = c0 + ct * kTile + row;
     if (c >= ncols) continue;
     const int i = c / G;
     const int g = c - i * G;
@@ -232,35 +324,34 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int kv
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
-  extern __shared__ int prefix[];  // [S + 1]: work items before each sequence
+  // dynamic LDS: kStages tile stages, then the work-list prefix [S + 1]
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int scan_scratch[kWaves];
+  lds_char* stages = (lds_char*)smem;
+  int* prefix = (int*)(smem + kStages * Stage<D>::kBytes);
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   for (int i = threadIdx.x; i < S; i += blockDim.x) {
     const int n = a.query_start[i + 1] - a.query_start[i];
-    prefix[i] = n > 0 ? (n * a.group + kCols - 1) / kCols * Hkv : 0;
+    prefix[i] = n > 0 ? (n * a.group + kItemCols - 1) / kItemCols * Hkv : 0;
   }
   __syncthreads();
   scan_counts_in_place(S, prefix, scan_scratch);
 
   const int total = prefix[S];
   const int lane = threadIdx.x & 63;
-  const int row = lane & 15;
-  const int kg = lane >> 4;
-  const int W = gridDim.x * kWaves;
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = gridDim.x;
+  const int wg = blockIdx.x;
   for (int k = 0; k * W < total; ++k) {
-    const int item = (k & 1) ? (k + 1) * W - 1 - w : k * W + w;
+    const int item = (k & 1) ? (k + 1) * W - 1 - wg : k * W + wg;
     if (item >= total) continue;
-    // items of one sequence: KV head major, column block minor, so the waves
-    // of a workgroup take neighbouring column blocks of one (sequence, KV
-    // head) and stream the same K/V tiles at the same time
     const int s = __builtin_amdgcn_readfirstlane(find_sequence(prefix, S, item));
     const int r = item - prefix[s];
     const int n = uniform_load(a.query_start, s + 1) - uniform_load(a.query_start, s);
-    const int ncb = (n * a.group + kCols - 1) / kCols;
-    const int kvh = r / ncb;
-    prefill_item<D>(a, s, kvh, r - kvh * ncb, row, kg);
+    const int ngrp = (n * a.group + kItemCols - 1) / kItemCols;
+    const int kvh = r / ngrp;
+    prefill_item<D>(a, stages, s, kvh, r - kvh * ngrp, wave, lane);
   }
 }
 
@@ -271,11 +362,16 @@ const void* prefill_mfma_fn(int head_dim) {
                         : (const void*)&prefill_mfma_kernel<128>;
 }
 
+size_t prefill_mfma_smem(int num_seqs, int head_dim) {
+  const size_t stage = head_dim == 64 ? Stage<64>::kBytes : Stage<128>::kBytes;
+  return kStages * stage + (size_t)(num_seqs + 1) * sizeof(int);
+}
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int head_dim, int grid, hipStream_t s) {
   PrefillArgs arg = a;
   void* args[] = {&arg};
   return hipLaunchKernel(prefill_mfma_fn(head_dim), dim3(grid), dim3(256), args,
-                         (size_t)(a.num_seqs + 1) * sizeof(int), s);
+                         prefill_mfma_smem(a.num_seqs, head_dim), s);
 }
 
 }  // namespace pagedkv

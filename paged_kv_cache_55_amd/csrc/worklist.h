@@ -18,9 +18,12 @@ namespace pagedkv {
 
 constexpr int kMaxSeqs = 4096;  // sequences per call (prefix lives in LDS)
 
-// Exclusive prefix over a block of 256 threads; `v` is this thread's value,
-// `scratch` holds 4 ints. Returns the exclusive prefix; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int* total) {
+// Exclusive prefix over a block of kThreads threads (a multiple of 64);
+// `v` is this thread's value, `scratch` holds kThreads / 64 ints. Returns
+// the exclusive prefix; *total gets the sum.
+template <int kThreads = 256>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  constexpr int kW = kThreads / 64;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   int inc = v;
@@ -33,7 +36,7 @@ __device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int
   __syncthreads();
   int base = 0, sum = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kW; ++i) {
     const int s = scratch[i];
     base += i < w ? s : 0;
     sum += s;
@@ -44,23 +47,25 @@ __device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int
 }
 
 // prefix[0..B] <- exclusive prefix of the counts already in prefix[0..B-1].
-// Needs blockDim.x == 256 and B <= kMaxSeqs; each thread scans a contiguous
-// chunk. Ends with a barrier.
+// Needs blockDim.x == kThreads and B <= kMaxSeqs; each thread scans a
+// contiguous chunk. Ends with a barrier.
+template <int kThreads = 256>
 __device__ __forceinline__ void scan_counts_in_place(int B, int* prefix, int* scratch) {
-  const int chunk = (B + 255) / 256;  // <= 16
+  constexpr int kMaxChunk = kMaxSeqs / kThreads;
+  const int chunk = (B + kThreads - 1) / kThreads;  // <= kMaxChunk
   const int first = threadIdx.x * chunk;
-  int counts[kMaxSeqs / 256];
+  int counts[kMaxChunk];
   int local = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxSeqs / 256; ++i) {
+  for (int i = 0; i < kMaxChunk; ++i) {
     const int c = (i < chunk && first + i < B) ? prefix[first + i] : 0;
     counts[i] = c;
     local += c;
   }
   int total;
-  int run = block_exclusive_scan_256(local, scratch, &total);
+  int run = block_exclusive_scan<kThreads>(local, scratch, &total);
 #pragma unroll
-  for (int i = 0; i < kMaxSeqs / 256; ++i) {
+  for (int i = 0; i < kMaxChunk; ++i) {
     if (i < chunk && first + i < B) {
       prefix[first + i] = run;
       run += counts[i];
