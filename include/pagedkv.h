@@ -163,7 +163,8 @@ pa_status pa_decode_append(const void* q, const void* k_new, const void* v_new,
  * decode competing for the device]. A sequence with n_s = 1 is a decode
  * row, n_s = 0 a row with nothing to do. Matrix-core kernel: bf16, D = 64
  * or 128, block_size >= 16 (PA_ERR_UNSUPPORTED otherwise); no workspace.
- * The caller guarantees 0 = query_start[0] <= ... <= query_start[num_seqs]
+ * scale must be finite and positive (PA_ERR_INVALID_ARG otherwise). The
+ * caller guarantees 0 = query_start[0] <= ... <= query_start[num_seqs]
  * = num_query_tokens and n_s <= seq_lens[s]; other values give undefined
  * results. out[r] is written for every query row r; bf16 rounding is to
  * nearest even. dims->partition_tokens and dims->kernel are ignored. */

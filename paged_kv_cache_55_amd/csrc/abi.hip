@@ -114,17 +114,18 @@ pa_status plan_decode(const pa_dims* d, Plan* p) {
   return PA_OK;
 }
 
-// Workgroups of `fn` (256 threads, `smem` dynamic LDS bytes) the current
-// device holds at once: CU count x occupancy. Cached per (device, kernel,
-// LDS size rounded up to 1 KiB); the only state the library keeps.
-hipError_t resident_workgroups(const void* fn, size_t smem, int* out) {
+// Workgroups of `fn` (`threads` per workgroup, `smem` dynamic LDS bytes)
+// the current device holds at once: CU count x occupancy. Cached per
+// (device, kernel, LDS size rounded up to 1 KiB, threads); the only state
+// the library keeps.
+hipError_t resident_workgroups(const void* fn, size_t smem, int* out, int threads = 256) {
   static std::mutex mu;
-  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  static std::map<std::tuple<int, const void*, size_t, int>, int> cache;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   smem = (smem + 1023) / 1024 * 1024;
-  const auto key = std::make_tuple(dev, fn, smem);
+  const auto key = std::make_tuple(dev, fn, smem, threads);
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) {
@@ -134,7 +135,7 @@ hipError_t resident_workgroups(const void* fn, size_t smem, int* out) {
   int ncu = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, smem);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, smem);
   if (e != hipSuccess) return e;
   *out = cache[key] = (ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
   return hipSuccess;
@@ -393,7 +394,8 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   if (num_query_tokens == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start || !out)
     return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  // positive: the kernel takes each column's max before scaling
+  if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_INVALID_ARG;
 
   PrefillArgs a;
   a.q = q;
@@ -416,7 +418,7 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   const size_t smem = prefill_mfma_smem(dims->num_seqs, dims->head_dim);
   if (smem > lds) return PA_ERR_UNSUPPORTED;
   int resident = 0;
-  e = resident_workgroups(prefill_mfma_fn(dims->head_dim), smem, &resident);
+  e = resident_workgroups(prefill_mfma_fn(dims->head_dim), smem, &resident, kPrefillThreads);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
   const int grid = resident < kMaxPrefillGrid ? resident : kMaxPrefillGrid;
   e = launch_prefill_mfma(a, dims->head_dim, grid, (hipStream_t)stream);

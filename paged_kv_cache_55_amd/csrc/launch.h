@@ -50,6 +50,7 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
 // Chunked-prefill attention (bf16, blocks of 16 or more tokens): persistent
 // grid of `grid` workgroups; dynamic LDS: the tile stages and (num_seqs + 1)
 // ints.
+constexpr int kPrefillThreads = 512;  // workgroup size of the prefill kernel
 const void* prefill_mfma_fn(int head_dim);
 size_t prefill_mfma_smem(int num_seqs, int head_dim);  // dynamic LDS bytes of a launch
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int head_dim, int grid, hipStream_t s);

@@ -44,15 +44,26 @@ __device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off
 }
 
 // Waits until at most kYounger of this wave's vector memory operations are
-// outstanding (they complete in order: everything older has landed), then
-// for every wave of the workgroup to get here. With kYounger no larger than
-// the loads each wave issued after a tile's, the tile is complete in LDS
-// for every wave, and every wave is done with the stages read before.
+// outstanding (they complete in order: everything older has landed), and
+// for this wave's LDS operations.
 template <int kYounger>
-__device__ __forceinline__ void tile_barrier() {
+__device__ __forceinline__ void wait_loads() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kYounger) : "memory");
+}
+
+// Every wave of the workgroup gets here; no memory operation is awaited.
+__device__ __forceinline__ void workgroup_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// wait_loads<kYounger>, then a workgroup barrier. With kYounger no larger
+// than the loads each wave issued after a tile's, the tile is complete in
+// LDS for every wave, and every wave is done with the stages read before.
+template <int kYounger>
+__device__ __forceinline__ void tile_barrier() {
+  wait_loads<kYounger>();
+  workgroup_barrier();
 }
 
 // A workgroup barrier for LDS traffic only; outstanding loads stay in flight.

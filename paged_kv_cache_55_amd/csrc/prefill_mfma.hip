@@ -16,18 +16,21 @@
 // steps per tile for the column's max and sum.
 //
 // A work item is 256 columns of one (sequence, KV head): its workgroup's
-// four waves own 64 columns each, and all of them read the same K/V tiles.
-// The 16-token tiles are staged once per workgroup in LDS by buffer loads
-// with an LDS destination (no staging registers), eight stages deep, six
-// tiles ahead of the two being folded, with K token rows padded to 2 D + 16
-// bytes and V^T dim rows to 48 bytes so that the operand reads run without
-// bank conflicts. Tiles are folded in pairs: the value product's k = 32 is
-// the pair's 32 tokens (4 of each tile per lane, the same k slots as the
-// two score accumulators give the probabilities). The probabilities enter
-// it as single bf16 numbers: their 2^-9 relative rounding averages out over
-// the weighted sum, and a hi/lo pair would double the value product's
-// matrix work. A lazy reference max keeps the rescale of the accumulators
-// off the common path.
+// eight waves (two per SIMD, so that one wave's softmax overlaps the other's
+// matrix work) own 32 columns each, and all of them read the same K/V
+// tiles. The 16-token tiles are staged once per workgroup in LDS by buffer
+// loads with an LDS destination (no staging registers), eight stages deep,
+// six tiles ahead of the two being folded, with K token rows padded to
+// 2 D + 16 bytes and V^T dim rows to 48 bytes so that the operand reads run
+// without bank conflicts. Tiles are folded in pairs: the value product's
+// k = 32 is the pair's 32 tokens (4 of each tile per lane, the same k slots
+// as the two score accumulators give the probabilities). The probabilities
+// enter it as single bf16 numbers: their 2^-9 relative rounding averages
+// out over the weighted sum, and a hi/lo pair would double the value
+// product's matrix work. A lazy reference max keeps the rescale of the
+// accumulators off the common path, where each score is only compared with
+// its column's threshold. Pairs wholly at or before a wave's first query
+// position, all but the last one or two, skip the causal and length masks.
 //
 // Every workgroup counts the items per sequence into an LDS prefix, and the
 // workgroups of a persistent grid take items in serpentine order (w,
@@ -54,8 +57,8 @@ using lds_stream::raw_rsrc;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 typedef __attribute__((address_space(3))) const short4_t lds_short4;
 
-constexpr int kWaves = 4;
-constexpr int kColTiles = 4;
+constexpr int kWaves = kPrefillThreads / 64;
+constexpr int kColTiles = 2;
 constexpr int kCols = kColTiles * kTile;     // columns per wave
 constexpr int kItemCols = kWaves * kCols;    // columns per work item
 constexpr float kLazyLog2 = 8.f;             // reference-max slack, log2 units
@@ -79,12 +82,14 @@ struct Stage {
   static constexpr int kLoads = kKLoads + kVLoads;
   static constexpr int kBytes = kLoads * 1024;
   static constexpr int kFewest = kLoads / kWaves;  // loads of one tile a wave issues, at least
+  static constexpr int kMore = kLoads % kWaves;    // waves below this issue one more
 };
 
 template <int D>
 struct ColState {
   float4_t acc[D / 16];  // O^T[d][c]: dims 16 n + 4 kg + r of this lane's column
   float m;               // running reference max (log2 domain) of the column
+  float th;              // (m + kLazyLog2) / scale_log2: the raw score that moves m
   float l;               // this lane's share of the column's sum
 };
 
@@ -118,15 +123,16 @@ __device__ __forceinline__ void load_tile(lds_char* stage, const bf16_t* kt, con
 }
 
 // Folds tiles (tok0 .. tok0 + 15) in stage a and (tok0 + 16 .. tok0 + 31) in
-// stage b into the column states. Tokens past the sequence (L) or past a
-// column's position are masked; V^T slots past L may hold anything (NaN
-// included), so the pair holding the sequence's end zeroes them.
-template <int D>
+// stage b into the column states. kMasked: tokens past the sequence (L) or
+// past a column's position are masked, and V^T slots past L, which may hold
+// anything (NaN included), are zeroed; a pair wholly at or before every
+// column's position (hence before L) needs neither.
+template <int D, bool kMasked>
 __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb,
                                           const bf16x8_t (&qb)[kColTiles][D / 32],
                                           ColState<D> (&st)[kColTiles],
                                           const int (&pos)[kColTiles], int tok0, int L,
-                                          float scale_log2, int row, int kg) {
+                                          float scale_log2, float inv_scale, int row, int kg) {
   using S = Stage<D>;
   constexpr int NQK = D / 32;
   constexpr int NDT = D / 16;
@@ -150,32 +156,40 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
       s1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c], qb[ct][c], s1[ct], 0, 0, 0);
     }
   }
-  // masked, scaled scores in place; the columns' tile maxima
-  float mcol[kColTiles];
-  bool grow = false;
+  // masked scores in place
+  if (kMasked) {
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) {
-    float mloc = -INFINITY;
+    for (int ct = 0; ct < kColTiles; ++ct) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s0[ct][r] = tok0 + kg * 4 + r <= pos[ct] ? s0[ct][r] * scale_log2 : -INFINITY;
-      s1[ct][r] = tok0 + kTile + kg * 4 + r <= pos[ct] ? s1[ct][r] * scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, fmaxf(s0[ct][r], s1[ct][r]));
+      for (int r = 0; r < 4; ++r) {
+        s0[ct][r] = tok0 + kg * 4 + r <= pos[ct] ? s0[ct][r] : -INFINITY;
+        s1[ct][r] = tok0 + kTile + kg * 4 + r <= pos[ct] ? s1[ct][r] : -INFINITY;
+      }
     }
-    mcol[ct] = max_over_kg(mloc);
-    grow |= mcol[ct] > st[ct].m + kLazyLog2;
   }
   // lazy reference max: a column keeps its reference m until a score
   // exceeds it by 2^kLazyLog2 (its first tile always does: m starts at
   // -inf, and token 0 is seen by every column); p = 2^(s - m) then stays
-  // <= 2^kLazyLog2, and the rescale of O and l runs only when some column
-  // of the wave moves its reference
+  // <= 2^kLazyLog2 (up to the rounding of th). The common path only
+  // compares raw scores with th; the columns' maxima and the rescale of O
+  // and l run only when a score of the wave passes its column's th.
+  bool grow = false;
+#pragma unroll
+  for (int ct = 0; ct < kColTiles; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) grow |= (s0[ct][r] > st[ct].th) | (s1[ct][r] > st[ct].th);
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
     for (int ct = 0; ct < kColTiles; ++ct) {
-      const float m_new = mcol[ct] > st[ct].m + kLazyLog2 ? mcol[ct] : st[ct].m;
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, fmaxf(s0[ct][r], s1[ct][r]));
+      // the scale is positive, so it commutes with the max
+      const float mcol = max_over_kg(mloc) * scale_log2;
+      const float m_new = mcol > st[ct].m + kLazyLog2 ? mcol : st[ct].m;
       const float alpha = fast_exp2(st[ct].m - m_new);  // 1 for columns that keep m
       st[ct].m = m_new;
+      st[ct].th = (m_new + kLazyLog2) * inv_scale;
       st[ct].l *= alpha;
 #pragma unroll
       for (int n = 0; n < NDT; ++n) st[ct].acc[n] *= alpha;
@@ -184,19 +198,21 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
   bf16x8_t pf[kColTiles];
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pa = fast_exp2(s0[ct][r] - st[ct].m);
-      const float pb = fast_exp2(s1[ct][r] - st[ct].m);
-      psum += pa + pb;
+      const float pa = fast_exp2(fmaf(s0[ct][r], scale_log2, -st[ct].m));
+      const float pb = fast_exp2(fmaf(s1[ct][r], scale_log2, -st[ct].m));
+      psum = r == 0 ? pa + pb : psum + (pa + pb);
       pf[ct][r] = (__bf16)pa;      // k slot 8 kg + r: token 4 kg + r of tile a
       pf[ct][4 + r] = (__bf16)pb;  // k slot 8 kg + 4 + r: token 4 kg + r of tile b
     }
     st[ct].l += psum;
   }
+  // the scheduler keeps the probabilities apart from the accumulators
+  __builtin_amdgcn_sched_barrier(0);
   // value operand: dim 16 n + row, tokens 4 kg .. + 3 of each tile; slots
-  // past L (only in the pair that holds the sequence's end) are zeroed
+  // past L are zeroed in a masked pair
   const int ta = tok0 + 4 * kg, tb = ta + kTile;
   const uint32_t m0 = (ta + 0 < L ? 0x0000ffffu : 0u) | (ta + 1 < L ? 0xffff0000u : 0u);
   const uint32_t m1 = (ta + 2 < L ? 0x0000ffffu : 0u) | (ta + 3 < L ? 0xffff0000u : 0u);
@@ -205,10 +221,13 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
 #pragma unroll
   for (int n = 0; n < NDT; ++n) {
     const int voff = S::kVBase + (16 * n + row) * S::kVRow + kg * 8;
-    const uint2 va = __builtin_bit_cast(uint2, *(lds_short4*)(sa + voff));
-    const uint2 vb = __builtin_bit_cast(uint2, *(lds_short4*)(sb + voff));
-    const bf16x8_t vf =
-        __builtin_bit_cast(bf16x8_t, make_uint4(va.x & m0, va.y & m1, vb.x & m2, vb.y & m3));
+    uint2 va = __builtin_bit_cast(uint2, *(lds_short4*)(sa + voff));
+    uint2 vb = __builtin_bit_cast(uint2, *(lds_short4*)(sb + voff));
+    if (kMasked) {
+      va = make_uint2(va.x & m0, va.y & m1);
+      vb = make_uint2(vb.x & m2, vb.y & m3);
+    }
+    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
 #pragma unroll
     for (int ct = 0; ct < kColTiles; ++ct)
       st[ct].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ct], st[ct].acc[n], 0, 0, 0);
@@ -235,6 +254,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   const int ncols = n * G;
   const int c0 = grp * kItemCols + wave * kCols;  // this wave's first column
   const bool active = c0 < ncols;
+  const int pos_min = p0 + c0 / G;  // no column of this wave sits before it
+  const float inv_scale = 1.f / a.scale_log2;
 
   // this lane's column in each column tile; padded columns repeat the
   // wave's last real column (computed, never written)
@@ -262,6 +283,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
 #pragma unroll
     for (int k = 0; k < NDT; ++k) st[ct].acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
     st[ct].m = -INFINITY;
+    st[ct].th = -INFINITY;
     st[ct].l = 0.f;
   }
   // the queries are in registers before any tile load is issued: the
@@ -284,21 +306,39 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
         ((((size_t)phys * Hkv + kvh) << a.block_shift) + (size_t)(j & sub_mask) * kTile) * D;
     load_tile<D>(stage, kpool + base, vpool + base, kTile * D * 2, wave, lane);
   };
-  for (int j = 0; j < kAhead && j < padded; ++j) issue(j);
-  for (int p = 0; p < pairs; ++p) {
-    // tiles 2p, 2p + 1 landed: the kAhead - 2 tiles issued after them may
-    // still be in flight while whole; at the stream's end nothing may
-    if (2 * p + kAhead <= padded)
-      lds_stream::tile_barrier<S::kFewest * (kAhead - 2)>();
+  auto advance = [&](int p) {  // pair p is in LDS for every wave; refill
+    // tiles 2p, 2p + 1 landed: the loads of the kAhead - 2 tiles issued
+    // after them may still be in flight while whole (this wave's own count
+    // of them); at the stream's end nothing may
+    if (2 * p + kAhead > padded)
+      lds_stream::wait_loads<0>();
+    else if (wave < S::kMore)
+      lds_stream::wait_loads<(S::kFewest + 1) * (kAhead - 2)>();
     else
-      lds_stream::tile_barrier<0>();
+      lds_stream::wait_loads<S::kFewest * (kAhead - 2)>();
+    lds_stream::workgroup_barrier();
     // refill the stages of the pair folded last (every wave is past it)
     if (2 * p + kAhead < padded) issue(2 * p + kAhead);
     if (2 * p + kAhead + 1 < padded) issue(2 * p + kAhead + 1);
+  };
+  for (int j = 0; j < kAhead && j < padded; ++j) issue(j);
+  // pairs wholly at or before this wave's first position need no masks;
+  // two loops, one per fold form, so that each keeps its accumulators in
+  // place (one loop that branches between the forms copies them)
+  const int clear = active ? (pos_min + 1) / (2 * kTile) : 0;
+  int p = 0;
+  for (; p < clear; ++p) {
+    advance(p);
+    fold_pair<D, false>(stages + ((2 * p) % kStages) * S::kBytes,
+                        stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos, 2 * p * kTile,
+                        L, a.scale_log2, inv_scale, row, kg);
+  }
+  for (; p < pairs; ++p) {
+    advance(p);
     if (active && 2 * p < wave_tiles)
-      fold_pair<D>(stages + ((2 * p) % kStages) * S::kBytes,
-                   stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos, 2 * p * kTile, L,
-                   a.scale_log2, row, kg);
+      fold_pair<D, true>(stages + ((2 * p) % kStages) * S::kBytes,
+                         stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos,
+                         2 * p * kTile, L, a.scale_log2, inv_scale, row, kg);
   }
   lds_barrier();  // every wave is done with the stages before the next item
 
@@ -323,7 +363,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(PrefillArgs a) {
   // dynamic LDS: kStages tile stages, then the work-list prefix [S + 1]
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int scan_scratch[kWaves];
@@ -336,7 +376,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     prefix[i] = n > 0 ? (n * a.group + kItemCols - 1) / kItemCols * Hkv : 0;
   }
   __syncthreads();
-  scan_counts_in_place(S, prefix, scan_scratch);
+  scan_counts_in_place<kPrefillThreads>(S, prefix, scan_scratch);
 
   const int total = prefix[S];
   const int lane = threadIdx.x & 63;
@@ -370,7 +410,7 @@ size_t prefill_mfma_smem(int num_seqs, int head_dim) {
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int head_dim, int grid, hipStream_t s) {
   PrefillArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(prefill_mfma_fn(head_dim), dim3(grid), dim3(256), args,
+  return hipLaunchKernel(prefill_mfma_fn(head_dim), dim3(grid), dim3(kPrefillThreads), args,
                          prefill_mfma_smem(a.num_seqs, head_dim), s);
 }
 

@@ -51,7 +51,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 // contiguous chunk. Ends with a barrier.
 template <int kThreads = 256>
 __device__ __forceinline__ void scan_counts_in_place(int B, int* prefix, int* scratch) {
-  constexpr int kMaxChunk = kMaxSeqs / kThreads;
+  constexpr int kMaxChunk = (kMaxSeqs + kThreads - 1) / kThreads;
   const int chunk = (B + kThreads - 1) / kThreads;  // <= kMaxChunk
   const int first = threadIdx.x * chunk;
   int counts[kMaxChunk];

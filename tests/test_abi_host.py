@@ -179,8 +179,8 @@ def test_append_rejects_null_new_tokens(lib):
     assert st == pk.PA_ERR_INVALID_ARG
 
 
-def prefill_status(lib, d, tokens=8, q=FAKE, qs=FAKE):
-    return lib.pa_prefill(q, FAKE, FAKE, FAKE, FAKE, qs, tokens, ctypes.c_float(0.1), FAKE,
+def prefill_status(lib, d, tokens=8, q=FAKE, qs=FAKE, scale=0.1):
+    return lib.pa_prefill(q, FAKE, FAKE, FAKE, FAKE, qs, tokens, ctypes.c_float(scale), FAKE,
                           ctypes.byref(d), None)
 
 
@@ -190,6 +190,8 @@ def test_prefill_host_checks(lib):
     assert prefill_status(lib, dims(), qs=None) == pk.PA_ERR_INVALID_ARG
     assert prefill_status(lib, dims(), tokens=-1) == pk.PA_ERR_INVALID_ARG
     assert prefill_status(lib, dims(num_q_heads=12)) == pk.PA_ERR_INVALID_ARG
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert prefill_status(lib, dims(), scale=bad) == pk.PA_ERR_INVALID_ARG
     assert prefill_status(lib, dims(), tokens=0) == pk.PA_OK  # nothing to do, nothing launched
 
 
