@@ -23,8 +23,10 @@
 // six tiles ahead of the two being folded, with K token rows padded to
 // 2 D + 16 bytes and V^T dim rows to 48 bytes so that the operand reads run
 // without bank conflicts. Tiles are folded in pairs: the value product's
-// k = 32 is the pair's 32 tokens (4 of each tile per lane, the same k slots
-// as the two score accumulators give the probabilities). The probabilities
+// k = 32 is the pair's 32 tokens. The two score products take the pair's
+// even and odd tokens as their rows, so that each lane's eight scores are
+// eight consecutive tokens: the probabilities' k slots, and one 16-byte
+// read of a V^T row for the value operand. The probabilities
 // enter it as single bf16 numbers: their 2^-9 relative rounding averages
 // out over the weighted sum, and a hi/lo pair would double the value
 // product's matrix work. A lazy reference max keeps the rescale of the
@@ -53,9 +55,10 @@ using lds_stream::lds_barrier;
 using lds_stream::lds_char;
 using lds_stream::load_to_lds;
 using lds_stream::raw_rsrc;
+using lds_stream::u32x4_t;
 
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
-typedef __attribute__((address_space(3))) const short4_t lds_short4;
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
 
 constexpr int kWaves = kPrefillThreads / 64;
 constexpr int kColTiles = 2;
@@ -81,6 +84,10 @@ struct Stage {
   static constexpr int kVBase = kKLoads * 1024;
   static constexpr int kLoads = kKLoads + kVLoads;
   static constexpr int kBytes = kLoads * 1024;
+  // stages sit kStride apart: the two tiles of a pair, which one score
+  // product reads together (rows 0-7 of its operand from one, 8-15 from
+  // the other), then fall on interleaved LDS banks
+  static constexpr int kStride = kBytes + 16;
   static constexpr int kFewest = kLoads / kWaves;  // loads of one tile a wave issues, at least
   static constexpr int kMore = kLoads % kWaves;    // waves below this issue one more
 };
@@ -136,12 +143,16 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
   using S = Stage<D>;
   constexpr int NQK = D / 32;
   constexpr int NDT = D / 16;
-  // score operands of both tiles: token `row`, elements 32 c + 8 kg .. + 7
+  // score operands: row i of the first product is the pair's token 2 i, of
+  // the second token 2 i + 1 (elements 32 c + 8 kg .. + 7), so that lane
+  // (column, kg) ends up with the pair's tokens 8 kg .. 8 kg + 7: even ones
+  // in the first accumulator, odd ones in the second
+  const lds_char* kt = (row < 8 ? sa : sb) + 2 * (row & 7) * S::kKRow + kg * 16;
   bf16x8_t ka[NQK], kb[NQK];
 #pragma unroll
   for (int c = 0; c < NQK; ++c) {
-    ka[c] = *(lds_bf16x8*)(sa + row * S::kKRow + c * 64 + kg * 16);
-    kb[c] = *(lds_bf16x8*)(sb + row * S::kKRow + c * 64 + kg * 16);
+    ka[c] = *(lds_bf16x8*)(kt + c * 64);
+    kb[c] = *(lds_bf16x8*)(kt + S::kKRow + c * 64);
   }
   // scores of all column tiles first (one stretch of matrix instructions),
   // then the softmax, then the value product
@@ -162,8 +173,8 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
     for (int ct = 0; ct < kColTiles; ++ct) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s0[ct][r] = tok0 + kg * 4 + r <= pos[ct] ? s0[ct][r] : -INFINITY;
-        s1[ct][r] = tok0 + kTile + kg * 4 + r <= pos[ct] ? s1[ct][r] : -INFINITY;
+        s0[ct][r] = tok0 + 8 * kg + 2 * r <= pos[ct] ? s0[ct][r] : -INFINITY;
+        s1[ct][r] = tok0 + 8 * kg + 2 * r + 1 <= pos[ct] ? s1[ct][r] : -INFINITY;
       }
     }
   }
@@ -204,30 +215,27 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
       const float pa = fast_exp2(fmaf(s0[ct][r], scale_log2, -st[ct].m));
       const float pb = fast_exp2(fmaf(s1[ct][r], scale_log2, -st[ct].m));
       psum = r == 0 ? pa + pb : psum + (pa + pb);
-      pf[ct][r] = (__bf16)pa;      // k slot 8 kg + r: token 4 kg + r of tile a
-      pf[ct][4 + r] = (__bf16)pb;  // k slot 8 kg + 4 + r: token 4 kg + r of tile b
+      pf[ct][2 * r] = (__bf16)pa;      // k slot 8 kg + 2 r: the pair's token 8 kg + 2 r
+      pf[ct][2 * r + 1] = (__bf16)pb;  // k slot 8 kg + 2 r + 1: its token 8 kg + 2 r + 1
     }
     st[ct].l += psum;
   }
   // the scheduler keeps the probabilities apart from the accumulators
   __builtin_amdgcn_sched_barrier(0);
-  // value operand: dim 16 n + row, tokens 4 kg .. + 3 of each tile; slots
-  // past L are zeroed in a masked pair
-  const int ta = tok0 + 4 * kg, tb = ta + kTile;
-  const uint32_t m0 = (ta + 0 < L ? 0x0000ffffu : 0u) | (ta + 1 < L ? 0xffff0000u : 0u);
-  const uint32_t m1 = (ta + 2 < L ? 0x0000ffffu : 0u) | (ta + 3 < L ? 0xffff0000u : 0u);
-  const uint32_t m2 = (tb + 0 < L ? 0x0000ffffu : 0u) | (tb + 1 < L ? 0xffff0000u : 0u);
-  const uint32_t m3 = (tb + 2 < L ? 0x0000ffffu : 0u) | (tb + 3 < L ? 0xffff0000u : 0u);
+  // value operand: dim 16 n + row, the pair's tokens 8 kg .. 8 kg + 7 (of
+  // tile a for kg < 2, else of tile b): 16 contiguous bytes of a V^T row;
+  // slots past L are zeroed in a masked pair
+  const lds_char* vt = (kg < 2 ? sa : sb) + S::kVBase + row * S::kVRow + (kg & 1) * 16;
+  const int t8 = tok0 + 8 * kg;
+  uint32_t vm[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    vm[q] = (t8 + 2 * q < L ? 0x0000ffffu : 0u) | (t8 + 2 * q + 1 < L ? 0xffff0000u : 0u);
 #pragma unroll
   for (int n = 0; n < NDT; ++n) {
-    const int voff = S::kVBase + (16 * n + row) * S::kVRow + kg * 8;
-    uint2 va = __builtin_bit_cast(uint2, *(lds_short4*)(sa + voff));
-    uint2 vb = __builtin_bit_cast(uint2, *(lds_short4*)(sb + voff));
-    if (kMasked) {
-      va = make_uint2(va.x & m0, va.y & m1);
-      vb = make_uint2(vb.x & m2, vb.y & m3);
-    }
-    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
+    u32x4_t v = *(lds_u32x4*)(vt + 16 * n * S::kVRow);
+    if (kMasked) v &= (u32x4_t){vm[0], vm[1], vm[2], vm[3]};
+    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, v);
 #pragma unroll
     for (int ct = 0; ct < kColTiles; ++ct)
       st[ct].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ct], st[ct].acc[n], 0, 0, 0);
@@ -296,7 +304,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   const int sub_mask = (1 << sub_shift) - 1;
   const size_t trow = (size_t)s * a.max_blocks;
   auto issue = [&](int j) {  // tile j of the stream into its stage
-    lds_char* stage = stages + (j % kStages) * S::kBytes;
+    lds_char* stage = stages + (j % kStages) * S::kStride;
     if (j >= item_tiles) {  // padding of the last pair: zeros
       load_tile<D>(stage, kpool, vpool, 0, wave, lane);
       return;
@@ -329,15 +337,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   int p = 0;
   for (; p < clear; ++p) {
     advance(p);
-    fold_pair<D, false>(stages + ((2 * p) % kStages) * S::kBytes,
-                        stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos, 2 * p * kTile,
+    fold_pair<D, false>(stages + ((2 * p) % kStages) * S::kStride,
+                        stages + ((2 * p + 1) % kStages) * S::kStride, qb, st, pos, 2 * p * kTile,
                         L, a.scale_log2, inv_scale, row, kg);
   }
   for (; p < pairs; ++p) {
     advance(p);
     if (active && 2 * p < wave_tiles)
-      fold_pair<D, true>(stages + ((2 * p) % kStages) * S::kBytes,
-                         stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos,
+      fold_pair<D, true>(stages + ((2 * p) % kStages) * S::kStride,
+                         stages + ((2 * p + 1) % kStages) * S::kStride, qb, st, pos,
                          2 * p * kTile, L, a.scale_log2, inv_scale, row, kg);
   }
   lds_barrier();  // every wave is done with the stages before the next item
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(PrefillAr
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int scan_scratch[kWaves];
   lds_char* stages = (lds_char*)smem;
-  int* prefix = (int*)(smem + kStages * Stage<D>::kBytes);
+  int* prefix = (int*)(smem + kStages * Stage<D>::kStride);
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   for (int i = threadIdx.x; i < S; i += blockDim.x) {
@@ -403,7 +411,7 @@ const void* prefill_mfma_fn(int head_dim) {
 }
 
 size_t prefill_mfma_smem(int num_seqs, int head_dim) {
-  const size_t stage = head_dim == 64 ? Stage<64>::kBytes : Stage<128>::kBytes;
+  const size_t stage = head_dim == 64 ? Stage<64>::kStride : Stage<128>::kStride;
   return kStages * stage + (size_t)(num_seqs + 1) * sizeof(int);
 }
 
