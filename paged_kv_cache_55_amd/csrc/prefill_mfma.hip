@@ -59,13 +59,16 @@ using lds_stream::u32x4_t;
 
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = kPrefillThreads / 64;
 constexpr int kColTiles = 2;
 constexpr int kCols = kColTiles * kTile;     // columns per wave
 constexpr int kItemCols = kWaves * kCols;    // columns per work item
-constexpr float kLazyLog2 = 8.f;             // reference-max slack, log2 units
+constexpr float kLazySum = 256.f;            // a lane's probability sum that moves m
+constexpr float kFarBelow = 1e30f;           // -m before a column's first pair
 constexpr int kStages = 8;                   // LDS tile stages
+constexpr int kXcds = 8;                     // L2 domains of the chip
 constexpr int kAhead = 6;                    // tiles in flight beyond the pair being folded
 static_assert(kAhead + 2 == kStages, "a pair's stages are refilled after it is folded");
 
@@ -84,10 +87,6 @@ struct Stage {
   static constexpr int kVBase = kKLoads * 1024;
   static constexpr int kLoads = kKLoads + kVLoads;
   static constexpr int kBytes = kLoads * 1024;
-  // stages sit kStride apart: the two tiles of a pair, which one score
-  // product reads together (rows 0-7 of its operand from one, 8-15 from
-  // the other), then fall on interleaved LDS banks
-  static constexpr int kStride = kBytes + 16;
   static constexpr int kFewest = kLoads / kWaves;  // loads of one tile a wave issues, at least
   static constexpr int kMore = kLoads % kWaves;    // waves below this issue one more
 };
@@ -96,7 +95,6 @@ template <int D>
 struct ColState {
   float4_t acc[D / 16];  // O^T[d][c]: dims 16 n + 4 kg + r of this lane's column
   float m;               // running reference max (log2 domain) of the column
-  float th;              // (m + kLazyLog2) / scale_log2: the raw score that moves m
   float l;               // this lane's share of the column's sum
 };
 
@@ -139,7 +137,7 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
                                           const bf16x8_t (&qb)[kColTiles][D / 32],
                                           ColState<D> (&st)[kColTiles],
                                           const int (&pos)[kColTiles], int tok0, int L,
-                                          float scale_log2, float inv_scale, int row, int kg) {
+                                          float scale_log2, int row, int kg) {
   using S = Stage<D>;
   constexpr int NQK = D / 32;
   constexpr int NDT = D / 16;
@@ -178,17 +176,38 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
       }
     }
   }
-  // lazy reference max: a column keeps its reference m until a score
-  // exceeds it by 2^kLazyLog2 (its first tile always does: m starts at
-  // -inf, and token 0 is seen by every column); p = 2^(s - m) then stays
-  // <= 2^kLazyLog2 (up to the rounding of th). The common path only
-  // compares raw scores with th; the columns' maxima and the rescale of O
-  // and l run only when a score of the wave passes its column's th.
+  // lazy reference max: the probabilities p = 2^(s scale - m) are taken
+  // against each column's reference m, and m moves only when a lane's eight
+  // of them sum past kLazySum (so every p stays below it; an overflow to
+  // inf counts too). Then, rarely, the wave takes the columns' maxima,
+  // rescales O and l, and takes the probabilities again. m starts at a
+  // finite -kFarBelow, so the first pair, which holds token 0 for every
+  // column, always moves it, and a masked score still gives p = 0. The sums
+  // add the bf16 probabilities themselves, the weights the value product
+  // applies.
+  bf16x8_t pf[kColTiles];
+  float psum[kColTiles];
+  auto probabilities = [&]() {
+#pragma unroll
+    for (int ct = 0; ct < kColTiles; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // k slots 8 kg + 2 r and 8 kg + 2 r + 1: the pair's tokens of those numbers
+        pf[ct][2 * r] = (__bf16)fast_exp2(fmaf(s0[ct][r], scale_log2, -st[ct].m));
+        pf[ct][2 * r + 1] = (__bf16)fast_exp2(fmaf(s1[ct][r], scale_log2, -st[ct].m));
+      }
+      const bf16x2_t* pp = (const bf16x2_t*)&pf[ct];
+      const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+      float sum = __builtin_amdgcn_fdot2_f32_bf16(pp[0], ones, 0.f, false);
+#pragma unroll
+      for (int q = 1; q < 4; ++q) sum = __builtin_amdgcn_fdot2_f32_bf16(pp[q], ones, sum, false);
+      psum[ct] = sum;
+    }
+  };
+  probabilities();
   bool grow = false;
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) grow |= (s0[ct][r] > st[ct].th) | (s1[ct][r] > st[ct].th);
+  for (int ct = 0; ct < kColTiles; ++ct) grow |= !(psum[ct] <= kLazySum);
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
     for (int ct = 0; ct < kColTiles; ++ct) {
@@ -196,30 +215,17 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
 #pragma unroll
       for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, fmaxf(s0[ct][r], s1[ct][r]));
       // the scale is positive, so it commutes with the max
-      const float mcol = max_over_kg(mloc) * scale_log2;
-      const float m_new = mcol > st[ct].m + kLazyLog2 ? mcol : st[ct].m;
-      const float alpha = fast_exp2(st[ct].m - m_new);  // 1 for columns that keep m
+      const float m_new = fmaxf(st[ct].m, max_over_kg(mloc) * scale_log2);
+      const float alpha = fast_exp2(st[ct].m - m_new);
       st[ct].m = m_new;
-      st[ct].th = (m_new + kLazyLog2) * inv_scale;
       st[ct].l *= alpha;
 #pragma unroll
       for (int n = 0; n < NDT; ++n) st[ct].acc[n] *= alpha;
     }
+    probabilities();
   }
-  bf16x8_t pf[kColTiles];
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) {
-    float psum;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pa = fast_exp2(fmaf(s0[ct][r], scale_log2, -st[ct].m));
-      const float pb = fast_exp2(fmaf(s1[ct][r], scale_log2, -st[ct].m));
-      psum = r == 0 ? pa + pb : psum + (pa + pb);
-      pf[ct][2 * r] = (__bf16)pa;      // k slot 8 kg + 2 r: the pair's token 8 kg + 2 r
-      pf[ct][2 * r + 1] = (__bf16)pb;  // k slot 8 kg + 2 r + 1: its token 8 kg + 2 r + 1
-    }
-    st[ct].l += psum;
-  }
+  for (int ct = 0; ct < kColTiles; ++ct) st[ct].l += psum[ct];
   // the scheduler keeps the probabilities apart from the accumulators
   __builtin_amdgcn_sched_barrier(0);
   // value operand: dim 16 n + row, the pair's tokens 8 kg .. 8 kg + 7 (of
@@ -263,7 +269,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   const int c0 = grp * kItemCols + wave * kCols;  // this wave's first column
   const bool active = c0 < ncols;
   const int pos_min = p0 + c0 / G;  // no column of this wave sits before it
-  const float inv_scale = 1.f / a.scale_log2;
 
   // this lane's column in each column tile; padded columns repeat the
   // wave's last real column (computed, never written)
@@ -290,8 +295,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   for (int ct = 0; ct < kColTiles; ++ct) {
 #pragma unroll
     for (int k = 0; k < NDT; ++k) st[ct].acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    st[ct].m = -INFINITY;
-    st[ct].th = -INFINITY;
+    st[ct].m = -kFarBelow;
     st[ct].l = 0.f;
   }
   // the queries are in registers before any tile load is issued: the
@@ -304,7 +308,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   const int sub_mask = (1 << sub_shift) - 1;
   const size_t trow = (size_t)s * a.max_blocks;
   auto issue = [&](int j) {  // tile j of the stream into its stage
-    lds_char* stage = stages + (j % kStages) * S::kStride;
+    lds_char* stage = stages + (j % kStages) * S::kBytes;
     if (j >= item_tiles) {  // padding of the last pair: zeros
       load_tile<D>(stage, kpool, vpool, 0, wave, lane);
       return;
@@ -337,16 +341,16 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   int p = 0;
   for (; p < clear; ++p) {
     advance(p);
-    fold_pair<D, false>(stages + ((2 * p) % kStages) * S::kStride,
-                        stages + ((2 * p + 1) % kStages) * S::kStride, qb, st, pos, 2 * p * kTile,
-                        L, a.scale_log2, inv_scale, row, kg);
+    fold_pair<D, false>(stages + ((2 * p) % kStages) * S::kBytes,
+                        stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos, 2 * p * kTile,
+                        L, a.scale_log2, row, kg);
   }
   for (; p < pairs; ++p) {
     advance(p);
     if (active && 2 * p < wave_tiles)
-      fold_pair<D, true>(stages + ((2 * p) % kStages) * S::kStride,
-                         stages + ((2 * p + 1) % kStages) * S::kStride, qb, st, pos,
-                         2 * p * kTile, L, a.scale_log2, inv_scale, row, kg);
+      fold_pair<D, true>(stages + ((2 * p) % kStages) * S::kBytes,
+                         stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos,
+                         2 * p * kTile, L, a.scale_log2, row, kg);
   }
   lds_barrier();  // every wave is done with the stages before the next item
 
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(PrefillAr
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int scan_scratch[kWaves];
   lds_char* stages = (lds_char*)smem;
-  int* prefix = (int*)(smem + kStages * Stage<D>::kStride);
+  int* prefix = (int*)(smem + kStages * Stage<D>::kBytes);
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   for (int i = threadIdx.x; i < S; i += blockDim.x) {
@@ -390,7 +394,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(PrefillAr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = gridDim.x;
-  const int wg = blockIdx.x;
+  // workgroups are dispatched to the XCDs in turn (w on XCD w % kXcds), and
+  // each XCD has its own L2: slot numbers run across one XCD's workgroups
+  // first, so consecutive items (the column groups of one sequence and KV
+  // head, which stream the same tiles) run side by side on one L2
+  const int wg = W % kXcds == 0 ? (blockIdx.x % kXcds) * (W / kXcds) + blockIdx.x / kXcds
+                                : (int)blockIdx.x;
   for (int k = 0; k * W < total; ++k) {
     const int item = (k & 1) ? (k + 1) * W - 1 - wg : k * W + wg;
     if (item >= total) continue;
@@ -411,7 +420,7 @@ const void* prefill_mfma_fn(int head_dim) {
 }
 
 size_t prefill_mfma_smem(int num_seqs, int head_dim) {
-  const size_t stage = head_dim == 64 ? Stage<64>::kStride : Stage<128>::kStride;
+  const size_t stage = head_dim == 64 ? Stage<64>::kBytes : Stage<128>::kBytes;
   return kStages * stage + (size_t)(num_seqs + 1) * sizeof(int);
 }
 
