@@ -23,24 +23,37 @@ __device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
 }
 
 // 16 bytes per lane from the buffer at byte offset `off` into LDS at
-// `dst` + 16 * lane (buffer_load_dwordx4 with the LDS destination in M0,
-// streaming cache policy). Written as assembly so that the compiler does
-// not track these LDS writes: it cannot tell the stages apart and would
-// otherwise make every later LDS read wait for all of them, the prefetch
-// included. Completion is awaited explicitly (tile_barrier). M0 belongs to
-// the compiler, so the sequence restores it.
+// `dst` + 16 * lane (buffer_load_dwordx4 with the LDS destination in M0).
+// kStream: non-temporal cache policy, for data read once; without it the
+// lines stay in L2 for other workgroups that read the same tile. Written as
+// assembly so that the compiler does not track these LDS writes: it cannot
+// tell the stages apart and would otherwise make every later LDS read wait
+// for all of them, the prefetch included. Completion is awaited explicitly
+// (tile_barrier). M0 belongs to the compiler, so the sequence restores it.
+template <bool kStream = true>
 __device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(off), "s"(rsrc)
-      : "memory");
+  if (kStream)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0), "v"(off), "s"(rsrc)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0), "v"(off), "s"(rsrc)
+        : "memory");
 }
 
 // Waits until at most kYounger of this wave's vector memory operations are

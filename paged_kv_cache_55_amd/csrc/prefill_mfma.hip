@@ -19,10 +19,13 @@
 // eight waves (two per SIMD, so that one wave's softmax overlaps the other's
 // matrix work) own 32 columns each, and all of them read the same K/V
 // tiles. The 16-token tiles are staged once per workgroup in LDS by buffer
-// loads with an LDS destination (no staging registers), eight stages deep,
-// six tiles ahead of the two being folded, with K token rows padded to
-// 2 D + 16 bytes and V^T dim rows to 48 bytes so that the operand reads run
-// without bank conflicts. Tiles are folded in pairs: the value product's
+// loads with an LDS destination (no staging registers), ten stages deep:
+// the pair being scored, the pair whose value product is pending, and six
+// tiles in flight. K token rows are padded to 2 D + 16 bytes and V^T dim
+// rows left at 32: each operand read then steps through rows an odd
+// multiple of 32 bytes apart, which the LDS serves without bank conflicts
+// (even multiples, and 48- or 80-byte steps, conflict two ways). Tiles are
+// folded in pairs: the value product's
 // k = 32 is the pair's 32 tokens. The two score products take the pair's
 // even and odd tokens as their rows, so that each lane's eight scores are
 // eight consecutive tokens: the probabilities' k slots, and one 16-byte
@@ -67,13 +70,14 @@ constexpr int kCols = kColTiles * kTile;     // columns per wave
 constexpr int kItemCols = kWaves * kCols;    // columns per work item
 constexpr float kLazySum = 256.f;            // a lane's probability sum that moves m
 constexpr float kFarBelow = 1e30f;           // -m before a column's first pair
-constexpr int kStages = 8;                   // LDS tile stages
+constexpr int kStages = 10;                  // LDS tile stages
 constexpr int kXcds = 8;                     // L2 domains of the chip
 constexpr int kAhead = 6;                    // tiles in flight beyond the pair being folded
-static_assert(kAhead + 2 == kStages, "a pair's stages are refilled after it is folded");
+static_assert(kAhead + 4 == kStages,
+              "the pair being scored and the pair whose value product is pending stay in LDS");
 
 // LDS stage of one 16-token tile: K rows [16][2 D + 16 bytes], then V^T
-// rows [D][48 bytes], each region whole wave loads of 1 KiB (lane l of
+// rows [D][32 bytes], each region whole wave loads of 1 KiB (lane l of
 // load k fills bytes 1024 k + 16 l).
 template <int D>
 struct Stage {
@@ -81,7 +85,7 @@ struct Stage {
   static constexpr int kKRowChunks = kKRow / 16;
   static constexpr int kKDataChunks = 2 * D / 16;
   static constexpr int kKLoads = (kTile * kKRowChunks + 63) / 64;
-  static constexpr int kVRow = 48;
+  static constexpr int kVRow = 2 * kTile;
   static constexpr int kVRowChunks = kVRow / 16;
   static constexpr int kVLoads = (D * kVRowChunks + 63) / 64;
   static constexpr int kVBase = kKLoads * 1024;
@@ -127,20 +131,19 @@ __device__ __forceinline__ void load_tile(lds_char* stage, const bf16_t* kt, con
   }
 }
 
-// Folds tiles (tok0 .. tok0 + 15) in stage a and (tok0 + 16 .. tok0 + 31) in
-// stage b into the column states. kMasked: tokens past the sequence (L) or
-// past a column's position are masked, and V^T slots past L, which may hold
-// anything (NaN included), are zeroed; a pair wholly at or before every
-// column's position (hence before L) needs neither.
+// Scores of the pair of tiles (tok0 .. tok0 + 15) in stage a and
+// (tok0 + 16 .. tok0 + 31) in stage b for every column tile. kMasked: the
+// scores of tokens past a column's position (hence of every token past L)
+// become -inf; a pair wholly at or before every column's position needs no
+// mask.
 template <int D, bool kMasked>
-__device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb,
-                                          const bf16x8_t (&qb)[kColTiles][D / 32],
-                                          ColState<D> (&st)[kColTiles],
-                                          const int (&pos)[kColTiles], int tok0, int L,
-                                          float scale_log2, int row, int kg) {
+__device__ __forceinline__ void pair_scores(const lds_char* sa, const lds_char* sb,
+                                            const bf16x8_t (&qb)[kColTiles][D / 32],
+                                            const int (&pos)[kColTiles], int tok0, int row,
+                                            int kg, float4_t (&s0)[kColTiles],
+                                            float4_t (&s1)[kColTiles]) {
   using S = Stage<D>;
   constexpr int NQK = D / 32;
-  constexpr int NDT = D / 16;
   // score operands: row i of the first product is the pair's token 2 i, of
   // the second token 2 i + 1 (elements 32 c + 8 kg .. + 7), so that lane
   // (column, kg) ends up with the pair's tokens 8 kg .. 8 kg + 7: even ones
@@ -152,9 +155,6 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
     ka[c] = *(lds_bf16x8*)(kt + c * 64);
     kb[c] = *(lds_bf16x8*)(kt + S::kKRow + c * 64);
   }
-  // scores of all column tiles first (one stretch of matrix instructions),
-  // then the softmax, then the value product
-  float4_t s0[kColTiles], s1[kColTiles];
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
     s0[ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
@@ -165,7 +165,6 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
       s1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c], qb[ct][c], s1[ct], 0, 0, 0);
     }
   }
-  // masked scores in place
   if (kMasked) {
 #pragma unroll
     for (int ct = 0; ct < kColTiles; ++ct) {
@@ -176,16 +175,25 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
       }
     }
   }
-  // lazy reference max: the probabilities p = 2^(s scale - m) are taken
-  // against each column's reference m, and m moves only when a lane's eight
-  // of them sum past kLazySum (so every p stays below it; an overflow to
-  // inf counts too). Then, rarely, the wave takes the columns' maxima,
-  // rescales O and l, and takes the probabilities again. m starts at a
-  // finite -kFarBelow, so the first pair, which holds token 0 for every
-  // column, always moves it, and a masked score still gives p = 0. The sums
-  // add the bf16 probabilities themselves, the weights the value product
-  // applies.
-  bf16x8_t pf[kColTiles];
+}
+
+// The pair's probabilities pf from its scores, folded into l (and, when the
+// reference moves, into the rescale of O and l).
+//
+// Lazy reference max: the probabilities p = 2^(s scale - m) are taken
+// against each column's reference m, and m moves only when a lane's eight
+// of them sum past kLazySum (so every p stays below it; an overflow to inf
+// counts too). Then, rarely, the wave takes the columns' maxima, rescales
+// O and l, and takes the probabilities again. m starts at a finite
+// -kFarBelow, so the first pair, which holds token 0 for every column,
+// always moves it, and a masked score still gives p = 0. The sums add the
+// bf16 probabilities themselves, the weights the value product applies.
+template <int D>
+__device__ __forceinline__ void pair_softmax(const float4_t (&s0)[kColTiles],
+                                             const float4_t (&s1)[kColTiles],
+                                             ColState<D> (&st)[kColTiles], float scale_log2,
+                                             bf16x8_t (&pf)[kColTiles]) {
+  constexpr int NDT = D / 16;
   float psum[kColTiles];
   auto probabilities = [&]() {
 #pragma unroll
@@ -226,11 +234,20 @@ __device__ __forceinline__ void fold_pair(const lds_char* sa, const lds_char* sb
   }
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) st[ct].l += psum[ct];
-  // the scheduler keeps the probabilities apart from the accumulators
-  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The value product of the pair in stages a, b (first token tok0) with its
+// probabilities pf. kMasked: V^T slots past L, which may hold anything (NaN
+// included), are zeroed.
+template <int D, bool kMasked>
+__device__ __forceinline__ void pair_values(const lds_char* sa, const lds_char* sb,
+                                            const bf16x8_t (&pf)[kColTiles],
+                                            ColState<D> (&st)[kColTiles], int tok0, int L,
+                                            int row, int kg) {
+  using S = Stage<D>;
+  constexpr int NDT = D / 16;
   // value operand: dim 16 n + row, the pair's tokens 8 kg .. 8 kg + 7 (of
-  // tile a for kg < 2, else of tile b): 16 contiguous bytes of a V^T row;
-  // slots past L are zeroed in a masked pair
+  // tile a for kg < 2, else of tile b): 16 contiguous bytes of a V^T row
   const lds_char* vt = (kg < 2 ? sa : sb) + S::kVBase + row * S::kVRow + (kg & 1) * 16;
   const int t8 = tok0 + 8 * kg;
   uint32_t vm[4];
@@ -329,29 +346,57 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
     else
       lds_stream::wait_loads<S::kFewest * (kAhead - 2)>();
     lds_stream::workgroup_barrier();
-    // refill the stages of the pair folded last (every wave is past it)
+    // refill the stages of pair p - 2 (every wave is past its value product)
     if (2 * p + kAhead < padded) issue(2 * p + kAhead);
     if (2 * p + kAhead + 1 < padded) issue(2 * p + kAhead + 1);
   };
   for (int j = 0; j < kAhead && j < padded; ++j) issue(j);
-  // pairs wholly at or before this wave's first position need no masks;
-  // two loops, one per fold form, so that each keeps its accumulators in
-  // place (one loop that branches between the forms copies them)
+  auto stage = [&](int j) -> const lds_char* { return stages + (j % kStages) * S::kBytes; };
+  // Software pipeline: iteration p takes the scores of pair p, then the
+  // value product of pair p - 1, whose probabilities are ready, then the
+  // softmax of pair p: the value product's matrix instructions do not wait
+  // on the softmax's vector instructions, so the two interleave. Pairs
+  // wholly at or before this wave's first position need no masks; they run
+  // in a loop of their own, so that it keeps its accumulators in place (one
+  // loop that branches between the forms copies them).
   const int clear = active ? (pos_min + 1) / (2 * kTile) : 0;
+  bf16x8_t pf[kColTiles];  // probabilities of the pair whose value product is pending
+  int pending = -1;        // that pair, or -1
   int p = 0;
-  for (; p < clear; ++p) {
-    advance(p);
-    fold_pair<D, false>(stages + ((2 * p) % kStages) * S::kBytes,
-                        stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos, 2 * p * kTile,
-                        L, a.scale_log2, row, kg);
+  if (clear > 0) {
+    advance(0);
+    float4_t s0[kColTiles], s1[kColTiles];
+    pair_scores<D, false>(stage(0), stage(1), qb, pos, 0, row, kg, s0, s1);
+    pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+    for (p = 1; p < clear; ++p) {
+      advance(p);
+      pair_scores<D, false>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
+                            s1);
+      pair_values<D, false>(stage(2 * p - 2), stage(2 * p - 1), pf, st, (2 * p - 2) * kTile, L,
+                            row, kg);
+      pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+    }
+    pending = clear - 1;
   }
   for (; p < pairs; ++p) {
     advance(p);
-    if (active && 2 * p < wave_tiles)
-      fold_pair<D, true>(stages + ((2 * p) % kStages) * S::kBytes,
-                         stages + ((2 * p + 1) % kStages) * S::kBytes, qb, st, pos,
-                         2 * p * kTile, L, a.scale_log2, row, kg);
+    const bool fold = active && 2 * p < wave_tiles;
+    float4_t s0[kColTiles], s1[kColTiles];
+    if (fold)
+      pair_scores<D, true>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
+                           s1);
+    if (pending >= 0)
+      pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st,
+                           2 * pending * kTile, L, row, kg);
+    pending = -1;
+    if (fold) {
+      pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+      pending = p;
+    }
   }
+  if (pending >= 0)
+    pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st, 2 * pending * kTile,
+                         L, row, kg);
   lds_barrier();  // every wave is done with the stages before the next item
 
   if (!active) return;
