@@ -102,7 +102,9 @@ struct ColState {
   float l;               // this lane's share of the column's sum
 };
 
-// Issues this wave's share of the loads of one tile: K rows from `kt`
+// Issues this wave's share of the loads of one tile: the default cache
+// policy, since the other column blocks of the (sequence, KV head), on the
+// same XCD, read the same tiles through its L2. K rows from `kt`
 // (16 x D, contiguous), V^T rows from `vt` (D x 16, contiguous); an empty
 // tile (bytes = 0) fills the stage with zeros.
 template <int D>
@@ -120,13 +122,13 @@ __device__ __forceinline__ void load_tile(lds_char* stage, const bf16_t* kt, con
       const int t = slot / S::kKRowChunks;
       const int ch = slot - t * S::kKRowChunks;
       const int off = t < kTile && ch < S::kKDataChunks ? t * 2 * D + ch * 16 : kPastRange;
-      load_to_lds(kr, stage + 1024 * k, off);
+      load_to_lds<false>(kr, stage + 1024 * k, off);
     } else {
       const int slot = 64 * (k - S::kKLoads) + lane;
       const int d = slot / S::kVRowChunks;
       const int ch = slot - d * S::kVRowChunks;
       const int off = d < D && ch < 2 ? d * 2 * kTile + ch * 16 : kPastRange;
-      load_to_lds(vr, stage + 1024 * k, off);
+      load_to_lds<false>(vr, stage + 1024 * k, off);
     }
   }
 }
