@@ -232,9 +232,10 @@ typedef struct {
 } pa_latent_dims;
 
 /* Bytes of device workspace pa_latent_decode needs: control counters, per
- * row two piece counters and an overflow flag, then partial records (each
- * piece's output normalised by its own sum, as bf16, and its fp32 max and
- * sum for 128 heads) for two pieces per workgroup of a grid of at most 256. Zero-fill it before its first use; every call leaves it
+ * row a description of its pieces and an overflow flag, then partial
+ * records (each piece's output normalised by its own sum, as bf16, and its
+ * fp32 max and sum for 128 heads) for two pieces per workgroup of a grid
+ * of at most 256. Zero-fill it before its first use; every call leaves it
  * reusable. Calls that may overlap in time need separate workspaces.
  * Returns 0 for invalid dims (pa_latent_decode reports those). */
 size_t pa_latent_workspace_bytes(const pa_latent_dims* dims);
@@ -243,10 +244,11 @@ size_t pa_latent_workspace_bytes(const pa_latent_dims* dims);
  *   out[b,h,:] = sum_t softmax_t(scale * <q[b,h,:], c_b[t]>) c_b[t][0:512]
  * over t < seq_lens[b], with the latents c_b gathered through
  * block_tables[b] (fp32 accumulation; weights enter the value product as
- * bf16). A persistent grid streams equal shares of all 32-token tiles; a
- * row split across workgroups is merged (log-sum-exp over the pieces'
- * bf16-rounded normalised outputs, in piece order) by its last piece, so
- * results do not depend on timing.
+ * bf16). A persistent grid streams equal shares of all 32-token tiles
+ * (each row's finish counted as a few tiles); the pieces of a row split
+ * across workgroups are merged by a second kernel on the same stream
+ * (log-sum-exp over the pieces' bf16-rounded normalised outputs, in piece
+ * order), so results do not depend on timing.
  * A row whose scores rise more than 2^32 above a piece's first-tile maximum
  * is recomputed exactly (two passes) at the end of the call. Slots at or
  * past seq_lens[b] never reach the result; bf16 output is rounded to

@@ -179,10 +179,10 @@ struct LatentArgs {
   const int32_t* seq_lens;
   void* out;                   // [B, H, 512]
   // cut rows: records of two piece slots per workgroup (bf16 O[h][d]
-  // normalised by the piece's sum, then fp32 m[H] and l[H]); per row two
-  // counters (pieces arrived, records written) and an overflow flag; two
-  // control counters (workgroups finished, segments flagged). The counters
-  // and flags are zero between calls.
+  // normalised by the piece's sum, then fp32 m[H] and l[H]); per row its
+  // pieces (first slot, count; written by every call for rows with tokens)
+  // and an overflow flag; two control counters (workgroups finished,
+  // segments flagged). The flags and counters are zero between calls.
   void* ws_rec;
   int* ws_cnt;   // [B][2]
   int* ws_flag;  // [B]

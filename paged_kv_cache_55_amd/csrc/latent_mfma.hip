@@ -29,16 +29,15 @@
 // work, which here is the other bound). The softmax keeps a lazy reference
 // max, as the prefill kernel does.
 //
-// Work split: the flat list of (row, 32-token tile) is cut into equal
-// contiguous ranges, one per workgroup of a persistent grid (one workgroup
-// per compute unit). A row cut by range boundaries is finished by the last
-// of its pieces to arrive: each piece first counts itself in; the last one
-// waits until the others, which have all counted already and so are
-// running, have written their records (output normalised by the piece's
-// sum as bf16, max and sum as fp32: 129 KiB, as much as 115 tokens of
-// latent cache), merges them with its own piece and writes the row. A cut
-// thus costs one record write and one read, and no workgroup ever waits
-// for one that has not started.
+// Work split: the flat list of (row, 32-token tile) is cut into contiguous
+// ranges, one per workgroup of a persistent grid (one workgroup per compute
+// unit), equal in cost: a row's tiles plus kFinishSlots tiles' worth for
+// writing it, so that workgroups with many short rows take fewer tiles. A
+// row cut by range boundaries leaves one record per piece (its output
+// normalised by the piece's sum as bf16, max and sum as fp32: 129 KiB, as
+// much as 115 tokens of latent cache) and a description of its pieces; a
+// second kernel merges each cut row in parallel over its heads. No
+// workgroup waits for another, and no merge sits at the end of a range.
 #include <type_traits>
 
 #include "launch.h"
@@ -82,7 +81,8 @@ constexpr int kQkSteps = kLatent / 32;  // 18 score steps
 constexpr int kDimTiles = kValue / 16;  // 32 output dim tiles
 constexpr float kOverflowLog2 = 32.f;   // weights up to 2^32 over the reference
 constexpr int kRecordBytes = kLatentRecordBytes;
-constexpr int kMergeBatch = 8;          // pieces whose loads a merge round issues together
+constexpr int kFinishSlots = 8;         // a row's finish, in tile-equivalents of work
+constexpr int kMergePieces = 4;         // pieces whose record loads a merge round issues together
 #ifndef LATENT_K_AHEAD
 #define LATENT_K_AHEAD 2
 #endif
@@ -91,7 +91,6 @@ constexpr int kMergeBatch = 8;          // pieces whose loads a merge round issu
 #endif
 constexpr int kKAhead = LATENT_K_AHEAD;  // score steps of LDS reads in flight
 constexpr int kVAhead = LATENT_V_AHEAD;  // value steps of LDS reads in flight
-constexpr int kCoherent = 16;           // buffer cache policy sc1 (device-coherent)
 
 static_assert(kPageTokens % kTileTokens == 0, "tiles never straddle a page");
 static_assert(kTileTokens == 32, "one value step of 32 tokens per tile");
@@ -351,17 +350,11 @@ __device__ __forceinline__ int record_l(int slot, int h) {
   return record_base(slot) + kHeads * kValue * 2 + kHeads * 4 + h * 4;
 }
 
-__device__ __forceinline__ float load_coherent(__amdgpu_buffer_rsrc_t rec, int off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rec, off, 0, kCoherent));
+__device__ __forceinline__ void store_rec8(__amdgpu_buffer_rsrc_t rec, int off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rec, off, 0, 0);
 }
-__device__ __forceinline__ uint2 load_coherent8(__amdgpu_buffer_rsrc_t rec, int off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rec, off, 0, kCoherent));
-}
-__device__ __forceinline__ void store_coherent8(__amdgpu_buffer_rsrc_t rec, int off, uint2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rec, off, 0, kCoherent);
-}
-__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t rec, int off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rec, off, 0, kCoherent);
+__device__ __forceinline__ void store_rec(__amdgpu_buffer_rsrc_t rec, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rec, off, 0, 0);
 }
 
 // A piece's normalised output chunk (4 dims of one head) as 4 bf16: what
@@ -394,144 +387,26 @@ __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slo
     const float inv = 1.f / ltot[ht];
 #pragma unroll
     for (int n = 0; n < kDimTiles; ++n)
-      store_coherent8(rec, record_x(slot, h, 16 * n + 4 * kg), normalised_chunk(st.o[ht][n], inv));
+      store_rec8(rec, record_x(slot, h, 16 * n + 4 * kg), normalised_chunk(st.o[ht][n], inv));
     if (kg == 0) {
-      store_coherent(rec, record_m(slot, h), st.m[ht]);
-      store_coherent(rec, record_l(slot, h), ltot[ht]);
+      store_rec(rec, record_m(slot, h), st.m[ht]);
+      store_rec(rec, record_l(slot, h), ltot[ht]);
     }
   }
 }
 
 // Slot of piece i (0 .. n - 1) of a row cut over workgroups v0 .. v0 + n - 1.
-__device__ __forceinline__ int piece_slot(int v0, int first_slot, int i) {
-  return i == 0 ? first_slot : 2 * (v0 + i);
-}
-
-// The last piece of a cut row writes the row: out = sum_i w_i x_i over the
-// pieces in piece order, x_i the piece's normalised output rounded to bf16
-// (its own computed from the registers exactly as its record would hold
-// it), w_i = l_i 2^(m_i - M) / L (log-sum-exp merge). The result is thus the
-// same whichever piece arrives last. Loads are issued a batch at a time: a
-// two-piece row (the common cut) takes one round trip for the other
-// piece's (m, l) and one for its data.
-__device__ __forceinline__ void merge_and_store(const LatentArgs& a, __amdgpu_buffer_rsrc_t rec,
-                                                const RowState& st, const float (&ltot)[2], int b,
-                                                int v0, int n, int first_slot, int my_slot,
-                                                int h0, int col, int kg) {
-  float M[2], L[2], inv_mine[2];
-  // merged max and sum per head, kMergeBatch pieces per round
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    M[ht] = st.m[ht];
-    L[ht] = 0.f;  // accumulated in piece order below
-    inv_mine[ht] = 1.f / ltot[ht];
-  }
-  for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int h = h0 + 16 * ht + col;
-      float mv[kMergeBatch];
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int slot = piece_slot(v0, first_slot, i0 + j);
-        const bool other = i0 + j < n && slot != my_slot;
-        mv[j] = other ? load_coherent(rec, record_m(slot, h)) : -INFINITY;
-      }
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) M[ht] = fmaxf(M[ht], mv[j]);
-    }
-  }
-  for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int h = h0 + 16 * ht + col;
-      float mv[kMergeBatch], lv[kMergeBatch];
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int slot = piece_slot(v0, first_slot, i0 + j);
-        const bool mine = slot == my_slot;
-        const bool other = i0 + j < n && !mine;
-        mv[j] = other ? load_coherent(rec, record_m(slot, h)) : (mine ? st.m[ht] : -INFINITY);
-        lv[j] = other ? load_coherent(rec, record_l(slot, h)) : (mine ? ltot[ht] : 0.f);
-      }
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j)
-        if (i0 + j < n) L[ht] += lv[j] * fast_exp2(mv[j] - M[ht]);
-    }
-  }
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int h = h0 + 16 * ht + col;
-    bf16_t* out = (bf16_t*)a.out + ((size_t)b * kHeads + h) * kValue + 4 * kg;
-    const float invL = 1.f / L[ht];
-    if (n == 2) {
-      const int other = piece_slot(v0, first_slot, first_slot == my_slot ? 1 : 0);
-      const float mo = load_coherent(rec, record_m(other, h));
-      const float lo = load_coherent(rec, record_l(other, h));
-      const float w_mine = ltot[ht] * fast_exp2(st.m[ht] - M[ht]) * invL;
-      const float w_other = lo * fast_exp2(mo - M[ht]) * invL;
-      const bool mine_first = first_slot == my_slot;
-      const float w0 = mine_first ? w_mine : w_other;
-      const float w1 = mine_first ? w_other : w_mine;
-      uint2 xo[kDimTiles];
-#pragma unroll
-      for (int nn = 0; nn < kDimTiles; ++nn)
-        xo[nn] = load_coherent8(rec, record_x(other, h, 16 * nn + 4 * kg));
-#pragma unroll
-      for (int nn = 0; nn < kDimTiles; ++nn) {
-        const float4_t xm = widen(normalised_chunk(st.o[ht][nn], inv_mine[ht]));
-        const float4_t xp = widen(xo[nn]);
-        // piece 0, then piece 1, as the general path sums
-        const float4_t v = fma4(mine_first ? xp : xm, w1, fma4(mine_first ? xm : xp, w0, zero4()));
-        *(uint2*)(out + 16 * nn) = make_uint2(pack_bf16x2(bf16_rne(v[0]), bf16_rne(v[1])),
-                                              pack_bf16x2(bf16_rne(v[2]), bf16_rne(v[3])));
-      }
-      continue;
-    }
-    // more pieces: 8 dims tiles at a time, kMergeBatch pieces per round
-#pragma unroll
-    for (int g = 0; g < kDimTiles; g += 8) {
-      float4_t acc[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = zero4();
-      for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
-        float w[kMergeBatch];
-        uint2 x[kMergeBatch][8];
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-          const int slot = piece_slot(v0, first_slot, i0 + j);
-          const bool other = i0 + j < n && slot != my_slot;
-          const float mj = other ? load_coherent(rec, record_m(slot, h)) : st.m[ht];
-          const float lj = other ? load_coherent(rec, record_l(slot, h)) : ltot[ht];
-          w[j] = i0 + j < n ? lj * fast_exp2(mj - M[ht]) * invL : 0.f;
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            x[j][u] = other ? load_coherent8(rec, record_x(slot, h, 16 * (g + u) + 4 * kg))
-                            : normalised_chunk(st.o[ht][g + u], inv_mine[ht]);
-        }
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j)
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (i0 + j < n) acc[u] = fma4(widen(x[j][u]), w[j], acc[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        *(uint2*)(out + 16 * (g + u)) =
-            make_uint2(pack_bf16x2(bf16_rne(acc[u][0]), bf16_rne(acc[u][1])),
-                       pack_bf16x2(bf16_rne(acc[u][2]), bf16_rne(acc[u][3])));
-    }
-  }
-}
-
-// A finished segment (flat tiles seg0 .. seg1 - 1 of row c.b). Whole rows
-// are written; a cut row's piece is counted in, then either written as a
-// record (not the last piece) or merged with the others and written (the
-// last). A segment marked for overflow flags its row for the slow path. The
+// A finished segment (flat tiles seg0 .. seg1 - 1 of row c.b). A whole row
+// is written; a piece of a cut row is written as a record, in slot
+// 2 w of workgroup w for its range's first segment and 2 w + 1 for its
+// last, for the merge kernel. The workgroup holding the row's first tile
+// also describes the row's pieces: its first slot and their number
+// (workgroups floor(x / T) over the row's tiles' cost positions x). A
+// segment marked for overflow flags its row for the slow path. The
 // protocol is workgroup-uniform.
 __device__ __forceinline__ void finish_segment(const LatentArgs& a, const Cursor& c,
                                                const RowState& st, int seg0, int seg1, int f0,
-                                               int chunk, const int* prefix,
+                                               int T, const int* prefix, const int* cprefix,
                                                __amdgpu_buffer_rsrc_t rec, int* bcast, int wave,
                                                int h0, int col, int kg) {
   const float ltot[2] = {sum_over_kg(st.l[0]), sum_over_kg(st.l[1])};
@@ -551,43 +426,19 @@ __device__ __forceinline__ void finish_segment(const LatentArgs& a, const Cursor
   }
   const int row0 = prefix[c.b];
   const int row1 = prefix[c.b + 1];
+  if (seg0 == row0 && threadIdx.x == 0) {  // device-scope: the slow path may overwrite
+    const int v1 = (cprefix[c.b] + (row1 - row0) - 1) / T;
+    __hip_atomic_store(a.ws_cnt + 2 * c.b, 2 * (int)blockIdx.x + (row0 == f0 ? 0 : 1),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.ws_cnt + 2 * c.b + 1, v1 - (int)blockIdx.x + 1, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (seg0 == row0 && seg1 == row1) {
     const float inv[2] = {1.f / ltot[0], 1.f / ltot[1]};
     store_scaled(a, st.o, inv, c.b, h0, col, kg);
     return;
   }
-  // pieces: workgroups v0 .. v1; the piece of workgroup v is its first
-  // segment (slot 2 v) unless v = v0 began before the row (slot 2 v + 1)
-  const int v0 = row0 / chunk;
-  const int v1 = (row1 - 1) / chunk;
-  const int first_slot = 2 * v0 + (v0 * chunk < row0 ? 1 : 0);
-  const int my_slot = 2 * (int)blockIdx.x + (seg0 == f0 ? 0 : 1);
-  int* done = a.ws_cnt + 2 * c.b;
-  int* written = done + 1;
-  if (threadIdx.x == 0)
-    bcast[0] = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  lds_barrier();
-  const int arrived = bcast[0];
-  lds_barrier();  // bcast is free again
-  if (arrived == v1 - v0) {
-    // the last piece: every other piece has counted itself in and is
-    // writing (or has written) its record
-    if (threadIdx.x == 0)
-      while (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < v1 - v0)
-        __builtin_amdgcn_s_sleep(2);
-    lds_barrier();
-    merge_and_store(a, rec, st, ltot, c.b, v0, v1 - v0 + 1, first_slot, my_slot, h0, col, kg);
-    if (threadIdx.x == 0) {  // rearm for the next call
-      __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(written, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  } else {
-    write_record(rec, my_slot, st, ltot, h0, col, kg);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
-    lds_barrier();                                     // ... and every wave's
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(written, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  write_record(rec, 2 * (int)blockIdx.x + (seg0 == f0 ? 0 : 1), st, ltot, h0, col, kg);
 }
 
 // ---- slow path: rows whose scores outran their reference --------------------
@@ -638,16 +489,28 @@ __device__ __forceinline__ void recompute_row(const LatentArgs& a, const int* pr
 }
 
 __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
-  // dynamic LDS: kStages tile stages, then the work-list prefix [B + 1]
+  // dynamic LDS: kStages tile stages, then the rows' tile prefix [B + 1]
+  // and cost prefix [B + 1]
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int scan_scratch[kWaves];
   __shared__ int bcast[1 + kWaves];
   lds_char* stages = (lds_char*)smem;
   int* prefix = (int*)(smem + kStages * kStageBytes);
+  int* cprefix = prefix + a.num_seqs + 1;
 
   const int B = a.num_seqs;
   if (threadIdx.x < 1 + kWaves) bcast[threadIdx.x] = 0;
-  build_partition_prefix(a.seq_lens, B, kTileTokens, prefix, scan_scratch);
+  // a row of L tokens is ceil(L / 32) tiles and costs kFinishSlots more for
+  // its finish (L > 0)
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const int L = a.seq_lens[i];
+    const int t = L > 0 ? (L + kTileTokens - 1) / kTileTokens : 0;
+    prefix[i] = t;
+    cprefix[i] = t > 0 ? t + kFinishSlots : 0;
+  }
+  __syncthreads();
+  scan_counts_in_place(B, prefix, scan_scratch);
+  scan_counts_in_place(B, cprefix, scan_scratch);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -662,10 +525,22 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
     for (int i = threadIdx.x; i < kHeads * kValue / 8; i += 256) o[i] = make_uint4(0, 0, 0, 0);
   }
 
+  // Workgroup w takes the cost range [w T, (w + 1) T): its tiles, with a
+  // boundary that falls among a row's finish slots moved to the row's end.
+  // With T > kFinishSlots every full range holds a tile, so the pieces of a
+  // cut row are consecutive workgroups, the tile at cost position x lies in
+  // workgroup floor(x / T), and the finishes spread with the tiles.
   const int total = prefix[B];
-  const int chunk = max((total + a.grid - 1) / a.grid, a.min_tiles);
-  const int f0 = blockIdx.x * chunk;
-  const int f1 = min(f0 + chunk, total);
+  const int ctotal = cprefix[B];
+  const int T = max((ctotal + a.grid - 1) / a.grid, a.min_tiles);
+  auto boundary = [&](int w) {
+    const int x = w * T;
+    if (x >= ctotal) return total;
+    const int b = find_sequence(cprefix, B, x);
+    return prefix[b] + min(x - cprefix[b], prefix[b + 1] - prefix[b]);
+  };
+  const int f0 = boundary(blockIdx.x);
+  const int f1 = boundary(blockIdx.x + 1);
   const __amdgpu_buffer_rsrc_t rec = range_rsrc(a.ws_rec, 2 * a.grid * kRecordBytes);
 
   if (f0 < f1) {
@@ -707,7 +582,7 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
       // it would also drain the tile prefetch)
       tile_step(std::true_type{});
       while (f < seg1) tile_step(std::false_type{});
-      finish_segment(a, cc, st, seg0, seg1, f0, chunk, prefix, rec, bcast, wave, h0, col, kg);
+      finish_segment(a, cc, st, seg0, seg1, f0, T, prefix, cprefix, rec, bcast, wave, h0, col, kg);
       if (f < f1) {  // the next row with tiles
         int b = cc.b + 1;
         while (prefix[b + 1] == prefix[b]) ++b;
@@ -731,8 +606,12 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
         continue;
       recompute_row(a, prefix, b, stages, wave, lane, h0, col, kg);
       lds_barrier();
-      if (threadIdx.x == 0)
+      if (threadIdx.x == 0) {
+        // the row is written: the merge kernel takes it as whole (its
+        // first-tile workgroup wrote the piece count before counting out)
+        __hip_atomic_store(a.ws_cnt + 2 * b + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.ws_flag + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   if (threadIdx.x == 0) {  // rearm for the next call
@@ -741,17 +620,90 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
   }
 }
 
+// ---- merging cut rows -----------------------------------------------------------
+//
+// Workgroup (b, q) writes heads 32 q .. 32 q + 31 of cut row b: out = sum_i
+// w_i x_i over the row's pieces in piece order, x_i a piece's normalised
+// output as its record holds it (bf16), w_i = l_i 2^(m_i - M) / L
+// (log-sum-exp merge), one fused multiply-add per piece and element. Thread
+// t takes head 32 q + t / 8 and 8 chunks of 8 dims (dims 64 j + 8 (t % 8)
+// .. + 7, j = 0..7); the record loads of kMergePieces pieces go out
+// together. Rows that are whole, empty or recomputed by the slow path (its
+// piece count set to 1) are left as the decode kernel wrote them.
+__global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
+  const int b = blockIdx.x >> 2;
+  const int q = blockIdx.x & 3;
+  if (uniform_load(a.seq_lens, b) <= 0) return;
+  const int n = uniform_load(a.ws_cnt, 2 * b + 1);
+  if (n < 2) return;
+  const int first_slot = uniform_load(a.ws_cnt, 2 * b);
+  const int v0 = first_slot >> 1;
+  const int h = 32 * q + (threadIdx.x >> 3);
+  const int d0 = 8 * (threadIdx.x & 7);
+  const __amdgpu_buffer_rsrc_t rec = range_rsrc(a.ws_rec, 2 * a.grid * kRecordBytes);
+  auto slot_of = [&](int i) { return i == 0 ? first_slot : 2 * (v0 + i); };
+  auto load_f = [&](int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rec, off, 0, 0));
+  };
+  // merged max and sum of the head, in piece order
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, load_f(record_m(slot_of(i), h)));
+  float Lsum = 0.f;
+  for (int i = 0; i < n; ++i) {
+    const int sl = slot_of(i);
+    Lsum += load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M);
+  }
+  const float invL = 1.f / Lsum;
+  float4_t acc[8][2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j][0] = acc[j][1] = zero4();
+  for (int i0 = 0; i0 < n; i0 += kMergePieces) {
+    float w[kMergePieces];
+    uint4 x[kMergePieces][8];
+#pragma unroll
+    for (int k = 0; k < kMergePieces; ++k) {
+      if (i0 + k >= n) break;
+      const int sl = slot_of(i0 + k);
+      w[k] = load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M) * invL;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[k][j] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rec, record_x(sl, h, 64 * j + d0), 0, 0));
+    }
+#pragma unroll
+    for (int k = 0; k < kMergePieces; ++k) {
+      if (i0 + k >= n) break;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[j][0] = fma4(widen(make_uint2(x[k][j].x, x[k][j].y)), w[k], acc[j][0]);
+        acc[j][1] = fma4(widen(make_uint2(x[k][j].z, x[k][j].w)), w[k], acc[j][1]);
+      }
+    }
+  }
+  bf16_t* out = (bf16_t*)a.out + ((size_t)b * kHeads + h) * kValue + d0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *(uint4*)(out + 64 * j) =
+        make_uint4(pack_bf16x2(bf16_rne(acc[j][0][0]), bf16_rne(acc[j][0][1])),
+                   pack_bf16x2(bf16_rne(acc[j][0][2]), bf16_rne(acc[j][0][3])),
+                   pack_bf16x2(bf16_rne(acc[j][1][0]), bf16_rne(acc[j][1][1])),
+                   pack_bf16x2(bf16_rne(acc[j][1][2]), bf16_rne(acc[j][1][3])));
+}
+
 }  // namespace
 
 const void* latent_decode_fn() { return (const void*)latent_decode_kernel; }
 
 size_t latent_decode_smem(int num_seqs) {
-  return (size_t)kStages * kStageBytes + (size_t)(num_seqs + 1) * sizeof(int);
+  return (size_t)kStages * kStageBytes + (size_t)2 * (num_seqs + 1) * sizeof(int);
 }
 
 hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(latent_decode_kernel, dim3(a.grid), dim3(256), latent_decode_smem(a.num_seqs),
                      s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(latent_merge_kernel, dim3(4 * a.num_seqs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
