@@ -75,6 +75,8 @@ static_assert(kTileTokens * kRowChunks % 64 == 0, "a tile is whole wave loads");
 static_assert(kTileLoads * 1024 == kLatentStageBytes, "stage size");
 constexpr int kStageBytes = kLatentStageBytes;
 constexpr int kStages = kLatentStages;
+constexpr int kAhead = kStages - 1;  // tiles in flight while one is folded
+static_assert(kAhead <= 3, "tile_barrier counts at most two younger tiles");
 constexpr int kWaveLoads = (kTileLoads + kWaves - 1) / kWaves;  // 10
 constexpr int kFewestLoads = kTileLoads / kWaves;               // 9
 constexpr int kQkSteps = kLatent / 32;  // 18 score steps
@@ -152,12 +154,9 @@ __device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, 
 // Waits until this wave's loads of the current tile have landed in LDS (at
 // most kFewestLoads younger ones, those of the next tile, may remain; none
 // when no tile follows), then for every wave of the workgroup.
-template <bool kNextInFlight>
+template <int kYoungerTiles>
 __device__ __forceinline__ void tile_barrier() {
-  if (kNextInFlight)
-    lds_stream::tile_barrier<kFewestLoads>();
-  else
-    lds_stream::tile_barrier<0>();
+  lds_stream::tile_barrier<kYoungerTiles * kFewestLoads>();
 }
 
 using lds_stream::lds_barrier;
@@ -547,9 +546,15 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
     Cursor cc = locate_tile(prefix, B, f0);
     Cursor lc = cc;
     load_tile(a, lc, stages, wave, lane);
-    if (f0 + 1 < f1) {
+    // written out: as a loop, the compiler loses track of the stage
+    // addresses being uniform
+    if (kAhead > 1 && f0 + 1 < f1) {
       next_tile(lc, prefix);
       load_tile(a, lc, stages + kStageBytes, wave, lane);
+    }
+    if (kAhead > 2 && f0 + 2 < f1) {
+      next_tile(lc, prefix);
+      load_tile(a, lc, stages + 2 * kStageBytes, wave, lane);
     }
     // tile f of the range sits in stage (f - f0) % kStages; segments: the
     // range's part of one row each, inside which the queries and the row
@@ -562,15 +567,19 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
       load_queries(a, cc.b, h0, col, kg, qf);
       RowState st;
       st.overflow = false;
-      // one tile: wait for it, start the tile two ahead, fold
+      // one tile: wait for it (the tiles issued after it may stay in
+      // flight), start the tile kAhead ahead in the stage folded last, fold
       auto tile_step = [&](auto first) {
-        if (f + 1 < f1)
-          tile_barrier<true>();
+        const int younger = min(kAhead - 1, f1 - 1 - f);
+        if (kAhead > 2 && younger >= 2)
+          tile_barrier<kAhead - 1>();
+        else if (younger >= 1)
+          tile_barrier<1>();
         else
-          tile_barrier<false>();
-        if (f + 2 < f1) {
+          tile_barrier<0>();
+        if (f + kAhead < f1) {
           next_tile(lc, prefix);
-          load_tile(a, lc, stages + ((f + 2 - f0) % kStages) * kStageBytes, wave, lane);
+          load_tile(a, lc, stages + ((f + kAhead - f0) % kStages) * kStageBytes, wave, lane);
         }
         const int valid = min(kTileTokens, L - (cc.j + f - seg0) * kTileTokens);
         const lds_char* tile = stages + ((f - f0) % kStages) * kStageBytes;
