@@ -421,7 +421,8 @@ def main():
         "copy_blocks_us": None if copy_us is None else round(copy_us, 2),
         "roofline": {
             "kernel": (f"prefill_mfma_kernel<{D}>" if args.config == 6 else
-                       "latent_decode_kernel (one launch per call; cut rows merged inside it)"
+                       "latent_decode_kernel + latent_merge_kernel (one call: the decode, then "
+                       "the merge of cut rows)"
                        if args.config == 7 else
                        roofline_kernel(kernel, part, D) + (" with the fused KV append"
                                                            if fused else "")),

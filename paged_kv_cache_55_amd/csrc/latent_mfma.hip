@@ -85,6 +85,7 @@ constexpr float kOverflowLog2 = 32.f;   // weights up to 2^32 over the reference
 constexpr int kRecordBytes = kLatentRecordBytes;
 constexpr int kFinishSlots = 8;         // a row's finish, in tile-equivalents of work
 constexpr int kMergePieces = 4;         // pieces whose record loads a merge round issues together
+constexpr int kFewPieces = 8;           // rows of at most this many pieces: (m, l) in registers
 #ifndef LATENT_K_AHEAD
 #define LATENT_K_AHEAD 2
 #endif
@@ -654,13 +655,28 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   auto load_f = [&](int off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rec, off, 0, 0));
   };
-  // merged max and sum of the head, in piece order
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, load_f(record_m(slot_of(i), h)));
-  float Lsum = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const int sl = slot_of(i);
-    Lsum += load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M);
+  // merged max and sum of the head, in piece order: every (m, l) in one
+  // round trip when the row has at most kFewPieces pieces
+  float M = -INFINITY, Lsum = 0.f;
+  float mv[kFewPieces], lv[kFewPieces];
+  if (n <= kFewPieces) {
+#pragma unroll
+    for (int k = 0; k < kFewPieces; ++k) {
+      const bool in = k < n;
+      mv[k] = in ? load_f(record_m(slot_of(k), h)) : -INFINITY;
+      lv[k] = in ? load_f(record_l(slot_of(k), h)) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kFewPieces; ++k) M = fmaxf(M, mv[k]);
+#pragma unroll
+    for (int k = 0; k < kFewPieces; ++k)
+      if (k < n) Lsum += lv[k] * fast_exp2(mv[k] - M);
+  } else {
+    for (int i = 0; i < n; ++i) M = fmaxf(M, load_f(record_m(slot_of(i), h)));
+    for (int i = 0; i < n; ++i) {
+      const int sl = slot_of(i);
+      Lsum += load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M);
+    }
   }
   const float invL = 1.f / Lsum;
   float4_t acc[8][2];
@@ -673,7 +689,15 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
     for (int k = 0; k < kMergePieces; ++k) {
       if (i0 + k >= n) break;
       const int sl = slot_of(i0 + k);
-      w[k] = load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M) * invL;
+      if (n <= kFewPieces) {  // weights from the registers (i0 + k < kFewPieces)
+        float mk = mv[0], lk = lv[0];
+#pragma unroll
+        for (int u = 1; u < kFewPieces; ++u)
+          if (u == i0 + k) mk = mv[u], lk = lv[u];
+        w[k] = lk * fast_exp2(mk - M) * invL;
+      } else {
+        w[k] = load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M) * invL;
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         x[k][j] = __builtin_bit_cast(
