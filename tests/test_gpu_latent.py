@@ -60,6 +60,38 @@ def test_latent_long_rows_over_many_workgroups(lens):
     check(wl.latent_case(1003 + len(lens), lens))
 
 
+def test_latent_4096_short_rows_sampled():
+    """The most rows a call takes: 4,096 rows of 0-90 tokens (a quarter of
+    them empty), so the work list's two prefixes fill their LDS share and
+    every workgroup range holds dozens of whole rows; 24 rows are checked,
+    empty ones among them."""
+    rng = np.random.default_rng(1013)
+    lens = rng.integers(0, 91, size=4096)
+    lens[rng.choice(4096, 1024, replace=False)] = 0
+    c = wl.latent_case(1013, lens.tolist())
+    rows = sorted(set(rng.choice(4096, 20, replace=False).tolist() + [0, 1, 4094, 4095]))
+    worst = check(c, rows)
+    print(f"latent 4096 rows worst ratio {worst:.3f}")
+
+
+def test_latent_one_long_row_among_short_ones():
+    """One 30,000-token row (938 tiles, cut over many workgroups) among 200
+    rows of 1-40 tokens: the ranges weigh the short rows' finishes, so the
+    long row's pieces and the short rows' workgroups differ widely in tiles."""
+    rng = np.random.default_rng(1014)
+    lens = rng.integers(1, 41, size=201)
+    lens[100] = 30000
+    c = wl.latent_case(1014, lens.tolist())
+    rows = [0, 50, 99, 100, 101, 150, 200]
+    check(c, rows)
+
+
+def test_latent_tiny_batch():
+    """Three rows of a few tokens: fewer cost slots than workgroups, so the
+    per-range cost takes its floor and most workgroups get no tiles."""
+    check(wl.latent_case(1015, [1, 3, 33]))
+
+
 def test_latent_decode_batch_full_size_sampled():
     """The measured workload (B = 256, the 70B serving batch's length mix):
     the kernel runs over the whole batch; the oracle checks 16 rows, the
