@@ -19,9 +19,9 @@
 // eight waves (two per SIMD, so that one wave's softmax overlaps the other's
 // matrix work) own 32 columns each, and all of them read the same K/V
 // tiles. The 16-token tiles are staged once per workgroup in LDS by buffer
-// loads with an LDS destination (no staging registers), ten stages deep:
-// the pair being scored, the pair whose value product is pending, and six
-// tiles in flight. K token rows are padded to 2 D + 16 bytes and V^T dim
+// loads with an LDS destination (no staging registers), eight stages deep:
+// the pair being scored, the pair whose value product is pending, and four
+// tiles in flight (measured faster than two or six). K token rows are padded to 2 D + 16 bytes and V^T dim
 // rows left at 32: each operand read then steps through rows an odd
 // multiple of 32 bytes apart, which the LDS serves without bank conflicts
 // (even multiples, and 48- or 80-byte steps, conflict two ways). Tiles are
@@ -70,9 +70,9 @@ constexpr int kCols = kColTiles * kTile;     // columns per wave
 constexpr int kItemCols = kWaves * kCols;    // columns per work item
 constexpr float kLazySum = 256.f;            // a lane's probability sum that moves m
 constexpr float kFarBelow = 1e30f;           // -m before a column's first pair
-constexpr int kStages = 10;                  // LDS tile stages
+constexpr int kStages = 8;                  // LDS tile stages
 constexpr int kXcds = 8;                     // L2 domains of the chip
-constexpr int kAhead = 6;                    // tiles in flight beyond the pair being folded
+constexpr int kAhead = 4;                    // tiles in flight beyond the pair being folded
 static_assert(kAhead + 4 == kStages,
               "the pair being scored and the pair whose value product is pending stay in LDS");
 
