@@ -102,34 +102,58 @@ struct ColState {
   float l;               // this lane's share of the column's sum
 };
 
-// Issues this wave's share of the loads of one tile: the default cache
-// policy, since the other column blocks of the (sequence, KV head), on the
-// same XCD, read the same tiles through its L2. K rows from `kt`
-// (16 x D, contiguous), V^T rows from `vt` (D x 16, contiguous); an empty
-// tile (bytes = 0) fills the stage with zeros.
+// This wave's share of a tile's loads, fixed for the kernel: load
+// k = wave + kWaves i (i < n) fills bytes 1024 k .. + 1023 of a stage, lane
+// l the 16 bytes at 1024 k + 16 l, taken from the tile's K rows (16 x D,
+// contiguous) for k < kKLoads, else from its V^T rows (D x 16, contiguous),
+// at byte offset off[i] (past the range for pad chunks, which load zeros).
+// Worked out once so that a tile's issue is a few scalar instructions: the
+// scalar unit serves both waves of a SIMD, and per-tile address arithmetic
+// there measurably slowed the whole kernel.
 template <int D>
-__device__ __forceinline__ void load_tile(lds_char* stage, const bf16_t* kt, const bf16_t* vt,
-                                          int bytes, int wave, int lane) {
+struct TileLoads {
   using S = Stage<D>;
-  const u32x4_t kr = raw_rsrc(kt, bytes);
-  const u32x4_t vr = raw_rsrc(vt, bytes);
+  static constexpr int kPerWave = (S::kLoads + kWaves - 1) / kWaves;
+  int n;                // loads per tile (uniform)
+  bool v[kPerWave];     // from the V^T rows (uniform)
+  int off[kPerWave];    // this lane's byte offset within the tile's K or V^T rows
+  __device__ __forceinline__ TileLoads(int wave, int lane) {
+    n = 0;
 #pragma unroll
-  for (int i = 0; i < (S::kLoads + kWaves - 1) / kWaves; ++i) {
-    const int k = wave + kWaves * i;
-    if (k >= S::kLoads) break;
-    if (k < S::kKLoads) {
-      const int slot = 64 * k + lane;
-      const int t = slot / S::kKRowChunks;
-      const int ch = slot - t * S::kKRowChunks;
-      const int off = t < kTile && ch < S::kKDataChunks ? t * 2 * D + ch * 16 : kPastRange;
-      load_to_lds<false>(kr, stage + 1024 * k, off);
-    } else {
-      const int slot = 64 * (k - S::kKLoads) + lane;
-      const int d = slot / S::kVRowChunks;
-      const int ch = slot - d * S::kVRowChunks;
-      const int off = d < D && ch < 2 ? d * 2 * kTile + ch * 16 : kPastRange;
-      load_to_lds<false>(vr, stage + 1024 * k, off);
+    for (int i = 0; i < kPerWave; ++i) {
+      const int k = wave + kWaves * i;
+      v[i] = k >= S::kKLoads;
+      off[i] = kPastRange;
+      if (k >= S::kLoads) continue;
+      n = i + 1;
+      if (k < S::kKLoads) {
+        const int slot = 64 * k + lane;
+        const int t = slot / S::kKRowChunks;
+        const int ch = slot - t * S::kKRowChunks;
+        off[i] = t < kTile && ch < S::kKDataChunks ? t * 2 * D + ch * 16 : kPastRange;
+      } else {
+        const int slot = 64 * (k - S::kKLoads) + lane;
+        const int d = slot / S::kVRowChunks;
+        const int ch = slot - d * S::kVRowChunks;
+        off[i] = d < D && ch < 2 ? d * 2 * kTile + ch * 16 : kPastRange;
+      }
     }
+  }
+};
+
+// Issues this wave's loads of one tile into `stage`: load i reads `bytes`
+// (0: the stage fills with zeros) from pool[i] + base, the pool (K or V)
+// that load takes. The default cache policy: the other column blocks of the
+// (sequence, KV head), on the same XCD, read the same tiles through its L2.
+template <int D>
+__device__ __forceinline__ void load_tile(const TileLoads<D>& tl, lds_char* stage,
+                                          const bf16_t* const (&pool)[TileLoads<D>::kPerWave],
+                                          size_t base, int bytes, int wave) {
+#pragma unroll
+  for (int i = 0; i < TileLoads<D>::kPerWave; ++i) {
+    if (i >= tl.n) break;
+    load_to_lds<false>(raw_rsrc(pool[i] + base, bytes), stage + 1024 * (wave + kWaves * i),
+                       tl.off[i]);
   }
 }
 
@@ -270,8 +294,9 @@ __device__ __forceinline__ void pair_values(const lds_char* sa, const lds_char* 
 // One work item: columns grp * 256 .. + 255 of (sequence s, KV head); wave
 // w owns columns grp * 256 + 64 w .. + 63.
 template <int D>
-__device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* stages, int s,
-                                             int kvh, int grp, int wave, int lane) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoads<D>& tl,
+                                             lds_char* stages, int s, int kvh, int grp, int wave,
+                                             int lane) {
   using S = Stage<D>;
   constexpr int NQK = D / 32;
   constexpr int NDT = D / 16;
@@ -321,22 +346,30 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
   // compiler's wait for them stays out of the tile loop
   __builtin_amdgcn_s_waitcnt(0);
 
-  const bf16_t* kpool = (const bf16_t*)a.k_pool;
-  const bf16_t* vpool = (const bf16_t*)a.v_pool;
+  // tile j's rows start phys * blk + kvh_off + (j & sub_mask) * sub elements
+  // into either pool (phys: the sequence's block holding the tile)
+  const bf16_t* kpool = (const bf16_t*)a.k_pool + ((size_t)kvh << a.block_shift) * D;
+  const bf16_t* vpool = (const bf16_t*)a.v_pool + ((size_t)kvh << a.block_shift) * D;
+  const size_t blk = ((size_t)Hkv << a.block_shift) * D;
   const int sub_shift = a.block_shift - 4;
   const int sub_mask = (1 << sub_shift) - 1;
-  const size_t trow = (size_t)s * a.max_blocks;
-  auto issue = [&](int j) {  // tile j of the stream into its stage
-    lds_char* stage = stages + (j % kStages) * S::kBytes;
-    if (j >= item_tiles) {  // padding of the last pair: zeros
-      load_tile<D>(stage, kpool, vpool, 0, wave, lane);
-      return;
-    }
-    const int32_t phys = uniform_load(a.block_tables, trow + (j >> sub_shift));
-    const size_t base =
-        ((((size_t)phys * Hkv + kvh) << a.block_shift) + (size_t)(j & sub_mask) * kTile) * D;
-    load_tile<D>(stage, kpool + base, vpool + base, kTile * D * 2, wave, lane);
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
+  const bf16_t* pool[TileLoads<D>::kPerWave];
+#pragma unroll
+  for (int i = 0; i < TileLoads<D>::kPerWave; ++i) pool[i] = tl.v[i] ? vpool : kpool;
+  // block-table entry of tile j (the padding tiles past the item take the
+  // last block's, and load nothing)
+  const int last_block = (item_tiles - 1) >> sub_shift;
+  auto entry = [&](int j) { return uniform_load(trow, min(j >> sub_shift, last_block)); };
+  auto issue = [&](int j, int32_t phys) {  // tile j of the stream into its stage
+    const size_t base = (size_t)phys * blk + (size_t)((j & sub_mask) * kTile * D);
+    load_tile<D>(tl, stages + (j % kStages) * S::kBytes, pool, base,
+                 j < item_tiles ? kTile * D * 2 : 0, wave);
   };
+  // the entries of the two tiles a refill issues are read one step before
+  // it: waiting for a scalar load right after the barrier held up both the
+  // refill and the fold
+  int32_t next_a = entry(kAhead), next_b = entry(kAhead + 1);
   auto advance = [&](int p) {  // pair p is in LDS for every wave; refill
     // tiles 2p, 2p + 1 landed: the loads of the kAhead - 2 tiles issued
     // after them may still be in flight while whole (this wave's own count
@@ -349,10 +382,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, lds_char* sta
       lds_stream::wait_loads<S::kFewest * (kAhead - 2)>();
     lds_stream::workgroup_barrier();
     // refill the stages of pair p - 2 (every wave is past its value product)
-    if (2 * p + kAhead < padded) issue(2 * p + kAhead);
-    if (2 * p + kAhead + 1 < padded) issue(2 * p + kAhead + 1);
+    const int32_t pa = next_a, pb = next_b;
+    next_a = entry(2 * p + 2 + kAhead);
+    next_b = entry(2 * p + 3 + kAhead);
+    if (2 * p + kAhead < padded) issue(2 * p + kAhead, pa);
+    if (2 * p + kAhead + 1 < padded) issue(2 * p + kAhead + 1, pb);
   };
-  for (int j = 0; j < kAhead && j < padded; ++j) issue(j);
+  for (int j = 0; j < kAhead && j < padded; ++j) issue(j, entry(j));
   auto stage = [&](int j) -> const lds_char* { return stages + (j % kStages) * S::kBytes; };
   // Software pipeline: iteration p takes the scores of pair p, then the
   // value product of pair p - 1, whose probabilities are ready, then the
@@ -440,6 +476,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(PrefillAr
   const int total = prefix[S];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const TileLoads<D> tl(wave, lane);
   const int W = gridDim.x;
   // workgroups are dispatched to the XCDs in turn (w on XCD w % kXcds), and
   // each XCD has its own L2: slot numbers run across one XCD's workgroups
@@ -455,7 +492,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(PrefillAr
     const int n = uniform_load(a.query_start, s + 1) - uniform_load(a.query_start, s);
     const int ngrp = (n * a.group + kItemCols - 1) / kItemCols;
     const int kvh = r / ngrp;
-    prefill_item<D>(a, stages, s, kvh, r - kvh * ngrp, wave, lane);
+    prefill_item<D>(a, tl, stages, s, kvh, r - kvh * ngrp, wave, lane);
   }
 }
 
