@@ -125,6 +125,13 @@ __device__ __forceinline__ int32_t uniform_load(const int32_t* base, size_t idx)
   return ((const const_i32_t*)base)[idx];
 }
 
+// The same for a non-negative index below 2^30: the byte offset stays a
+// 32-bit register operand of the scalar load, with no 64-bit address math.
+__device__ __forceinline__ int32_t uniform_load_u32(const int32_t* base, uint32_t idx) {
+  typedef __attribute__((address_space(4))) const char const_char_t;
+  return *(const const_i32_t*)((const const_char_t*)base + (idx << 2));
+}
+
 // ---- decode arguments ------------------------------------------------------
 
 // Everything a decode kernel needs; passed by value.

@@ -56,6 +56,24 @@ __device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off
         : "memory");
 }
 
+// 16 bytes per lane from the global address `src` (one per lane) into LDS
+// at `dst` + 16 * lane (global_load_lds_dwordx4), default cache policy.
+// The same conventions as load_to_lds: untracked by the compiler, awaited
+// with wait_loads / tile_barrier, M0 restored.
+__device__ __forceinline__ void global_load_to_lds(const void* src, lds_char* dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+
 // Waits until at most kYounger of this wave's vector memory operations are
 // outstanding (they complete in order: everything older has landed), and
 // for this wave's LDS operations.

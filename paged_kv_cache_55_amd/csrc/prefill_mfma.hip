@@ -18,14 +18,16 @@
 // A work item is 256 columns of one (sequence, KV head): its workgroup's
 // eight waves (two per SIMD, so that one wave's softmax overlaps the other's
 // matrix work) own 32 columns each, and all of them read the same K/V
-// tiles. The 16-token tiles are staged once per workgroup in LDS by buffer
-// loads with an LDS destination (no staging registers), eight stages deep:
-// the pair being scored, the pair whose value product is pending, and four
-// tiles in flight (measured faster than two or six). K token rows are padded to 2 D + 16 bytes and V^T dim
-// rows left at 32: each operand read then steps through rows an odd
-// multiple of 32 bytes apart, which the LDS serves without bank conflicts
-// (even multiples, and 48- or 80-byte steps, conflict two ways). Tiles are
-// folded in pairs: the value product's
+// tiles. The 16-token tiles are staged once per workgroup in LDS by global
+// loads with an LDS destination (no staging registers; each lane holds its
+// own address, so a tile's issue is one uniform offset added per load),
+// eight stages deep: the pair being scored, the pair whose value product is
+// pending, and four tiles in flight (measured faster than two or six). K
+// token rows are padded to 2 D + 16 bytes and V^T dim rows left at 32: each
+// operand read then steps through rows an odd multiple of 32 bytes apart,
+// which the LDS serves without bank conflicts (even multiples, and 48- or
+// 80-byte steps, conflict two ways). Tiles are folded in pairs: the value
+// product's
 // k = 32 is the pair's 32 tokens. The two score products take the pair's
 // even and odd tokens as their rows, so that each lane's eight scores are
 // eight consecutive tokens: the probabilities' k slots, and one 16-byte
@@ -53,11 +55,8 @@ namespace pagedkv {
 namespace {
 
 using namespace mfma;
-using lds_stream::kPastRange;
 using lds_stream::lds_barrier;
 using lds_stream::lds_char;
-using lds_stream::load_to_lds;
-using lds_stream::raw_rsrc;
 using lds_stream::u32x4_t;
 
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
@@ -106,10 +105,11 @@ struct ColState {
 // k = wave + kWaves i (i < n) fills bytes 1024 k .. + 1023 of a stage, lane
 // l the 16 bytes at 1024 k + 16 l, taken from the tile's K rows (16 x D,
 // contiguous) for k < kKLoads, else from its V^T rows (D x 16, contiguous),
-// at byte offset off[i] (past the range for pad chunks, which load zeros).
-// Worked out once so that a tile's issue is a few scalar instructions: the
-// scalar unit serves both waves of a SIMD, and per-tile address arithmetic
-// there measurably slowed the whole kernel.
+// at byte offset off[i]. Lanes whose 16 bytes are stage padding (the pad of
+// a K row, the gap after the K rows), which nothing reads, load the tile's
+// first 16 bytes. Worked out once so that a tile's issue is a few
+// instructions: the scalar unit serves both waves of a SIMD, and per-tile
+// address arithmetic there measurably slowed the whole kernel.
 template <int D>
 struct TileLoads {
   using S = Stage<D>;
@@ -123,37 +123,36 @@ struct TileLoads {
     for (int i = 0; i < kPerWave; ++i) {
       const int k = wave + kWaves * i;
       v[i] = k >= S::kKLoads;
-      off[i] = kPastRange;
+      off[i] = 0;
       if (k >= S::kLoads) continue;
       n = i + 1;
       if (k < S::kKLoads) {
         const int slot = 64 * k + lane;
         const int t = slot / S::kKRowChunks;
         const int ch = slot - t * S::kKRowChunks;
-        off[i] = t < kTile && ch < S::kKDataChunks ? t * 2 * D + ch * 16 : kPastRange;
+        off[i] = t < kTile && ch < S::kKDataChunks ? t * 2 * D + ch * 16 : 0;
       } else {
         const int slot = 64 * (k - S::kKLoads) + lane;
         const int d = slot / S::kVRowChunks;
         const int ch = slot - d * S::kVRowChunks;
-        off[i] = d < D && ch < 2 ? d * 2 * kTile + ch * 16 : kPastRange;
+        off[i] = d < D && ch < 2 ? d * 2 * kTile + ch * 16 : 0;
       }
     }
   }
 };
 
-// Issues this wave's loads of one tile into `stage`: load i reads `bytes`
-// (0: the stage fills with zeros) from pool[i] + base, the pool (K or V)
-// that load takes. The default cache policy: the other column blocks of the
+// Issues this wave's loads of one tile into `stage`: lane src[i] + toff
+// for load i, src[i] being this lane's address in the tile at offset 0 of
+// its pool. The default cache policy: the other column blocks of the
 // (sequence, KV head), on the same XCD, read the same tiles through its L2.
 template <int D>
 __device__ __forceinline__ void load_tile(const TileLoads<D>& tl, lds_char* stage,
-                                          const bf16_t* const (&pool)[TileLoads<D>::kPerWave],
-                                          size_t base, int bytes, int wave) {
+                                          const char* const (&src)[TileLoads<D>::kPerWave],
+                                          uint64_t toff, int wave) {
 #pragma unroll
   for (int i = 0; i < TileLoads<D>::kPerWave; ++i) {
     if (i >= tl.n) break;
-    load_to_lds<false>(raw_rsrc(pool[i] + base, bytes), stage + 1024 * (wave + kWaves * i),
-                       tl.off[i]);
+    lds_stream::global_load_to_lds(src[i] + toff, stage + 1024 * (wave + kWaves * i));
   }
 }
 
@@ -332,7 +331,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
   const int wave_tiles = (p0 + min(c0 + kCols - 1, ncols - 1) / G) / kTile + 1;
   const int item_tiles = (p0 + min(grp * kItemCols + kItemCols - 1, ncols - 1) / G) / kTile + 1;
   const int pairs = (item_tiles + 1) / 2;
-  const int padded = 2 * pairs;
 
   ColState<D> st[kColTiles];
 #pragma unroll
@@ -346,35 +344,41 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
   // compiler's wait for them stays out of the tile loop
   __builtin_amdgcn_s_waitcnt(0);
 
-  // tile j's rows start phys * blk + kvh_off + (j & sub_mask) * sub elements
-  // into either pool (phys: the sequence's block holding the tile)
-  const bf16_t* kpool = (const bf16_t*)a.k_pool + ((size_t)kvh << a.block_shift) * D;
-  const bf16_t* vpool = (const bf16_t*)a.v_pool + ((size_t)kvh << a.block_shift) * D;
-  const size_t blk = ((size_t)Hkv << a.block_shift) * D;
+  // tile j's rows start phys * blk + kvh_off + (j & sub_mask) * kTile D
+  // elements into either pool (phys: the sequence's block holding the tile)
+  const size_t kvh_off = ((size_t)kvh << a.block_shift) * D * sizeof(bf16_t);
+  const uint32_t blk_bytes = ((uint32_t)Hkv << a.block_shift) * D * sizeof(bf16_t);
+  constexpr uint32_t kTileBytes = kTile * D * sizeof(bf16_t);
   const int sub_shift = a.block_shift - 4;
   const int sub_mask = (1 << sub_shift) - 1;
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
-  const bf16_t* pool[TileLoads<D>::kPerWave];
+  const char* src[TileLoads<D>::kPerWave];
 #pragma unroll
-  for (int i = 0; i < TileLoads<D>::kPerWave; ++i) pool[i] = tl.v[i] ? vpool : kpool;
-  // block-table entry of tile j (the padding tiles past the item take the
-  // last block's, and load nothing)
+  for (int i = 0; i < TileLoads<D>::kPerWave; ++i)
+    src[i] = (const char*)(tl.v[i] ? a.v_pool : a.k_pool) + kvh_off + tl.off[i];
+  // block-table entry of tile j (clamped to the item's last block for the
+  // lookahead past the item's end)
   const int last_block = (item_tiles - 1) >> sub_shift;
-  auto entry = [&](int j) { return uniform_load(trow, min(j >> sub_shift, last_block)); };
-  auto issue = [&](int j, int32_t phys) {  // tile j of the stream into its stage
-    const size_t base = (size_t)phys * blk + (size_t)((j & sub_mask) * kTile * D);
-    load_tile<D>(tl, stages + (j % kStages) * S::kBytes, pool, base,
-                 j < item_tiles ? kTile * D * 2 : 0, wave);
+  auto entry = [&](int j) {
+    return uniform_load_u32(trow, (uint32_t)min(j >> sub_shift, last_block));
+  };
+  auto issue = [&](int j, int32_t phys) {  // tile j (< item_tiles) into its stage
+    const uint64_t toff =
+        (uint64_t)(uint32_t)phys * blk_bytes + (uint32_t)(j & sub_mask) * kTileBytes;
+    load_tile<D>(tl, stages + (j % kStages) * S::kBytes, src, toff, wave);
   };
   // the entries of the two tiles a refill issues are read one step before
   // it: waiting for a scalar load right after the barrier held up both the
   // refill and the fold
   int32_t next_a = entry(kAhead), next_b = entry(kAhead + 1);
+  // The padding tile that rounds an odd item up to whole pairs is never
+  // loaded: its stage keeps older data (or none), and the masks, which
+  // select, turn every score and value of tokens past L into -inf and 0.
   auto advance = [&](int p) {  // pair p is in LDS for every wave; refill
     // tiles 2p, 2p + 1 landed: the loads of the kAhead - 2 tiles issued
-    // after them may still be in flight while whole (this wave's own count
-    // of them); at the stream's end nothing may
-    if (2 * p + kAhead > padded)
+    // after them may still be in flight while all of them are real tiles
+    // (this wave's own count of them); else nothing may
+    if (2 * p + kAhead > item_tiles)
       lds_stream::wait_loads<0>();
     else if (wave < S::kMore)
       lds_stream::wait_loads<(S::kFewest + 1) * (kAhead - 2)>();
@@ -385,10 +389,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
     const int32_t pa = next_a, pb = next_b;
     next_a = entry(2 * p + 2 + kAhead);
     next_b = entry(2 * p + 3 + kAhead);
-    if (2 * p + kAhead < padded) issue(2 * p + kAhead, pa);
-    if (2 * p + kAhead + 1 < padded) issue(2 * p + kAhead + 1, pb);
+    if (2 * p + kAhead < item_tiles) issue(2 * p + kAhead, pa);
+    if (2 * p + kAhead + 1 < item_tiles) issue(2 * p + kAhead + 1, pb);
   };
-  for (int j = 0; j < kAhead && j < padded; ++j) issue(j, entry(j));
+  for (int j = 0; j < kAhead && j < item_tiles; ++j) issue(j, entry(j));
   auto stage = [&](int j) -> const lds_char* { return stages + (j % kStages) * S::kBytes; };
   // Software pipeline: iteration p takes the scores of pair p, then the
   // value product of pair p - 1, whose probabilities are ready, then the
