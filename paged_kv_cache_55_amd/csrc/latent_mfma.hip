@@ -81,7 +81,8 @@ constexpr int kWaveLoads = (kTileLoads + kWaves - 1) / kWaves;  // 10
 constexpr int kFewestLoads = kTileLoads / kWaves;               // 9
 constexpr int kQkSteps = kLatent / 32;  // 18 score steps
 constexpr int kDimTiles = kValue / 16;  // 32 output dim tiles
-constexpr float kOverflowLog2 = 32.f;   // weights up to 2^32 over the reference
+constexpr int kOverflowLog2 = 32;  // weights up to 2^32 over the reference
+constexpr float kOverflowWeight = (float)(1ull << kOverflowLog2);
 constexpr int kRecordBytes = kLatentRecordBytes;
 constexpr int kFinishSlots = 8;         // a row's finish, in tile-equivalents of work
 constexpr int kMergePieces = 4;         // pieces whose record loads a merge round issues together
@@ -177,7 +178,7 @@ struct RowState {
   float4_t o[2][kDimTiles];  // O^T[d][h]: dims 16 n + 4 kg + r of head h0 + 16 ht + col
   float m[2];                // reference max (log2 domain) of the lane's head
   float l[2];                // this lane's share of the head's sum of weights
-  bool overflow;             // a score exceeded the reference by kOverflowLog2
+  bool overflow;             // a lane's weights reached 2^kOverflowLog2 in a tile
 };
 
 // The B operand of the score product: head h0 + 16 ht + col, elements
@@ -294,8 +295,11 @@ __device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t 
 }
 
 // Folds a tile into the row state. kFirst: the segment's first tile, which
-// sets the reference max; otherwise a score above reference + kOverflowLog2
-// marks the segment.
+// sets the reference max. Otherwise a lane whose weights sum to 2^32 or more
+// (inf and NaN included) marks the segment: every score above
+// reference + kOverflowLog2 does, its weight alone rounding to at least
+// 2^32. The test is lane-local, so later tiles take no tile max at all
+// (its cross-lane steps sat between the two products).
 template <bool kFirst>
 __device__ __forceinline__ void fold_tile(const lds_char* tile, const bf16x8_t (&qf)[2][kQkSteps],
                                           RowState& st, int valid, float scale_log2, int col,
@@ -305,14 +309,13 @@ __device__ __forceinline__ void fold_tile(const lds_char* tile, const bf16x8_t (
   bf16x8_t pf[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const float mt = tile_max(x[ht]);
     if (kFirst) {
-      st.m[ht] = mt;
+      st.m[ht] = tile_max(x[ht]);
       st.l[ht] = 0.f;
-    } else {
-      st.overflow |= mt > st.m[ht] + kOverflowLog2;
     }
-    st.l[ht] += make_weights(x[ht], st.m[ht], pf[ht]);
+    const float ps = make_weights(x[ht], st.m[ht], pf[ht]);
+    if (!kFirst) st.overflow |= !(ps < kOverflowWeight);
+    st.l[ht] += ps;
   }
   value_tile<kFirst>(tile, pf, st.o, col, kg);
 }
