@@ -58,6 +58,7 @@ using lds_stream::raw_rsrc;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kHeads = kLatentHeads;
@@ -193,14 +194,11 @@ __device__ __forceinline__ void load_queries(const LatentArgs& a, int b, int h0,
       qf[ht][s] = *(const bf16x8_t*)(q + (size_t)ht * 16 * kLatent + s * 32);
 }
 
-// Scores of the tile, scaled to the log2 domain: x[ht][tt][r] for token
-// 16 tt + 4 kg + r and head h0 + 16 ht + col; -inf past the row's end (the
-// stage holds zeros there).
-__device__ __forceinline__ void score_tile(const lds_char* tile,
-                                           const bf16x8_t (&qf)[2][kQkSteps], int valid,
-                                           float scale_log2, int col, int kg,
-                                           float (&x)[2][2][4]) {
-  float4_t sc[2][2];
+// Raw scores of the tile: sc[tt][ht][r] = C[token 16 tt + 4 kg + r] .
+// q[head h0 + 16 ht + col].
+__device__ __forceinline__ void score_products(const lds_char* tile,
+                                               const bf16x8_t (&qf)[2][kQkSteps], int col,
+                                               int kg, float4_t (&sc)[2][2]) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -227,6 +225,17 @@ __device__ __forceinline__ void score_tile(const lds_char* tile,
     sc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qf[1][s], sc[1][1], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Scores of the tile, scaled to the log2 domain: x[ht][tt][r] for token
+// 16 tt + 4 kg + r and head h0 + 16 ht + col; -inf past the row's end (the
+// stage holds zeros there).
+__device__ __forceinline__ void score_tile(const lds_char* tile,
+                                           const bf16x8_t (&qf)[2][kQkSteps], int valid,
+                                           float scale_log2, int col, int kg,
+                                           float (&x)[2][2][4]) {
+  float4_t sc[2][2];
+  score_products(tile, qf, col, kg, sc);
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
@@ -246,20 +255,31 @@ __device__ __forceinline__ float tile_max(const float (&xh)[2][4]) {
   return max_over_kg(mx);
 }
 
-// Weights 2^(x - m) as bf16, the value product's B operand (k slot
-// 8 kg + 4 tt + r is token 16 tt + 4 kg + r); returns their sum, taken over
-// the rounded weights so that the normalisation matches the product.
-__device__ __forceinline__ float make_weights(const float (&xh)[2][4], float m, bf16x8_t& pf) {
-  float ps = 0.f;
+// Weights 2^e as bf16, the value product's B operand (k slot 8 kg + 4 tt + r
+// is token 16 tt + 4 kg + r); returns their sum, taken over the rounded
+// weights (bf16 dot products with ones) so that the normalisation matches
+// the product.
+__device__ __forceinline__ float weights(const float (&e)[2][4], bf16x8_t& pf) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const __bf16 p = (__bf16)fast_exp2(xh[tt][r] - m);
-      pf[4 * tt + r] = p;
-      ps += (float)p;
-    }
+    for (int r = 0; r < 4; ++r) pf[4 * tt + r] = (__bf16)fast_exp2(e[tt][r]);
+  const bf16x2_t* pp = (const bf16x2_t*)&pf;
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+  float ps = __builtin_amdgcn_fdot2_f32_bf16(pp[0], ones, 0.f, false);
+#pragma unroll
+  for (int q = 1; q < 4; ++q) ps = __builtin_amdgcn_fdot2_f32_bf16(pp[q], ones, ps, false);
   return ps;
+}
+
+// Weights 2^(x - m) of scaled scores x (see weights).
+__device__ __forceinline__ float make_weights(const float (&xh)[2][4], float m, bf16x8_t& pf) {
+  float e[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[tt][r] = xh[tt][r] - m;
+  return weights(e, pf);
 }
 
 // O^T += C^T P^T over the tile (kFirst: O^T = C^T P^T). The transposing
@@ -299,21 +319,45 @@ __device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t 
 // (inf and NaN included) marks the segment: every score above
 // reference + kOverflowLog2 does, its weight alone rounding to at least
 // 2^32. The test is lane-local, so later tiles take no tile max at all
-// (its cross-lane steps sat between the two products).
+// (its cross-lane steps sat between the two products); their exponents are
+// one fused multiply-add each, masked only in a row's partial last tile.
 template <bool kFirst>
 __device__ __forceinline__ void fold_tile(const lds_char* tile, const bf16x8_t (&qf)[2][kQkSteps],
                                           RowState& st, int valid, float scale_log2, int col,
                                           int kg) {
-  float x[2][2][4];
-  score_tile(tile, qf, valid, scale_log2, col, kg, x);
+  float4_t sc[2][2];
+  score_products(tile, qf, col, kg, sc);
   bf16x8_t pf[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
+    float e[2][4];
     if (kFirst) {
-      st.m[ht] = tile_max(x[ht]);
+      float x[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[tt][r] = 16 * tt + 4 * kg + r < valid ? sc[tt][ht][r] * scale_log2 : -INFINITY;
+      st.m[ht] = tile_max(x);
       st.l[ht] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[tt][r] = x[tt][r] - st.m[ht];
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[tt][r] = fmaf(sc[tt][ht][r], scale_log2, -st.m[ht]);
+      if (valid < kTileTokens) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * tt + 4 * kg + r >= valid) e[tt][r] = -INFINITY;
+      }
     }
-    const float ps = make_weights(x[ht], st.m[ht], pf[ht]);
+    const float ps = weights(e, pf[ht]);
     if (!kFirst) st.overflow |= !(ps < kOverflowWeight);
     st.l[ht] += ps;
   }
