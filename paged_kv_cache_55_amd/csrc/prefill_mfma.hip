@@ -72,6 +72,7 @@ constexpr float kFarBelow = 1e30f;           // -m before a column's first pair
 constexpr int kStages = 8;                  // LDS tile stages
 constexpr int kXcds = 8;                     // L2 domains of the chip
 constexpr int kAhead = 4;                    // tiles in flight beyond the pair being folded
+constexpr int kLoadWaves = 4;                // waves that issue the tile loads, one per SIMD
 static_assert(kAhead + 4 == kStages,
               "the pair being scored and the pair whose value product is pending stay in LDS");
 
@@ -90,8 +91,8 @@ struct Stage {
   static constexpr int kVBase = kKLoads * 1024;
   static constexpr int kLoads = kKLoads + kVLoads;
   static constexpr int kBytes = kLoads * 1024;
-  static constexpr int kFewest = kLoads / kWaves;  // loads of one tile a wave issues, at least
-  static constexpr int kMore = kLoads % kWaves;    // waves below this issue one more
+  static constexpr int kFewest = kLoads / kLoadWaves;  // loads of one tile a loading wave issues, at least
+  static constexpr int kMore = kLoads % kLoadWaves;    // waves below this issue one more
 };
 
 template <int D>
@@ -113,7 +114,7 @@ struct ColState {
 template <int D>
 struct TileLoads {
   using S = Stage<D>;
-  static constexpr int kPerWave = (S::kLoads + kWaves - 1) / kWaves;
+  static constexpr int kPerWave = (S::kLoads + kLoadWaves - 1) / kLoadWaves;
   int n;                // loads per tile (uniform)
   bool v[kPerWave];     // from the V^T rows (uniform)
   int off[kPerWave];    // this lane's byte offset within the tile's K or V^T rows
@@ -121,10 +122,10 @@ struct TileLoads {
     n = 0;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int k = wave + kWaves * i;
+      const int k = wave + kLoadWaves * i;
       v[i] = k >= S::kKLoads;
       off[i] = 0;
-      if (k >= S::kLoads) continue;
+      if (wave >= kLoadWaves || k >= S::kLoads) continue;
       n = i + 1;
       if (k < S::kKLoads) {
         const int slot = 64 * k + lane;
@@ -152,7 +153,7 @@ __device__ __forceinline__ void load_tile(const TileLoads<D>& tl, lds_char* stag
 #pragma unroll
   for (int i = 0; i < TileLoads<D>::kPerWave; ++i) {
     if (i >= tl.n) break;
-    lds_stream::global_load_to_lds(src[i] + toff, stage + 1024 * (wave + kWaves * i));
+    lds_stream::global_load_to_lds(src[i] + toff, stage + 1024 * (wave + kLoadWaves * i));
   }
 }
 
@@ -370,7 +371,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
   // the entries of the two tiles a refill issues are read one step before
   // it: waiting for a scalar load right after the barrier held up both the
   // refill and the fold
-  int32_t next_a = entry(kAhead), next_b = entry(kAhead + 1);
+  const bool loader = wave < kLoadWaves;  // the others issue no tile loads
+  int32_t next_a = 0, next_b = 0;
+  if (loader) {
+    next_a = entry(kAhead);
+    next_b = entry(kAhead + 1);
+  }
   // The padding tile that rounds an odd item up to whole pairs is never
   // loaded: its stage keeps older data (or none), and the masks, which
   // select, turn every score and value of tokens past L into -inf and 0.
@@ -390,6 +396,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
     lds_stream::workgroup_barrier();
     // refill the stages of pair p - 2 (every wave is past its value product):
     // tiles j and j + 1, j even, go to two consecutive stages
+    if (!loader) return;
     const int j = 2 * p + kAhead;
     lds_char* stage_j = stages + (j % kStages) * S::kBytes;
     const int32_t pa = next_a, pb = next_b;
@@ -402,8 +409,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
       issue(stage_j, j, pa);
     }
   };
-  for (int j = 0; j < kAhead && j < item_tiles; ++j)
-    issue(stages + j * S::kBytes, j, entry(j));
+  if (loader)
+    for (int j = 0; j < kAhead && j < item_tiles; ++j)
+      issue(stages + j * S::kBytes, j, entry(j));
   auto stage = [&](int j) -> const lds_char* { return stages + (j % kStages) * S::kBytes; };
   // Software pipeline: iteration p takes the scores of pair p, then the
   // value product of pair p - 1, whose probabilities are ready, then the
