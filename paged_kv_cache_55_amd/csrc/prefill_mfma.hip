@@ -72,7 +72,8 @@ constexpr float kFarBelow = 1e30f;           // -m before a column's first pair
 constexpr int kStages = 8;                  // LDS tile stages
 constexpr int kXcds = 8;                     // L2 domains of the chip
 constexpr int kAhead = 4;                    // tiles in flight beyond the pair being folded
-constexpr int kLoadWaves = 4;                // waves that issue the tile loads, one per SIMD
+constexpr int kLoadWaves = 2;                // waves that issue the tile loads (measured
+                                             // faster than one, four or eight)
 static_assert(kAhead + 4 == kStages,
               "the pair being scored and the pair whose value product is pending stay in LDS");
 
