@@ -80,6 +80,7 @@ constexpr int kAhead = kStages - 1;  // tiles in flight while one is folded
 static_assert(kAhead <= 3, "tile_barrier counts at most two younger tiles");
 constexpr int kWaveLoads = (kTileLoads + kWaves - 1) / kWaves;  // 10
 constexpr int kFewestLoads = kTileLoads / kWaves;               // 9
+static_assert(kWaveLoads <= kLatent / 32, "a wave's loads of a tile fit one per score step");
 constexpr int kQkSteps = kLatent / 32;  // 18 score steps
 constexpr int kDimTiles = kValue / 16;  // 32 output dim tiles
 constexpr int kOverflowLog2 = 32;  // weights up to 2^32 over the reference
@@ -125,24 +126,17 @@ __device__ __forceinline__ void next_tile(Cursor& c, const int* prefix) {
   c.n = __builtin_amdgcn_readfirstlane(prefix[b + 1] - prefix[b]);
 }
 
-// Issues this wave's share of the loads of tile c into `stage`: wave load k
+// This wave's share of the loads of tile c into `stage`: wave load k
 // (k = wave, wave + 4, ...) fills LDS bytes 1024 k .. 1024 k + 1023, lane l
 // the 16 bytes at 1024 k + 16 l, i.e. chunk ch of token t with
 // 78 t + ch = 64 k + l. Pad chunks (ch >= 72) and tokens past the row get
-// an offset past the descriptor's range, which loads zeros.
-__device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, lds_char* stage,
-                                          int wave, int lane) {
-  const int L = uniform_load(a.seq_lens, c.b);
-  const int valid = min(kTileTokens, L - c.j * kTileTokens);
-  const int page = uniform_load(a.block_tables, (size_t)c.b * a.max_blocks +
-                                                    (c.j / (kPageTokens / kTileTokens)));
-  const char* base =
-      (const char*)a.kv_pool +
-      ((size_t)page * kPageTokens + (size_t)(c.j % (kPageTokens / kTileTokens)) * kTileTokens) *
-          kTokenBytes;
-  const u32x4_t r = raw_rsrc(base, valid * kTokenBytes);
-#pragma unroll
-  for (int i = 0; i < kWaveLoads; ++i) {
+// an offset past the descriptor's range, which loads zeros. Prepared once
+// per tile; load(i) issues the wave's load i (nothing past kTileLoads).
+struct TileIssue {
+  u32x4_t r;
+  lds_char* stage;
+  int wave, lane;
+  __device__ __forceinline__ void load(int i) const {
     const int k = wave + kWaves * i;
     if (k < kTileLoads) {
       const int slot = 64 * k + lane;
@@ -152,6 +146,32 @@ __device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, 
       load_to_lds(r, stage + 1024 * k, off);
     }
   }
+};
+
+__device__ __forceinline__ TileIssue prepare_tile(const LatentArgs& a, const Cursor& c,
+                                                  lds_char* stage, int wave, int lane) {
+  const int L = uniform_load(a.seq_lens, c.b);
+  const int valid = min(kTileTokens, L - c.j * kTileTokens);
+  const int page = uniform_load(a.block_tables, (size_t)c.b * a.max_blocks +
+                                                    (c.j / (kPageTokens / kTileTokens)));
+  const char* base =
+      (const char*)a.kv_pool +
+      ((size_t)page * kPageTokens + (size_t)(c.j % (kPageTokens / kTileTokens)) * kTileTokens) *
+          kTokenBytes;
+  TileIssue t;
+  t.r = raw_rsrc(base, valid * kTokenBytes);
+  t.stage = stage;
+  t.wave = wave;
+  t.lane = lane;
+  return t;
+}
+
+// All of this wave's loads of tile c at once.
+__device__ __forceinline__ void load_tile(const LatentArgs& a, const Cursor& c, lds_char* stage,
+                                          int wave, int lane) {
+  const TileIssue t = prepare_tile(a, c, stage, wave, lane);
+#pragma unroll
+  for (int i = 0; i < kWaveLoads; ++i) t.load(i);
 }
 
 // Waits until this wave's loads of the current tile have landed in LDS (at
@@ -196,9 +216,12 @@ __device__ __forceinline__ void load_queries(const LatentArgs& a, int b, int h0,
 
 // Raw scores of the tile: sc[tt][ht][r] = C[token 16 tt + 4 kg + r] .
 // q[head h0 + 16 ht + col].
+// on_step(s) runs after the products of score step s (the tile refill's
+// loads go out there, one per step, among the matrix instructions).
+template <typename OnStep>
 __device__ __forceinline__ void score_products(const lds_char* tile,
                                                const bf16x8_t (&qf)[2][kQkSteps], int col,
-                                               int kg, float4_t (&sc)[2][2]) {
+                                               int kg, float4_t (&sc)[2][2], OnStep on_step) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -223,6 +246,7 @@ __device__ __forceinline__ void score_products(const lds_char* tile,
     sc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[s], qf[1][s], sc[0][1], 0, 0, 0);
     sc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qf[0][s], sc[1][0], 0, 0, 0);
     sc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[s], qf[1][s], sc[1][1], 0, 0, 0);
+    on_step(s);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -235,7 +259,7 @@ __device__ __forceinline__ void score_tile(const lds_char* tile,
                                            float scale_log2, int col, int kg,
                                            float (&x)[2][2][4]) {
   float4_t sc[2][2];
-  score_products(tile, qf, col, kg, sc);
+  score_products(tile, qf, col, kg, sc, [](int) {});
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
@@ -286,18 +310,31 @@ __device__ __forceinline__ float make_weights(const float (&xh)[2][4], float m, 
 // read gives lane (kg, col) dim 16 n + col of tokens 16 tt + 4 kg .. + 3
 // when lane 16 kg + 4 e + c4 addresses token 16 tt + 4 kg + e at dims
 // 16 n + 4 c4 .. + 3.
-template <bool kFirst>
-__device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t (&pf)[2],
-                                           float4_t (&o)[2][kDimTiles], int col, int kg) {
-  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
-  const lds_char* vrow = tile + (4 * kg + (col >> 2)) * kRowBytes + (col & 3) * 8;
-  // kVAhead steps of fragments in flight: a step is only two products
-  short4_t v0[kDimTiles], v1[kDimTiles];
+__device__ __forceinline__ const lds_char* value_row(const lds_char* tile, int col, int kg) {
+  return tile + (4 * kg + (col >> 2)) * kRowBytes + (col & 3) * 8;
+}
+
+// The value operand's first kVAhead steps of fragments (kVAhead steps stay
+// in flight: a step is only two products). Issued before the weights are
+// taken, their LDS latency passes under that vector work.
+__device__ __forceinline__ void value_prefetch(const lds_char* tile, int col, int kg,
+                                               short4_t (&v0)[kDimTiles],
+                                               short4_t (&v1)[kDimTiles]) {
+  const lds_char* vrow = value_row(tile, col, kg);
 #pragma unroll
   for (int n = 0; n < kVAhead; ++n) {
     v0[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + n * 32));
     v1[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vrow + 16 * kRowBytes + n * 32));
   }
+}
+
+template <bool kFirst>
+__device__ __forceinline__ void value_products(const lds_char* tile, const bf16x8_t (&pf)[2],
+                                               float4_t (&o)[2][kDimTiles], int col, int kg,
+                                               short4_t (&v0)[kDimTiles],
+                                               short4_t (&v1)[kDimTiles]) {
+  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const lds_char* vrow = value_row(tile, col, kg);
 #pragma unroll
   for (int n = 0; n < kDimTiles; ++n) {
     if (n + kVAhead < kDimTiles) {
@@ -314,6 +351,14 @@ __device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t 
   }
 }
 
+template <bool kFirst>
+__device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t (&pf)[2],
+                                           float4_t (&o)[2][kDimTiles], int col, int kg) {
+  short4_t v0[kDimTiles], v1[kDimTiles];
+  value_prefetch(tile, col, kg, v0, v1);
+  value_products<kFirst>(tile, pf, o, col, kg, v0, v1);
+}
+
 // Folds a tile into the row state. kFirst: the segment's first tile, which
 // sets the reference max. Otherwise a lane whose weights sum to 2^32 or more
 // (inf and NaN included) marks the segment: every score above
@@ -321,12 +366,14 @@ __device__ __forceinline__ void value_tile(const lds_char* tile, const bf16x8_t 
 // 2^32. The test is lane-local, so later tiles take no tile max at all
 // (its cross-lane steps sat between the two products); their exponents are
 // one fused multiply-add each, masked only in a row's partial last tile.
-template <bool kFirst>
+template <bool kFirst, typename OnStep>
 __device__ __forceinline__ void fold_tile(const lds_char* tile, const bf16x8_t (&qf)[2][kQkSteps],
                                           RowState& st, int valid, float scale_log2, int col,
-                                          int kg) {
+                                          int kg, OnStep on_step) {
   float4_t sc[2][2];
-  score_products(tile, qf, col, kg, sc);
+  score_products(tile, qf, col, kg, sc, on_step);
+  short4_t v0[kDimTiles], v1[kDimTiles];
+  value_prefetch(tile, col, kg, v0, v1);
   bf16x8_t pf[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
@@ -361,7 +408,7 @@ __device__ __forceinline__ void fold_tile(const lds_char* tile, const bf16x8_t (
     if (!kFirst) st.overflow |= !(ps < kOverflowWeight);
     st.l[ht] += ps;
   }
-  value_tile<kFirst>(tile, pf, st.o, col, kg);
+  value_products<kFirst>(tile, pf, st.o, col, kg, v0, v1);
 }
 
 // ---- finishing a row ----------------------------------------------------------
@@ -625,13 +672,20 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
           tile_barrier<1>();
         else
           tile_barrier<0>();
-        if (f + kAhead < f1) {
+        // the refill's loads go out one per score step
+        const bool refill = f + kAhead < f1;
+        TileIssue next;
+        if (refill) {
           next_tile(lc, prefix);
-          load_tile(a, lc, stages + ((f + kAhead - f0) % kStages) * kStageBytes, wave, lane);
+          next = prepare_tile(a, lc, stages + ((f + kAhead - f0) % kStages) * kStageBytes, wave,
+                              lane);
         }
         const int valid = min(kTileTokens, L - (cc.j + f - seg0) * kTileTokens);
         const lds_char* tile = stages + ((f - f0) % kStages) * kStageBytes;
-        fold_tile<decltype(first)::value>(tile, qf, st, valid, a.scale_log2, col, kg);
+        fold_tile<decltype(first)::value>(tile, qf, st, valid, a.scale_log2, col, kg,
+                                          [&](int s) {
+                                            if (refill && s < kWaveLoads) next.load(s);
+                                          });
         ++f;
       };
       // the first tile is peeled: it consumes the queries, so the
