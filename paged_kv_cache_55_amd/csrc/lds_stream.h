@@ -1,8 +1,9 @@
-// Streaming tiles from HBM into LDS with buffer loads that carry an LDS
-// destination (gfx950 buffer_load_dwordx4 ... lds): lane l of a wave load
-// writes 16 bytes at M0 + 16 l, from any byte offset of a buffer descriptor
-// (offsets past the descriptor's range load zeros). Shared by the kernels
-// whose workgroups share each tile among their waves.
+// Streaming tiles from HBM into LDS with loads that carry an LDS destination
+// (gfx950 buffer_load_dwordx4 ... lds and global_load_lds_dwordx4): lane l
+// of a wave load writes 16 bytes at M0 + 16 l. The buffer form reads any
+// byte offset of a descriptor (offsets past its range load zeros); the
+// global form reads one address per lane. Shared by the kernels whose
+// workgroups share each tile among their waves.
 #pragma once
 
 #include "device_common.h"
@@ -23,43 +24,31 @@ __device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
 }
 
 // 16 bytes per lane from the buffer at byte offset `off` into LDS at
-// `dst` + 16 * lane (buffer_load_dwordx4 with the LDS destination in M0).
-// kStream: non-temporal cache policy, for data read once; without it the
-// lines stay in L2 for other workgroups that read the same tile. Written as
+// `dst` + 16 * lane (buffer_load_dwordx4 with the LDS destination in M0),
+// with the non-temporal cache policy: for data read once. Written as
 // assembly so that the compiler does not track these LDS writes: it cannot
 // tell the stages apart and would otherwise make every later LDS read wait
 // for all of them, the prefetch included. Completion is awaited explicitly
 // (tile_barrier). M0 belongs to the compiler, so the sequence restores it.
-template <bool kStream = true>
 __device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   uint32_t saved;
-  if (kStream)
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(m0), "v"(off), "s"(rsrc)
-        : "memory");
-  else
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(m0), "v"(off), "s"(rsrc)
-        : "memory");
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(off), "s"(rsrc)
+      : "memory");
 }
 
 // 16 bytes per lane from the global address `src` (one per lane) into LDS
-// at `dst` + 16 * lane (global_load_lds_dwordx4), default cache policy.
-// The same conventions as load_to_lds: untracked by the compiler, awaited
-// with wait_loads / tile_barrier, M0 restored.
+// at `dst` + 16 * lane (global_load_lds_dwordx4), default cache policy: the
+// lines stay in L2 for other workgroups that read the same tile. The same
+// conventions as load_to_lds: untracked by the compiler, awaited with
+// wait_loads / tile_barrier, M0 restored.
 __device__ __forceinline__ void global_load_to_lds(const void* src, lds_char* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   uint32_t saved;
