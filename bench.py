@@ -58,6 +58,8 @@ KERNEL_SRC = {
     "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
     "latent": ["latent_mfma.hip", "lds_stream.h", "mfma_tile.h", "device_common.h", "worklist.h",
                "launch.h"],
+    "prefill": ["prefill_mfma.hip", "lds_stream.h", "mfma_tile.h", "device_common.h", "worklist.h",
+                "launch.h"],
 }
 
 
@@ -363,13 +365,17 @@ def main():
     prefill_flops = None
     if args.config == 6:  # QK and PV: 2 D flops each per (query head, key) pair
         qs = case.query_start.numpy()
+        # bytes: every row's K/V once, the chunk rows' queries read and
+        # outputs written, tables, lengths and row starts
+        per_call_alg = (kv_bytes / layers + 2 * int(qs[-1]) * Hq * D * 2 + table_bytes
+                        + 4 * B + 4 * (B + 1))
         prefill_flops = 0
         for s_i, L in enumerate(lens_host.tolist()):
             n = int(qs[s_i + 1] - qs[s_i])
             keys = n * (L - n) + n * (n + 1) // 2  # sum over chunk rows of (p + 1)
             prefill_flops += 4 * Hq * D * keys
         achieved = prefill_flops / mean_call_s / 1e12
-        traffic = None
+        traffic = load_traffic("prefill", workload)
     mfma_share = None
     if latent_flops is not None:
         mfma_share = {"achieved_tflops": round(latent_flops / mean_call_s / 1e12, 1),
