@@ -72,8 +72,9 @@ constexpr float kFarBelow = 1e30f;           // -m before a column's first pair
 constexpr int kStages = 8;                  // LDS tile stages
 constexpr int kXcds = 8;                     // L2 domains of the chip
 constexpr int kAhead = 4;                    // tiles in flight beyond the pair being folded
-constexpr int kLoadWaves = 2;                // waves that issue the tile loads (measured
-                                             // faster than one, four or eight)
+constexpr int kTileLoaders = 2;              // waves that load one tile
+constexpr int kLoadWaves = 2 * kTileLoaders; // loaders of a pair's even and of its odd tile
+static_assert(kAhead % 2 == 0, "each loader refills one tile of every pair");
 static_assert(kAhead + 4 == kStages,
               "the pair being scored and the pair whose value product is pending stay in LDS");
 
@@ -92,8 +93,8 @@ struct Stage {
   static constexpr int kVBase = kKLoads * 1024;
   static constexpr int kLoads = kKLoads + kVLoads;
   static constexpr int kBytes = kLoads * 1024;
-  static constexpr int kFewest = kLoads / kLoadWaves;  // loads of one tile a loading wave issues, at least
-  static constexpr int kMore = kLoads % kLoadWaves;    // waves below this issue one more
+  static constexpr int kFewest = kLoads / kTileLoaders;  // loads of one tile a loader issues, at least
+  static constexpr int kMore = kLoads % kTileLoaders;    // loaders below this issue one more
 };
 
 template <int D>
@@ -115,7 +116,7 @@ struct ColState {
 template <int D>
 struct TileLoads {
   using S = Stage<D>;
-  static constexpr int kPerWave = (S::kLoads + kLoadWaves - 1) / kLoadWaves;
+  static constexpr int kPerWave = (S::kLoads + kTileLoaders - 1) / kTileLoaders;
   int n;                // loads per tile (uniform)
   bool v[kPerWave];     // from the V^T rows (uniform)
   int off[kPerWave];    // this lane's byte offset within the tile's K or V^T rows
@@ -123,7 +124,7 @@ struct TileLoads {
     n = 0;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int k = wave + kLoadWaves * i;
+      const int k = wave % kTileLoaders + kTileLoaders * i;
       v[i] = k >= S::kKLoads;
       off[i] = 0;
       if (wave >= kLoadWaves || k >= S::kLoads) continue;
@@ -154,7 +155,8 @@ __device__ __forceinline__ void load_tile(const TileLoads<D>& tl, lds_char* stag
 #pragma unroll
   for (int i = 0; i < TileLoads<D>::kPerWave; ++i) {
     if (i >= tl.n) break;
-    lds_stream::global_load_to_lds(src[i] + toff, stage + 1024 * (wave + kLoadWaves * i));
+    lds_stream::global_load_to_lds(src[i] + toff,
+                                   stage + 1024 * (wave % kTileLoaders + kTileLoaders * i));
   }
 }
 
@@ -372,46 +374,39 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
   // the entries of the two tiles a refill issues are read one step before
   // it: waiting for a scalar load right after the barrier held up both the
   // refill and the fold
-  const bool loader = wave < kLoadWaves;  // the others issue no tile loads
-  int32_t next_a = 0, next_b = 0;
-  if (loader) {
-    next_a = entry(kAhead);
-    next_b = entry(kAhead + 1);
-  }
+  // waves 0, 1 load the even tiles, waves 2, 3 the odd ones (one per SIMD
+  // and pair); the others issue no tile loads
+  const bool loader = wave < kLoadWaves;
+  const int parity = wave / kTileLoaders;
+  int32_t next = 0;
+  if (loader) next = entry(kAhead + parity);
   // The padding tile that rounds an odd item up to whole pairs is never
   // loaded: its stage keeps older data (or none), and the masks, which
   // select, turn every score and value of tokens past L into -inf and 0.
   auto advance = [&](int p) {  // pair p is in LDS for every wave; refill
     // tiles 2p, 2p + 1 landed: the loads of the kAhead - 2 tiles issued
     // after them may still be in flight while all of them are real tiles
-    // (this wave's own count of them); else nothing may. Where every wave
-    // issues loads, the waves with one more per tile wait as the others do,
-    // for part of the next tile too: safe, and measured faster than
-    // branching on the wave.
+    // (a loader's own count of them: half those tiles, its parity's);
+    // else nothing may. The loader with one more load per tile waits as
+    // the other does, for part of the next tile too: safe, and measured
+    // faster than branching on the wave.
     if (2 * p + kAhead > item_tiles)
       lds_stream::wait_loads<0>();
     else if (S::kFewest == 0 && wave < S::kMore)
-      lds_stream::wait_loads<(S::kFewest + 1) * (kAhead - 2)>();
+      lds_stream::wait_loads<(S::kFewest + 1) * (kAhead - 2) / 2>();
     else
-      lds_stream::wait_loads<S::kFewest * (kAhead - 2)>();
+      lds_stream::wait_loads<S::kFewest * (kAhead - 2) / 2>();
     lds_stream::workgroup_barrier();
-    // refill the stages of pair p - 2 (every wave is past its value product):
-    // tiles j and j + 1, j even, go to two consecutive stages
+    // refill the stage of this loader's tile of pair p + kAhead / 2 (every
+    // wave is past the value product of pair p - 2, which held it)
     if (!loader) return;
-    const int j = 2 * p + kAhead;
-    lds_char* stage_j = stages + (j % kStages) * S::kBytes;
-    const int32_t pa = next_a, pb = next_b;
-    next_a = entry(j + 2);
-    next_b = entry(j + 3);
-    if (j + 1 < item_tiles) {
-      issue(stage_j, j, pa);
-      issue(stage_j + S::kBytes, j + 1, pb);
-    } else if (j < item_tiles) {
-      issue(stage_j, j, pa);
-    }
+    const int j = 2 * p + kAhead + parity;
+    const int32_t pj = next;
+    next = entry(j + 2);
+    if (j < item_tiles) issue(stages + (j % kStages) * S::kBytes, j, pj);
   };
   if (loader)
-    for (int j = 0; j < kAhead && j < item_tiles; ++j)
+    for (int j = parity; j < kAhead && j < item_tiles; j += 2)
       issue(stages + j * S::kBytes, j, entry(j));
   auto stage = [&](int j) -> const lds_char* { return stages + (j % kStages) * S::kBytes; };
   // Software pipeline: iteration p takes the scores of pair p, then the
