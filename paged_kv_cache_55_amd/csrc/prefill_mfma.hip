@@ -104,8 +104,9 @@ struct ColState {
   float l;               // this lane's share of the column's sum
 };
 
-// This wave's share of a tile's loads, fixed for the kernel: load
-// k = wave + kWaves i (i < n) fills bytes 1024 k .. + 1023 of a stage, lane
+// A loading wave's share of its tiles' loads, fixed for the kernel: load
+// k = wave % kTileLoaders + kTileLoaders i (i < n; n = 0 for the waves that
+// load nothing) fills bytes 1024 k .. + 1023 of a stage, lane
 // l the 16 bytes at 1024 k + 16 l, taken from the tile's K rows (16 x D,
 // contiguous) for k < kKLoads, else from its V^T rows (D x 16, contiguous),
 // at byte offset off[i]. Lanes whose 16 bytes are stage padding (the pad of
