@@ -267,12 +267,14 @@ __device__ __forceinline__ void pair_softmax(const float4_t (&s0)[kColTiles],
 }
 
 // The value product of the pair in stages a, b (first token tok0) with its
-// probabilities pf. kMasked: V^T slots past L, which may hold anything (NaN
-// included), are zeroed.
+// probabilities pf. kMasked: V^T slots of tokens at or past `limit` (the
+// first token no column of the wave sees: past L, or past the wave's last
+// position), which may hold anything (NaN included, and a stage's older
+// data), are zeroed; their weights are 0, and 0 * NaN would not be.
 template <int D, bool kMasked>
 __device__ __forceinline__ void pair_values(const lds_char* sa, const lds_char* sb,
                                             const bf16x8_t (&pf)[kColTiles],
-                                            ColState<D> (&st)[kColTiles], int tok0, int L,
+                                            ColState<D> (&st)[kColTiles], int tok0, int limit,
                                             int row, int kg) {
   using S = Stage<D>;
   constexpr int NDT = D / 16;
@@ -283,7 +285,7 @@ __device__ __forceinline__ void pair_values(const lds_char* sa, const lds_char* 
   uint32_t vm[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    vm[q] = (t8 + 2 * q < L ? 0x0000ffffu : 0u) | (t8 + 2 * q + 1 < L ? 0xffff0000u : 0u);
+    vm[q] = (t8 + 2 * q < limit ? 0x0000ffffu : 0u) | (t8 + 2 * q + 1 < limit ? 0xffff0000u : 0u);
 #pragma unroll
   for (int n = 0; n < NDT; ++n) {
     u32x4_t v = *(lds_u32x4*)(vt + 16 * n * S::kVRow);
@@ -333,7 +335,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
     for (int k = 0; k < NQK; ++k) qb[ct][k] = *(const bf16x8_t*)(qp + k * 32 + kg * 8);
   }
   // tiles this wave folds, and the item's (the last active wave's)
-  const int wave_tiles = (p0 + min(c0 + kCols - 1, ncols - 1) / G) / kTile + 1;
+  const int pos_max = p0 + min(c0 + kCols - 1, ncols - 1) / G;  // no column sits after it
+  const int wave_tiles = pos_max / kTile + 1;
+  const int vlimit = min(L, pos_max + 1);  // tokens from here on have weight 0 in every column
   const int item_tiles = (p0 + min(grp * kItemCols + kItemCols - 1, ncols - 1) / G) / kTile + 1;
   const int pairs = (item_tiles + 1) / 2;
 
@@ -382,8 +386,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
   int32_t next = 0;
   if (loader) next = entry(kAhead + parity);
   // The padding tile that rounds an odd item up to whole pairs is never
-  // loaded: its stage keeps older data (or none), and the masks, which
-  // select, turn every score and value of tokens past L into -inf and 0.
+  // loaded: its stage keeps older data (or none). Its tokens lie past every
+  // column's position, so the masks, which select, turn their scores into
+  // -inf and their values into 0 (values by the wave's limit, not by L: an
+  // item that ends before its sequence has such tokens below L).
   auto advance = [&](int p) {  // pair p is in LDS for every wave; refill
     // tiles 2p, 2p + 1 landed: the loads of the kAhead - 2 tiles issued
     // after them may still be in flight while all of them are real tiles
@@ -430,7 +436,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
       advance(p);
       pair_scores<D, false>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
                             s1);
-      pair_values<D, false>(stage(2 * p - 2), stage(2 * p - 1), pf, st, (2 * p - 2) * kTile, L,
+      pair_values<D, false>(stage(2 * p - 2), stage(2 * p - 1), pf, st, (2 * p - 2) * kTile, vlimit,
                             row, kg);
       pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
     }
@@ -445,7 +451,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
                            s1);
     if (pending >= 0)
       pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st,
-                           2 * pending * kTile, L, row, kg);
+                           2 * pending * kTile, vlimit, row, kg);
     pending = -1;
     if (fold) {
       pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
@@ -454,7 +460,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
   }
   if (pending >= 0)
     pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st, 2 * pending * kTile,
-                         L, row, kg);
+                         vlimit, row, kg);
   lds_barrier();  // every wave is done with the stages before the next item
 
   if (!active) return;

@@ -46,6 +46,15 @@ def test_prefill_small(chunks, contexts, hq, hkv, d):
     check(c)
 
 
+def test_prefill_item_ending_before_its_sequence():
+    """A 216-token chunk after 2 cached tokens, 64-token blocks: the first
+    column block's items end before the sequence does and have an odd tile
+    count. The padding tile that completes their last pair is not loaded;
+    its stage's older contents (here once a poisoned tail slot) must be
+    masked by the wave's last position, not only by L."""
+    check(wl.prefill_case(5507, [216], [2], 32, 8, 128, block_size=64))
+
+
 @pytest.mark.parametrize("bs", [64, 256])
 def test_prefill_block_sizes(bs):
     c = wl.prefill_case(950 + bs, [100, 3, 250], [60, 700, 1], 32, 8, 128, block_size=bs)
