@@ -233,8 +233,8 @@ typedef struct {
 
 /* Bytes of device workspace pa_latent_decode needs: control counters, per
  * row a description of its pieces and an overflow flag, then partial
- * records (each piece's output normalised by its own sum, as bf16, and its
- * fp32 max and sum for 128 heads) for two pieces per workgroup of a grid
+ * records (each piece's output normalised by its own sum, and its max and
+ * sum, all fp32, for 128 heads) for two pieces per workgroup of a grid
  * of at most 256. Zero-fill it before its first use; every call leaves it
  * reusable. Calls that may overlap in time need separate workspaces.
  * Returns 0 for invalid dims (pa_latent_decode reports those). */

@@ -87,7 +87,7 @@ constexpr int kOverflowLog2 = 32;  // weights up to 2^32 over the reference
 constexpr float kOverflowWeight = (float)(1ull << kOverflowLog2);
 constexpr int kRecordBytes = kLatentRecordBytes;
 constexpr int kFinishSlots = 8;         // a row's finish, in tile-equivalents of work
-constexpr int kMergePieces = 4;         // pieces whose record loads a merge round issues together
+constexpr int kMergePieces = 2;         // pieces whose record loads a merge round issues together
 constexpr int kFewPieces = 8;           // rows of at most this many pieces: (m, l) in registers
 #ifndef LATENT_K_AHEAD
 #define LATENT_K_AHEAD 2
@@ -432,32 +432,30 @@ __device__ __forceinline__ void store_scaled(const LatentArgs& a, const float4_t
   }
 }
 
-// Record of a piece: x[h][d] = bf16(O / l), then m[H], then l[H] (fp32).
+// Record of a piece: x[h][d] = O / l, then m[H], then l[H], all fp32 (a bf16
+// x added its rounding to the output's in rows merged from partly
+// cancelling pieces).
 __device__ __forceinline__ int record_base(int slot) { return slot * kRecordBytes; }
 __device__ __forceinline__ int record_x(int slot, int h, int d) {
-  return record_base(slot) + (h * kValue + d) * 2;
+  return record_base(slot) + (h * kValue + d) * 4;
 }
 __device__ __forceinline__ int record_m(int slot, int h) {
-  return record_base(slot) + kHeads * kValue * 2 + h * 4;
+  return record_base(slot) + kHeads * kValue * 4 + h * 4;
 }
 __device__ __forceinline__ int record_l(int slot, int h) {
-  return record_base(slot) + kHeads * kValue * 2 + kHeads * 4 + h * 4;
+  return record_base(slot) + kHeads * kValue * 4 + kHeads * 4 + h * 4;
 }
 
-__device__ __forceinline__ void store_rec8(__amdgpu_buffer_rsrc_t rec, int off, uint2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rec, off, 0, 0);
+__device__ __forceinline__ void store_rec16(__amdgpu_buffer_rsrc_t rec, int off, float4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rec, off, 0, 0);
 }
 __device__ __forceinline__ void store_rec(__amdgpu_buffer_rsrc_t rec, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rec, off, 0, 0);
 }
 
-// A piece's normalised output chunk (4 dims of one head) as 4 bf16: what
-// its record holds, computed the same way for a piece kept in registers.
-__device__ __forceinline__ uint2 normalised_chunk(float4_t o, float inv) {
-  const float4_t v = o * inv;
-  return make_uint2(pack_bf16x2(bf16_rne(v[0]), bf16_rne(v[1])),
-                    pack_bf16x2(bf16_rne(v[2]), bf16_rne(v[3])));
-}
+// A piece's normalised output chunk (4 dims of one head): what its record
+// holds.
+__device__ __forceinline__ float4_t normalised_chunk(float4_t o, float inv) { return o * inv; }
 
 __device__ __forceinline__ float4_t zero4() { return (float4_t){0.f, 0.f, 0.f, 0.f}; }
 
@@ -468,9 +466,6 @@ __device__ __forceinline__ float4_t fma4(float4_t x, float w, float4_t acc) {
                     __builtin_fmaf(x[2], w, acc[2]), __builtin_fmaf(x[3], w, acc[3])};
 }
 
-__device__ __forceinline__ float4_t widen(uint2 x) {
-  return (float4_t){bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
-}
 
 __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slot,
                                              const RowState& st, const float (&ltot)[2], int h0,
@@ -481,7 +476,7 @@ __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slo
     const float inv = 1.f / ltot[ht];
 #pragma unroll
     for (int n = 0; n < kDimTiles; ++n)
-      store_rec8(rec, record_x(slot, h, 16 * n + 4 * kg), normalised_chunk(st.o[ht][n], inv));
+      store_rec16(rec, record_x(slot, h, 16 * n + 4 * kg), normalised_chunk(st.o[ht][n], inv));
     if (kg == 0) {
       store_rec(rec, record_m(slot, h), st.m[ht]);
       store_rec(rec, record_l(slot, h), ltot[ht]);
@@ -785,7 +780,7 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   for (int j = 0; j < 8; ++j) acc[j][0] = acc[j][1] = zero4();
   for (int i0 = 0; i0 < n; i0 += kMergePieces) {
     float w[kMergePieces];
-    uint4 x[kMergePieces][8];
+    float4_t x[kMergePieces][8][2];
 #pragma unroll
     for (int k = 0; k < kMergePieces; ++k) {
       if (i0 + k >= n) break;
@@ -801,16 +796,19 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        x[k][j] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(rec, record_x(sl, h, 64 * j + d0), 0, 0));
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          x[k][j][e] = __builtin_bit_cast(
+              float4_t,
+              __builtin_amdgcn_raw_buffer_load_b128(rec, record_x(sl, h, 64 * j + d0 + 4 * e), 0, 0));
     }
 #pragma unroll
     for (int k = 0; k < kMergePieces; ++k) {
       if (i0 + k >= n) break;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        acc[j][0] = fma4(widen(make_uint2(x[k][j].x, x[k][j].y)), w[k], acc[j][0]);
-        acc[j][1] = fma4(widen(make_uint2(x[k][j].z, x[k][j].w)), w[k], acc[j][1]);
+        acc[j][0] = fma4(x[k][j][0], w[k], acc[j][0]);
+        acc[j][1] = fma4(x[k][j][1], w[k], acc[j][1]);
       }
     }
   }

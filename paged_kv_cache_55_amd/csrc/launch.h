@@ -67,7 +67,7 @@ constexpr int kLatentStageBytes = 39 * 1024;
 constexpr int kLatentStages = 3;
 // record of one piece of a cut row: its output normalised by its own sum as
 // bf16 [H][512], then fp32 max m[H] and sum l[H]
-constexpr int kLatentRecordBytes = kLatentHeads * kLatentValueDim * 2 + 2 * kLatentHeads * 4;
+constexpr int kLatentRecordBytes = kLatentHeads * kLatentValueDim * 4 + 2 * kLatentHeads * 4;
 const void* latent_decode_fn();
 size_t latent_decode_smem(int num_seqs);
 hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t s);
