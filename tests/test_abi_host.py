@@ -243,7 +243,7 @@ def latent_dims(**kw):
 def test_latent_workspace_size(lib):
     align = lambda x: (x + 255) // 256 * 256
     B = 256
-    rec = 128 * 512 * 2 + 2 * 128 * 4  # bf16 normalised output, fp32 max and sum
+    rec = 128 * 512 * 4 + 2 * 128 * 4  # normalised output, max and sum, all fp32
     off_flag = align(256 + 2 * B * 4)
     off_rec = align(off_flag + B * 4)
     assert pk.pa_latent_workspace_bytes(latent_dims()) == off_rec + 2 * 256 * rec
