@@ -231,12 +231,12 @@ typedef struct {
   int32_t dtype;              /* pa_dtype; PA_BF16 */
 } pa_latent_dims;
 
-/* Bytes of device workspace pa_latent_decode needs: control counters, per
- * row a description of its pieces and an overflow flag, then partial
+/* Bytes of device workspace pa_latent_decode needs: per row a description
+ * of its pieces, then partial
  * records (each piece's output normalised by its own sum, and its max and
  * sum, all fp32, for 128 heads) for two pieces per workgroup of a grid
- * of at most 256. Zero-fill it before its first use; every call leaves it
- * reusable. Calls that may overlap in time need separate workspaces.
+ * of at most 256. Every call writes what it reads back (no zero-fill
+ * needed). Calls that may overlap in time need separate workspaces.
  * Returns 0 for invalid dims (pa_latent_decode reports those). */
 size_t pa_latent_workspace_bytes(const pa_latent_dims* dims);
 
@@ -247,10 +247,13 @@ size_t pa_latent_workspace_bytes(const pa_latent_dims* dims);
  * bf16). A persistent grid streams equal shares of all 32-token tiles
  * (each row's finish counted as a few tiles); the pieces of a row split
  * across workgroups are merged by a second kernel on the same stream
- * (log-sum-exp over the pieces' bf16-rounded normalised outputs, in piece
- * order), so results do not depend on timing.
- * A row whose scores rise more than 2^32 above a piece's first-tile maximum
- * is recomputed exactly (two passes) at the end of the call. Slots at or
+ * (log-sum-exp over the pieces' fp32 normalised outputs, in piece order),
+ * so results do not depend on timing.
+ * A piece of a row in which some weight 2^(s - m) reaches 2^32, m being the
+ * piece's first-tile maximum of the log2-scaled scores s, is recomputed
+ * exactly (two passes, with the piece's true maximum) by its workgroup after
+ * that workgroup's share of the stream, and written then instead of the
+ * overflowed result. Slots at or
  * past seq_lens[b] never reach the result; bf16 output is rounded to
  * nearest even. PA_ERR_UNSUPPORTED for any shape but H = 128, 576 / 512,
  * BS = 64, bf16. */

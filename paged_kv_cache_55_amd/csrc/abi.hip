@@ -269,7 +269,7 @@ constexpr int kMaxLatentGrid = 256;
 constexpr int kLatentMinTiles = 8;
 
 struct LatentPlan {
-  size_t off_ctl, off_cnt, off_flag, off_rec, ws_bytes;
+  size_t off_cnt, off_rec, ws_bytes;
 };
 
 pa_status plan_latent(const pa_latent_dims* d, LatentPlan* p) {
@@ -284,10 +284,8 @@ pa_status plan_latent(const pa_latent_dims* d, LatentPlan* p) {
     return PA_ERR_UNSUPPORTED;
   if (d->num_seqs > kMaxSeqs || d->max_blocks_per_seq > (1 << 20)) return PA_ERR_UNSUPPORTED;
   const size_t B = (size_t)d->num_seqs;
-  p->off_ctl = 0;
-  p->off_cnt = kAlign;
-  p->off_flag = align_up(p->off_cnt + 2 * B * sizeof(int));
-  p->off_rec = align_up(p->off_flag + B * sizeof(int));
+  p->off_cnt = 0;
+  p->off_rec = align_up(2 * B * sizeof(int));
   p->ws_bytes = p->off_rec + (size_t)2 * kMaxLatentGrid * kLatentRecordBytes;
   return PA_OK;
 }
@@ -329,8 +327,6 @@ pa_status pa_latent_decode(const void* q, const void* kv_pool, const int32_t* bl
   a.out = out;
   a.ws_rec = (float*)(ws + plan.off_rec);
   a.ws_cnt = (int*)(ws + plan.off_cnt);
-  a.ws_flag = (int*)(ws + plan.off_flag);
-  a.ws_ctl = (int*)(ws + plan.off_ctl);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = dims->num_seqs;
   a.max_blocks = dims->max_blocks_per_seq;

@@ -185,15 +185,12 @@ struct LatentArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;                   // [B, H, 512]
-  // cut rows: records of two piece slots per workgroup (bf16 O[h][d]
-  // normalised by the piece's sum, then fp32 m[H] and l[H]); per row its
-  // pieces (first slot, count; written by every call for rows with tokens)
-  // and an overflow flag; two control counters (workgroups finished,
-  // segments flagged). The flags and counters are zero between calls.
+  // cut rows: records of two piece slots per workgroup (fp32 O[h][d]
+  // normalised by the piece's sum, then fp32 m[H] and l[H]) and per row a
+  // description of its pieces (first slot, count), written by every call
+  // for the rows with tokens
   void* ws_rec;
   int* ws_cnt;   // [B][2]
-  int* ws_flag;  // [B]
-  int* ws_ctl;   // [2]
   float scale_log2;
   int num_seqs, max_blocks;
   int grid;       // workgroups of the launch

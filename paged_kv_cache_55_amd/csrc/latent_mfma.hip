@@ -34,8 +34,8 @@
 // unit), equal in cost: a row's tiles plus kFinishSlots tiles' worth for
 // writing it, so that workgroups with many short rows take fewer tiles. A
 // row cut by range boundaries leaves one record per piece (its output
-// normalised by the piece's sum as bf16, max and sum as fp32: 129 KiB, as
-// much as 115 tokens of latent cache) and a description of its pieces; a
+// normalised by the piece's sum, its max and its sum, all fp32: 257 KiB, as
+// much as 228 tokens of latent cache) and a description of its pieces; a
 // second kernel merges each cut row in parallel over its heads. No
 // workgroup waits for another, and no merge sits at the end of a range.
 #include <type_traits>
@@ -192,7 +192,7 @@ using lds_stream::lds_barrier;
 // first tile starts the accumulator from zero (a zero C operand) and fixes
 // the segment's reference max (its tile max); later weights are
 // 2^(s - reference), which stays far from overflow unless a score exceeds
-// the reference by more than kOverflowLog2 (then the row is flagged and
+// the reference by more than kOverflowLog2 (then the segment is flagged and
 // recomputed exactly by the slow path below).
 
 struct RowState {
@@ -484,38 +484,58 @@ __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slo
   }
 }
 
-// Slot of piece i (0 .. n - 1) of a row cut over workgroups v0 .. v0 + n - 1.
-// A finished segment (flat tiles seg0 .. seg1 - 1 of row c.b). A whole row
-// is written; a piece of a cut row is written as a record, in slot
-// 2 w of workgroup w for its range's first segment and 2 w + 1 for its
-// last, for the merge kernel. The workgroup holding the row's first tile
-// also describes the row's pieces: its first slot and their number
-// (workgroups floor(x / T) over the row's tiles' cost positions x). A
-// segment marked for overflow flags its row for the slow path. The
+// Writes a finished segment (flat tiles seg0 .. seg1 - 1 of row c.b): a
+// whole row to `out`, a piece of a cut row as a record, in slot 2 w of
+// workgroup w for its range's first segment and 2 w + 1 for its last, for
+// the merge kernel.
+__device__ __forceinline__ void write_segment(const LatentArgs& a, int b, const RowState& st,
+                                              int seg0, int seg1, int row0, int row1, int f0,
+                                              __amdgpu_buffer_rsrc_t rec, int h0, int col,
+                                              int kg) {
+  const float ltot[2] = {sum_over_kg(st.l[0]), sum_over_kg(st.l[1])};
+  if (seg0 == row0 && seg1 == row1) {
+    const float inv[2] = {1.f / ltot[0], 1.f / ltot[1]};
+    store_scaled(a, st.o, inv, b, h0, col, kg);
+    return;
+  }
+  write_record(rec, 2 * (int)blockIdx.x + (seg0 == f0 ? 0 : 1), st, ltot, h0, col, kg);
+}
+
+// A finished segment of row c.b. The workgroup holding the row's first tile
+// describes the row's pieces: its first slot and their number (workgroups
+// floor(x / T) over the row's tiles' cost positions x). A segment in which
+// some lane's weights outran the reference is not written: the workgroup
+// marks its row in the LDS set `redo` and, after its stream, recomputes this
+// same segment exactly and writes it then (the segment's only write). The
 // protocol is workgroup-uniform.
+//
+// The per-wave overflow votes in bcast[1 + wave] carry the segment's tag
+// (seg0 + 1, unique within the launch), so they need no reset: between two
+// finishes every wave passes the barrier of at least one tile.
+//
+// The order here (the sums first, the writes last and each one guarded)
+// keeps the streaming loop's registers as they are: other arrangements of
+// the same steps made the compiler move the tile loads' lane offsets to
+// scratch, and the reloads' waits drained the tile prefetch (twice the
+// call time).
 __device__ __forceinline__ void finish_segment(const LatentArgs& a, const Cursor& c,
                                                const RowState& st, int seg0, int seg1, int f0,
                                                int T, const int* prefix, const int* cprefix,
-                                               __amdgpu_buffer_rsrc_t rec, int* bcast, int wave,
-                                               int h0, int col, int kg) {
+                                               __amdgpu_buffer_rsrc_t rec, int* bcast,
+                                               unsigned* redo, int wave, int h0, int col,
+                                               int kg) {
   const float ltot[2] = {sum_over_kg(st.l[0]), sum_over_kg(st.l[1])};
-  // overflow anywhere in the workgroup flags the row
-  if (__builtin_amdgcn_ballot_w64(st.overflow) != 0 && (threadIdx.x & 63) == 0) bcast[1 + wave] = 1;
+  const int tag = seg0 + 1;
+  if (__builtin_amdgcn_ballot_w64(st.overflow) != 0 && (threadIdx.x & 63) == 0)
+    bcast[1 + wave] = tag;
   lds_barrier();
-  if (threadIdx.x == 0) {
-    int any = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      any |= bcast[1 + w];
-      bcast[1 + w] = 0;
-    }
-    if (any) {
-      __hip_atomic_store(a.ws_flag + c.b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(a.ws_ctl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  bool flagged = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) flagged |= bcast[1 + w] == tag;
+  if (flagged && threadIdx.x == 0) redo[c.b >> 5] |= 1u << (c.b & 31);
   const int row0 = prefix[c.b];
   const int row1 = prefix[c.b + 1];
-  if (seg0 == row0 && threadIdx.x == 0) {  // device-scope: the slow path may overwrite
+  if (seg0 == row0 && threadIdx.x == 0) {
     const int v1 = (cprefix[c.b] + (row1 - row0) - 1) / T;
     __hip_atomic_store(a.ws_cnt + 2 * c.b, 2 * (int)blockIdx.x + (row0 == f0 ? 0 : 1),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -523,72 +543,123 @@ __device__ __forceinline__ void finish_segment(const LatentArgs& a, const Cursor
                        __HIP_MEMORY_SCOPE_AGENT);
   }
   if (seg0 == row0 && seg1 == row1) {
-    const float inv[2] = {1.f / ltot[0], 1.f / ltot[1]};
-    store_scaled(a, st.o, inv, c.b, h0, col, kg);
+    if (!flagged) {
+      const float inv[2] = {1.f / ltot[0], 1.f / ltot[1]};
+      store_scaled(a, st.o, inv, c.b, h0, col, kg);
+    }
     return;
   }
-  write_record(rec, 2 * (int)blockIdx.x + (seg0 == f0 ? 0 : 1), st, ltot, h0, col, kg);
+  if (!flagged)
+    write_record(rec, 2 * (int)blockIdx.x + (seg0 == f0 ? 0 : 1), st, ltot, h0, col, kg);
 }
 
-// ---- slow path: rows whose scores outran their reference --------------------
+// ---- slow path: segments whose scores outran their reference --------------
 //
-// Exact two-pass recompute of row b by one workgroup: the first pass finds
-// every head's maximum score, the second folds the row with it as the
-// reference (all weights <= 1). Runs only after the streaming loop, when
-// the accumulator registers are free.
-__device__ __forceinline__ void recompute_row(const LatentArgs& a, const int* prefix, int b,
-                                              lds_char* stage, int wave, int lane, int h0,
-                                              int col, int kg) {
-  Cursor c;
-  c.b = b;
-  c.n = prefix[b + 1] - prefix[b];
-  const int L = uniform_load(a.seq_lens, b);
+// The slow path's tile loader: tile j of row b into `stage` in the layout
+// of the streaming loop (token rows of kRowBytes, pad chunks and tokens past
+// the row zero), by plain loads through registers and LDS stores, followed
+// by a workgroup barrier.
+__device__ __forceinline__ void load_tile_plain(const LatentArgs& a, int b, int j, int L,
+                                                lds_char* stage) {
+  const int valid = min(kTileTokens, L - j * kTileTokens);
+  const int page = a.block_tables[(size_t)b * a.max_blocks + j / (kPageTokens / kTileTokens)];
+  const char* base =
+      (const char*)a.kv_pool +
+      ((size_t)page * kPageTokens + (size_t)(j % (kPageTokens / kTileTokens)) * kTileTokens) *
+          kTokenBytes;
+  for (int i = threadIdx.x; i < kTileTokens * kRowChunks; i += blockDim.x) {
+    const int t = i / kRowChunks;
+    const int ch = i - t * kRowChunks;
+    typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (ch < kDataChunks && t < valid) v = *(const u32x4_t*)(base + t * kTokenBytes + ch * 16);
+    *(lds_u32x4*)(stage + t * kRowBytes + ch * 16) = v;
+  }
+  __syncthreads();
+}
+
+// Exact two-pass recompute of row b's tiles j0 .. j1 - 1 (one segment) by
+// its workgroup: the first pass finds every head's maximum score over the
+// segment, the second folds the segment with it as the reference (all
+// weights <= 1); the result is the segment's exact (O, m, l), written like a
+// fast-path segment. Runs after the workgroup's streaming loop, when the
+// accumulator registers and the tile stages are free, so its cost is bounded
+// by the workgroup's own range.
+__device__ __forceinline__ void recompute_segment(const LatentArgs& a, int b, int j0, int j1,
+                                                  lds_char* stage, int h0, int col, int kg,
+                                                  RowState& st) {
+  const int L = a.seq_lens[b];
   bf16x8_t qf[2][kQkSteps];
   load_queries(a, b, h0, col, kg, qf);
   float mx[2] = {-INFINITY, -INFINITY};
-  for (c.j = 0; c.j < c.n; ++c.j) {
-    load_tile(a, c, stage, wave, lane);
-    tile_barrier<false>();
+  for (int j = j0; j < j1; ++j) {
+    load_tile_plain(a, b, j, L, stage);
     float x[2][2][4];
-    score_tile(stage, qf, min(kTileTokens, L - c.j * kTileTokens), a.scale_log2, col, kg, x);
+    score_tile(stage, qf, min(kTileTokens, L - j * kTileTokens), a.scale_log2, col, kg, x);
     mx[0] = fmaxf(mx[0], tile_max(x[0]));
     mx[1] = fmaxf(mx[1], tile_max(x[1]));
-    lds_barrier();  // everyone is done with the stage
+    __syncthreads();  // everyone is done with the stage
   }
-  RowState st;
-  for (c.j = 0; c.j < c.n; ++c.j) {
-    load_tile(a, c, stage, wave, lane);
-    tile_barrier<false>();
+  st.m[0] = mx[0];
+  st.m[1] = mx[1];
+  for (int j = j0; j < j1; ++j) {
+    load_tile_plain(a, b, j, L, stage);
     float x[2][2][4];
-    score_tile(stage, qf, min(kTileTokens, L - c.j * kTileTokens), a.scale_log2, col, kg, x);
+    score_tile(stage, qf, min(kTileTokens, L - j * kTileTokens), a.scale_log2, col, kg, x);
     bf16x8_t pf[2];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       const float w = make_weights(x[ht], mx[ht], pf[ht]);
-      st.l[ht] = c.j == 0 ? w : st.l[ht] + w;
+      st.l[ht] = j == j0 ? w : st.l[ht] + w;
     }
-    if (c.j == 0)
+    if (j == j0)
       value_tile<true>(stage, pf, st.o, col, kg);
     else
       value_tile<false>(stage, pf, st.o, col, kg);
-    lds_barrier();
+    __syncthreads();
   }
-  const float inv[2] = {1.f / sum_over_kg(st.l[0]), 1.f / sum_over_kg(st.l[1])};
-  store_scaled(a, st.o, inv, b, h0, col, kg);
+}
+
+// Recomputes and writes every segment of this workgroup's range [f0, f1)
+// whose row is marked in `redo`. Kept out of line: inlined, its second
+// accumulator changed the register allocation of the streaming loop (twice
+// the spills, and the call took twice as long).
+__device__ __forceinline__ void recompute_flagged(const LatentArgs& a,
+                                                            const int* prefix,
+                                                            const unsigned* redo, int f0, int f1,
+                                                            lds_char* stages, int wave, int col,
+                                                            int kg) {
+  const int B = a.num_seqs;
+  const int h0 = wave * kHeadsPerWave;
+  const __amdgpu_buffer_rsrc_t rec = range_rsrc(a.ws_rec, 2 * a.grid * kRecordBytes);
+  const int b_first = find_sequence(prefix, B, f0);
+  const int b_last = find_sequence(prefix, B, f1 - 1);
+  for (int b = b_first; b <= b_last; ++b) {
+    if (!(redo[b >> 5] & (1u << (b & 31)))) continue;
+    const int row0 = prefix[b], row1 = prefix[b + 1];
+    const int seg0 = max(f0, row0), seg1 = min(f1, row1);
+    RowState st;
+    recompute_segment(a, b, seg0 - row0, seg1 - row0, stages, h0, col, kg, st);
+    write_segment(a, b, st, seg0, seg1, row0, row1, f0, rec, h0, col, kg);
+  }
 }
 
 __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
   // dynamic LDS: kStages tile stages, then the rows' tile prefix [B + 1]
-  // and cost prefix [B + 1]
+  // and cost prefix [B + 1]; static: the bit set of rows whose segment in
+  // this range is to be recomputed (a fixed address, so no register holds
+  // it through the streaming loop)
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int scan_scratch[kWaves];
   __shared__ int bcast[1 + kWaves];
+  __shared__ unsigned redo[kMaxSeqs / 32];
   lds_char* stages = (lds_char*)smem;
   int* prefix = (int*)(smem + kStages * kStageBytes);
   int* cprefix = prefix + a.num_seqs + 1;
 
   const int B = a.num_seqs;
   if (threadIdx.x < 1 + kWaves) bcast[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < (B + 31) / 32; i += blockDim.x) redo[i] = 0u;
   // a row of L tokens is ceil(L / 32) tiles and costs kFinishSlots more for
   // its finish (L > 0)
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
@@ -688,7 +759,8 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
       // it would also drain the tile prefetch)
       tile_step(std::true_type{});
       while (f < seg1) tile_step(std::false_type{});
-      finish_segment(a, cc, st, seg0, seg1, f0, T, prefix, cprefix, rec, bcast, wave, h0, col, kg);
+      finish_segment(a, cc, st, seg0, seg1, f0, T, prefix, cprefix, rec, bcast, redo, wave, h0,
+                     col, kg);
       if (f < f1) {  // the next row with tiles
         int b = cc.b + 1;
         while (prefix[b + 1] == prefix[b]) ++b;
@@ -699,43 +771,22 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
     }
   }
 
-  // every workgroup counts itself out; the last one recomputes flagged rows
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the segments this workgroup flagged, recomputed exactly one at a time
+  // (every stage load has landed: the last tile waited for all of them)
   lds_barrier();
-  if (threadIdx.x == 0)
-    bcast[0] = __hip_atomic_fetch_add(a.ws_ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  lds_barrier();
-  if (bcast[0] != a.grid - 1) return;
-  if (__hip_atomic_load(a.ws_ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > 0) {
-    for (int b = 0; b < B; ++b) {
-      if (__hip_atomic_load(a.ws_flag + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
-        continue;
-      recompute_row(a, prefix, b, stages, wave, lane, h0, col, kg);
-      lds_barrier();
-      if (threadIdx.x == 0) {
-        // the row is written: the merge kernel takes it as whole (its
-        // first-tile workgroup wrote the piece count before counting out)
-        __hip_atomic_store(a.ws_cnt + 2 * b + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.ws_flag + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  if (threadIdx.x == 0) {  // rearm for the next call
-    __hip_atomic_store(a.ws_ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.ws_ctl + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (f0 < f1) recompute_flagged(a, prefix, redo, f0, f1, stages, wave, col, kg);
 }
 
 // ---- merging cut rows -----------------------------------------------------------
 //
 // Workgroup (b, q) writes heads 32 q .. 32 q + 31 of cut row b: out = sum_i
 // w_i x_i over the row's pieces in piece order, x_i a piece's normalised
-// output as its record holds it (bf16), w_i = l_i 2^(m_i - M) / L
+// output as its record holds it (fp32), w_i = l_i 2^(m_i - M) / L
 // (log-sum-exp merge), one fused multiply-add per piece and element. Thread
 // t takes head 32 q + t / 8 and 8 chunks of 8 dims (dims 64 j + 8 (t % 8)
 // .. + 7, j = 0..7); the record loads of kMergePieces pieces go out
-// together. Rows that are whole, empty or recomputed by the slow path (its
-// piece count set to 1) are left as the decode kernel wrote them.
+// together. Rows that are whole or empty are left as the decode kernel
+// wrote them.
 __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   const int b = blockIdx.x >> 2;
   const int q = blockIdx.x & 3;

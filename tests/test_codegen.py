@@ -1,0 +1,61 @@
+"""Properties of the generated gfx950 code that the kernels' speed depends
+on, checked on the CPU (hipcc cross-compiles; no GPU needed).
+
+The latent decode kernel runs at the register file's limit (256 VGPRs and
+256 accumulation registers per lane, one wave per SIMD). If the compiler
+moves the tile loads' per-lane offsets to scratch, every refill load is
+preceded by a scratch reload and a wait for all vector memory operations,
+which drains the tile prefetch and doubles the call time; an innocuous
+change to the code after the streaming loop did exactly that once. The test
+compiles the kernel and checks the score steps of its streaming loop (the
+basic blocks with four matrix products and one tile load into LDS) for
+scratch reloads."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "paged_kv_cache_55_amd", "csrc")
+
+
+def device_asm(src, tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc is not available")
+    out = tmp_path / "k.s"
+    cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-S", "--offload-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", os.path.join(CSRC, src),
+           "-o", str(out)]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    return out.read_text()
+
+
+def kernel_blocks(asm, kernel_prefix):
+    start = asm.index("\n" + kernel_prefix)
+    end = asm.index("s_endpgm", start)
+    blocks, cur = [], []
+    for line in asm[start:end].splitlines():
+        if re.match(r"^\.LBB\S+:", line):
+            blocks.append(cur)
+            cur = []
+        else:
+            cur.append(line.strip())
+    blocks.append(cur)
+    return blocks
+
+
+def test_latent_streaming_loop_has_no_scratch_reloads(tmp_path):
+    asm = device_asm("latent_mfma.hip", tmp_path)
+    blocks = kernel_blocks(asm, "_ZN7pagedkv12_GLOBAL__N_120latent_decode_kernel")
+    steps = [b for b in blocks
+             if sum("v_mfma" in x for x in b) == 4
+             and sum("buffer_load_dwordx4" in x and " lds" in x for x in b) == 1]
+    assert len(steps) >= 10, "the score steps with a tile refill were not found"
+    bad = [i for i, b in enumerate(steps) if any(x.startswith("scratch_load") for x in b)]
+    assert not bad, f"{len(bad)} of {len(steps)} score steps reload from scratch"

@@ -138,6 +138,13 @@ def spiked_case(seed, gain):
     return c
 
 
+def plant_spike(c, b, t, gain, head=0):
+    """Latent t of row b becomes `gain` times the query of `head`."""
+    bs = c.kv_pool.shape[1]
+    blk = int(c.block_tables[b, t // bs])
+    c.kv_pool[blk, t % bs] = (gain * c.q[b, head].float()).to(c.kv_pool.dtype)
+
+
 @pytest.mark.parametrize("gain", [1.5, 5.0])
 def test_latent_overflow_takes_the_exact_path(gain):
     c = spiked_case(1006, gain)
@@ -147,7 +154,7 @@ def test_latent_overflow_takes_the_exact_path(gain):
 
 
 def test_latent_overflow_then_normal_on_one_workspace():
-    """The flags and control counters are rearmed by the call that used them."""
+    """A call after one that took the exact path, on the same workspace."""
     c = spiked_case(1008, 5.0)
     d = c.to("cuda")
     dims = pk.make_latent_dims(4, c.block_tables.shape[1], c.kv_pool.shape[0])
@@ -161,9 +168,6 @@ def test_latent_overflow_then_normal_on_one_workspace():
                                workspace=ws)
     torch.cuda.synchronize()
     compare(gpu_out_f64(out2), oracle_latent(c2), c2.seq_lens.numpy(), "bf16")
-    # all control words are back to zero
-    head = ws[:256].view(torch.int32).cpu()
-    assert int(head[0]) == 0 and int(head[1]) == 0
 
 
 def test_latent_write_bit_exact():
@@ -208,3 +212,51 @@ def test_latent_rejects_unsupported():
     c = wl.latent_case(1012, [10, 20], num_heads=64).to("cuda")
     with pytest.raises(pk.PagedKVError):
         pk.pa_latent_decode(c.q, c.kv_pool, c.block_tables, c.seq_lens, c.scale)
+
+
+def whole_rows_case(seed):
+    """256 rows of 300 tokens: 10 tiles plus 8 finish slots each, so the
+    per-workgroup cost is 18 on a grid of 256 workgroups and every row lies
+    whole inside one workgroup's range (the fast path writes it directly)."""
+    return wl.latent_case(seed, [300] * 256)
+
+
+@pytest.mark.parametrize("rows", [[37], list(range(3, 256, 16)), list(range(256))],
+                         ids=["one", "sixteen", "all"])
+def test_latent_overflow_in_whole_rows(rows):
+    """A spike at token 170 (tile 5, long after the reference max was fixed)
+    of whole rows, at gain 5: the fast path's weights overflow fp32 there, so
+    only the exact recompute gives a finite result, and it must be the only
+    write of those rows. Checked on every row against the oracle, then a
+    normal call on the same workspace."""
+    c = whole_rows_case(1016)
+    for b in rows:
+        plant_spike(c, b, 170, 5.0)
+    d = c.to("cuda")
+    dims = pk.make_latent_dims(256, c.block_tables.shape[1], c.kv_pool.shape[0])
+    ws = torch.zeros(pk.pa_latent_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    print(f"latent whole-row spikes in {len(rows)} rows", flush=True)
+    out = pk.pa_latent_decode(d.q, d.kv_pool, d.block_tables, d.seq_lens, c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    compare(gpu_out_f64(out), oracle_latent(c), c.seq_lens.numpy(), "bf16")
+    c2 = whole_rows_case(1017)
+    d2 = c2.to("cuda")
+    out2 = pk.pa_latent_decode(d2.q, d2.kv_pool, d2.block_tables, d2.seq_lens, c2.scale,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    compare(gpu_out_f64(out2), oracle_latent(c2), c2.seq_lens.numpy(), "bf16")
+
+
+def test_latent_overflow_in_cut_and_whole_rows():
+    """Spikes in a row cut over many workgroups and in short whole rows of
+    the same batch, in different tiles: every flagged segment is recomputed
+    by its own workgroup and written once."""
+    rng = np.random.default_rng(1018)
+    lens = rng.integers(40, 400, size=120).tolist()
+    lens[60] = 9000
+    c = wl.latent_case(1018, lens)
+    for b in (0, 17, 60, 61, 119):
+        plant_spike(c, b, lens[b] - 3, 5.0, head=b % 128)
+    plant_spike(c, 60, 4500, 5.0, head=3)
+    check(c)
