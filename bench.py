@@ -4,15 +4,19 @@
                     [--kernel auto|mfma|valu] [--partition P] [--bucket B]
 
 A step is one pass of the hot path over one batch:
-  config 2 (default; Llama-3-8B-shaped layer, B = 64, L ~ U[128, 4096]):
+  config 5 (default; the full Llama-3-8B-shaped decode step, attention only:
+      32 layers, each with its own KV pool, bucket B = 256 rows of which the
+      seeded real rows have L ~ U[1, 8192] and the rest are padded at L = 0,
+      one [B, 512] table for every layer): pa_decode for each of the 32
+      layers, with the balanced split (partition_tokens 0, the library's
+      default; --partition 512 runs the fixed 512-token split instead);
+  config 2 (Llama-3-8B-shaped layer, B = 64, L ~ U[128, 4096]):
       the KV append of the 64 new tokens and pa_decode over all 64 rows,
       as pa_write_kv then pa_decode (--step separate, the default) or as
       one pa_decode_append call (--step fused); the line reports the other
       form's step time too;
   config 4 (Llama-3.3-70B-shaped layer, B = 256, lognormal lengths):
       pa_decode;
-  config 5 (8B decode step, 32 layers, bucket B of padded rows):
-      pa_decode for each of the 32 layers;
   config 6 (chunked prefill on an 8B-shaped layer: 8 prompts, one 512-token
       chunk each, 0 .. 3,584 tokens already cached):
       pa_write_kv of the 4,096 chunk tokens, then pa_prefill; its roofline is
@@ -32,8 +36,10 @@ per step by itself and uses one copy).
 
 Printed: one JSON line with the achieved KV bandwidth (valid tokens' K and V
 bytes / step time), sequences per second per layer, the roofline of the
-decode kernel (algorithmic bytes per call / mean call time from HIP events on
-the launch stream), and the CPU oracle timed on a bounded sample.
+attention call (algorithmic bytes, or flops, per call / its mean duration:
+HIP events on the launch stream around back-to-back calls, which for the
+decode-only steps is the timed region itself), and the CPU oracle timed on a
+bounded sample.
 """
 
 from __future__ import annotations
@@ -68,11 +74,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=5, choices=[2, 4, 5, 6, 7])
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
-    ap.add_argument("--partition", type=int, default=None,
-                    help="split-K partition tokens; 0 = balanced split (default 0 for "
-                         "configs 2 and 4, 512 for the 32-layer step)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="split-K partition tokens; 0 = balanced split (the default)")
     ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--block-size", type=int, default=16,
@@ -91,6 +96,10 @@ def parse():
                     help="CPU work budget for the oracle baseline (0 = skip)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run a plain copy kernel of known size (counter calibration)")
+    ap.add_argument("--spike-rows", type=int, default=0,
+                    help="config 7: rows (of those longer than two tiles) whose last latent "
+                         "is made to outscore their first tiles by far, so that they take "
+                         "the exact recompute (-1 = all of them)")
     return ap.parse_args()
 
 
@@ -136,7 +145,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     kernel = args.kernel if args.kernel != "auto" else "mfma"
-    part = (512 if args.config == 5 else 0) if args.partition is None else args.partition
+    part = args.partition
 
     # ---------------- inputs ----------------
     if args.config in (2, 4):
@@ -193,6 +202,9 @@ def main():
             pk.pa_write_kv(c.k_new, c.v_new, c.slot_mapping, c.k_pool, c.v_pool)
     elif args.config == 7:
         case = wl.latent_decode_batch()
+        spiked = []
+        if args.spike_rows:
+            spiked = spike_latent_rows(case, args.spike_rows)
         copies = [case.to(dev) for _ in range(max(1, args.copies))]
         B, Hq, Hkv, D = case.q.shape[0], case.q.shape[1], 1, case.q.shape[2]
         n_real = int((case.seq_lens > 0).sum())
@@ -200,6 +212,8 @@ def main():
         layers = 1
         lens_host = case.seq_lens.numpy()
         workload = "deepseek_v3_mla_layer_b256_lognormal1024"
+        if spiked:
+            workload += f"_spiked{len(spiked)}"
         outs = [torch.empty((B, Hq, wl.LATENT_VALUE_DIM), dtype=torch.bfloat16, device=dev)
                 for _ in copies]
         ldims = pk.make_latent_dims(B, case.block_tables.shape[1], case.kv_pool.shape[0])
@@ -238,6 +252,8 @@ def main():
         def pre(i):
             pass
 
+    if part > 0:
+        workload += f"_split{part}"
     stream = torch.cuda.current_stream()
 
     def step(i, events=None, mode=None):
@@ -308,7 +324,33 @@ def main():
             step(i, mode=other)
         other_ms = timed_steps(other)
 
-    # per-call decode durations, measured in a second pass with events
+    # The attention call's mean duration for the roofline: HIP events on the
+    # launch stream around back-to-back calls. A decode-only step (configs 4,
+    # 5 and 7, eager) is exactly that, so its timed region is used as is;
+    # steps that also append K/V (configs 2 and 6) or run as a graph get a
+    # pass of their own with the calls alone.
+    calls_per_step = len(decode_calls(0))
+    decode_only = args.config in (4, 5, 7) and not args.graph
+    if decode_only:
+        kernel_ms = ms_per_step / calls_per_step
+    else:
+        saved_pre = pre
+        pre = lambda i: None  # noqa: E731  the calls alone (a fused call keeps its append)
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        ka = torch.cuda.Event(enable_timing=True)
+        kb = torch.cuda.Event(enable_timing=True)
+        ka.record(stream)
+        for i in range(args.steps):
+            step(i)
+        kb.record(stream)
+        torch.cuda.synchronize()
+        kernel_ms = ka.elapsed_time(kb) / (args.steps * calls_per_step)
+        pre = saved_pre
+
+    # per-call durations with an event pair around each call (a diagnostic:
+    # the events add their own gaps)
     events = []
     for i in range(args.steps):
         step(i, events)
@@ -359,7 +401,7 @@ def main():
     if fused:  # the appended tokens: k_new/v_new read, their slots written, slot ids
         T = int((case.slot_mapping >= 0).sum())
         per_call_alg += 4 * T * Hkv * D * 2 + 4 * B
-    mean_call_s = float(call_ms.mean()) / 1e3
+    mean_call_s = kernel_ms / 1e3
     achieved = per_call_alg / mean_call_s / 1e9
     traffic = load_traffic(kernel, workload)
     prefill_flops = None
@@ -386,7 +428,11 @@ def main():
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(args, case, lens_host, kv_bytes / layers, workload)
+        if args.config == 5:
+            cpu = cpu_baseline_step(args, spec, layer_t, workload)
+        else:
+            cpu = cpu_baseline(args, case, lens_host, kv_bytes / layers, workload)
+        cpu.update(host_threads())
 
     rec = {
         "metric": METRIC,
@@ -456,6 +502,92 @@ def roofline_kernel(kernel: str, part: int, head_dim: int) -> str:
     return f"{name}<{head_dim}> + decode_reduce_kernel when a row spans several partitions"
 
 
+def host_threads():
+    """What the host offers and what the oracle used: every timed oracle call
+    runs under a BLAS limit of one thread (numpy's matrix products), and the
+    oracle itself is single-threaded Python."""
+    from threadpoolctl import threadpool_info
+    return {"host_cpus": os.cpu_count(),
+            "blas_threads": 1,
+            "blas_libraries": sorted({i.get("internal_api", "?") for i in threadpool_info()})}
+
+
+def spike_latent_rows(case, n):
+    """Makes the last latent of `n` rows (evenly spaced among the rows longer
+    than two 32-token tiles; all of them for n < 0) equal 5 x the query of
+    head 0: that head's score there exceeds the rest of the row by about 120
+    natural-log units, so the piece holding it flags the row (unless the
+    token opens that piece) and the row takes the exact recompute. Returns
+    the rows."""
+    import numpy as np
+    lens = case.seq_lens.numpy()
+    cand = [b for b in range(len(lens)) if lens[b] > 64]
+    if n >= 0 and n < len(cand):
+        cand = [cand[i] for i in np.linspace(0, len(cand) - 1, n).round().astype(int)]
+    bs = case.kv_pool.shape[1]
+    for b in cand:
+        t = int(lens[b]) - 1
+        blk = int(case.block_tables[b, t // bs])
+        case.kv_pool[blk, t % bs] = (5.0 * case.q[b, 0].float()).to(case.kv_pool.dtype)
+    return cand
+
+
+def cpu_baseline_step(args, spec, layer_t, workload):
+    """The float64 oracle on one host core over a sample of the 32-layer step:
+    16 real rows (seeded) of 4 layers (0, 10, 21, 31), the sample repeated
+    until the time budget is spent. Each (layer, row set) gets a host copy of
+    just the blocks its rows reference, made before timing; the oracle's own
+    table walk over that copy is timed. The rate (KV bytes per second) gives
+    the time of the whole step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import to_numpy
+
+    rng = np.random.default_rng(55_005)
+    rows = sorted(rng.choice(spec.n_real, size=min(16, spec.n_real), replace=False).tolist())
+    layers = [l for l in (0, 10, 21, 31) if l < len(layer_t)]
+    elem, Hkv, D = 2, spec.num_kv_heads, spec.head_dim
+    samples = []
+    for l in layers:
+        q, k, v = layer_t[l]
+        need = sorted({int(spec.block_tables[b, j]) for b in rows
+                       for j in range(math.ceil(int(spec.seq_lens[b]) / 16))})
+        remap = np.zeros(spec.num_blocks, dtype=np.int64)
+        remap[need] = np.arange(len(need))
+        idx = torch.tensor(need, dtype=torch.long, device=k.device)
+        samples.append(dict(q=to_numpy(q[rows]), k_pool=to_numpy(k[idx]), v_pool=to_numpy(v[idx]),
+                            block_tables=remap[spec.block_tables[rows]].astype(np.int32),
+                            seq_lens=spec.seq_lens[rows], scale=1.0 / math.sqrt(D),
+                            dtype="bf16"))
+    sample_bytes = int(spec.seq_lens[rows].astype(np.int64).sum()) * Hkv * D * 2 * elem
+    done_bytes, done_decodes, t_total, passes = 0, 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while t_total < args.cpu_seconds:
+            for a in samples:
+                t = time.perf_counter()
+                oracle.paged_decode(**a)
+                t_total += time.perf_counter() - t
+                done_bytes += sample_bytes
+                done_decodes += len(rows)
+            passes += 1
+    rate = done_bytes / t_total
+    return {
+        "value": round(rate / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(rows)} real rows x {len(layers)} layers ({layers}) of {workload}, "
+                  f"{passes} pass(es): {done_decodes} sequence decodes, "
+                  f"{done_bytes / 1e6:.1f} MB of K/V in {t_total:.1f} s, float64 numpy, "
+                  "BLAS limited to 1 thread; the step time is scaled by K/V bytes",
+        "seqs_per_s": round(done_decodes / t_total, 2),
+        "step_s": round(spec.kv_bytes_per_layer() * len(layer_t) / rate, 2),
+    }
+
+
 def cpu_baseline(args, case, lens_host, kv_bytes_per_layer, workload):
     """Time the float64 oracle on host cores over a bounded sample."""
     import numpy as np
@@ -465,8 +597,6 @@ def cpu_baseline(args, case, lens_host, kv_bytes_per_layer, workload):
     import workloads as wl
     from workloads import to_numpy
 
-    if case is None:  # config 5: one layer's sample of rows, drawn on the host
-        return None
     if isinstance(case, wl.LatentCase):
         return cpu_baseline_latent(args, case, lens_host, workload)
     if case.query_start is not None:

@@ -18,6 +18,8 @@ Tolerances (spec bar):
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -114,3 +116,19 @@ def oracle_prefill(case):
                                to_numpy(case.seq_lens), to_numpy(case.query_start), case.scale,
                                case.dtype, block_size=case.block_size)
     return out, k, v
+
+
+def oracle_config5_rows(spec, q, k, v, rows):
+    """The oracle on rows `rows` of one layer of the 32-layer step, whose
+    tensors live on the device: host copies are made of just the blocks
+    those rows reference (the oracle walks the remapped tables)."""
+    need = sorted({int(spec.block_tables[b, j]) for b in rows
+                   for j in range(math.ceil(int(spec.seq_lens[b]) / 16))} | {spec.poison_block})
+    remap = np.full(spec.num_blocks, -1, dtype=np.int64)
+    remap[need] = np.arange(len(need))
+    idx = torch.tensor(need, dtype=torch.long, device=k.device)
+    kh, vh = to_numpy(k[idx]), to_numpy(v[idx])
+    tables = remap[spec.block_tables[rows]]
+    tables[tables < 0] = remap[spec.poison_block]  # entries past each row's end
+    return oracle.paged_decode(to_numpy(q)[rows], kh, vh, tables.astype(np.int32),
+                               spec.seq_lens[rows], 1.0 / math.sqrt(128), "bf16")
