@@ -126,6 +126,24 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     float scale, void* out, const pa_dims* dims,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, serving loops and harnesses that
+ * forbid allocation). Same arguments, kernels and results as pa_decode,
+ * bit for bit; the workspace is instead a device array of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. The call allocates nothing. Dims whose
+ * pa_decode_workspace_bytes() exceeds PA_NOALLOC_SCRATCH_BYTES return
+ * PA_ERR_UNSUPPORTED before anything runs (the balanced split at the
+ * supported head groups needs at most about 17 MiB; the fixed split's
+ * partials grow with B * Hq * partitions). With the balanced split a zero
+ * fill of its piece counters runs on `stream` before the decode. Every call
+ * on one GPU shares that GPU's array: calls that may overlap in time on one
+ * GPU (other streams, other threads) race and give undefined results. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            float scale, void* out, const pa_dims* dims, void* stream);
+
 /* One decode step in one call: the KV append of every row's new token,
  * then paged decode attention over the updated cache. Equivalent to
  *   pa_write_kv(k_new, v_new, slot_mapping, num_seqs, ...);

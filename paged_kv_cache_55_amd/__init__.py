@@ -36,7 +36,8 @@ from .build import LIB_PATH
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_LAUNCH",
     "PaDims", "PagedKVError", "SYMBOLS", "load_library", "make_dims",
-    "pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_prefill", "pa_write_kv",
+    "pa_decode", "pa_decode_append", "pa_decode_noalloc", "pa_decode_workspace_bytes",
+    "pa_prefill", "pa_write_kv", "NOALLOC_SCRATCH_BYTES",
     "pa_copy_blocks", "PaLatentDims", "make_latent_dims", "pa_latent_decode",
     "pa_latent_write", "pa_latent_workspace_bytes",
     "pa_status_string", "pa_version", "validate",
@@ -47,10 +48,12 @@ PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 BLOCK_SIZE = 16
 
-SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_append", "pa_prefill",
+SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_noalloc", "pa_decode_append",
+           "pa_prefill",
            "pa_write_kv", "pa_copy_blocks", "pa_latent_workspace_bytes", "pa_latent_decode",
            "pa_latent_write", "pa_status_string", "pa_version")
 LATENT_HEADS, LATENT_DIM, LATENT_VALUE_DIM, LATENT_BLOCK = 128, 576, 512, 64
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 
 class PaDims(ctypes.Structure):
@@ -91,6 +94,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_bytes.restype = SZ
     lib.pa_decode.argtypes = [P, P, P, P, P, F32, P, D, P, SZ, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, F32, P, D, P]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_append.argtypes = [P, P, P, P, P, P, P, P, F32, P, D, P, SZ, P]
     lib.pa_decode_append.restype = ctypes.c_int
     lib.pa_prefill.argtypes = [P, P, P, P, P, P, I32, F32, P, D, P]
@@ -238,6 +243,22 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
                                   _stream(stream))
     if st != PA_OK:
         raise PagedKVError("pa_decode", st)
+    return out
+
+
+def pa_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
+                      partition_tokens=0, kernel="auto", stream=None):
+    """pa_decode with the library's own per-GPU scratch array as workspace:
+    the library call allocates nothing (pass ``out`` to allocate nothing
+    here either). Calls that may overlap in time on one GPU race."""
+    dims, out = _decode_dims(q, k_pool, v_pool, block_tables, seq_lens, out,
+                             partition_tokens, kernel)
+    st = load_library().pa_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(block_tables), _ptr(seq_lens),
+                                          ctypes.c_float(scale), _ptr(out), ctypes.byref(dims),
+                                          _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_decode_noalloc", st)
     return out
 
 

@@ -263,6 +263,36 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
   return PA_OK;
 }
 
+// ---- allocation-free decode -----------------------------------------------
+//
+// pa_decode_noalloc's workspace: a device array of the library's own, one
+// copy per GPU, held until the process ends. In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address comes
+// from hipGetSymbolAddress, once per device with that device current, and
+// only that address is passed to kernels.
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (ptr == nullptr) return hipErrorInvalidSymbol;
+  *out = cache[dev] = ptr;
+  return hipSuccess;
+}
+
 // Latent decode: one workgroup per compute unit, at most this many; a
 // workgroup's range holds at least kLatentMinTiles 32-token tiles.
 constexpr int kMaxLatentGrid = 256;
@@ -362,6 +392,28 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     void* stream) {
   return decode_impl(q, nullptr, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens, scale,
                      out, dims, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                            void* out, const pa_dims* dims, void* stream) {
+  Plan plan;
+  pa_status st = plan_decode(dims, &plan);
+  if (st != PA_OK) return st;
+  if (plan.ws_bytes > kScratchBytes) return PA_ERR_UNSUPPORTED;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return PA_ERR_LAUNCH;
+  if (plan.balanced) {
+    // the piece counters must start at zero; the previous call on this GPU
+    // left them so unless it failed, and the fill makes it certain
+    const hipError_t e = launch_zero_fill((char*)ws + plan.off_cnt, plan.off_o - plan.off_cnt,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return decode_impl(q, nullptr, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens, scale,
+                     out, dims, ws, kScratchBytes, stream);
 }
 
 pa_status pa_decode_append(const void* q, const void* k_new, const void* v_new,

@@ -1,5 +1,5 @@
-// KV append (pa_write_kv, pa_latent_write) and copy-on-write block copy
-// (pa_copy_blocks).
+// KV append (pa_write_kv, pa_latent_write), copy-on-write block copy
+// (pa_copy_blocks) and a zero fill of device memory.
 //
 // Both are bit copies. A new token's K row is contiguous in the token-major
 // K region of its block; its V column is strided in the dim-major V tile
@@ -123,6 +123,24 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* 
   void* args[] = {&kn, &vn, &slots, &kp, &vp, &num_tokens, &num_kv_heads, &head_dim,
                   &block_shift};
   return hipLaunchKernel((const void*)&write_kv_kernel<uint32_t>, grid, block, args, 0, s);
+}
+
+// Zero-fill of n 16-byte vectors: a kernel rather than a memset, so that a
+// captured graph replays it like any other launch.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  uint4* v = (uint4*)p;
+  size_t n = bytes / sizeof(uint4);
+  const size_t blocks = (n + 255) / 256;
+  void* args[] = {&v, &n};
+  return hipLaunchKernel((const void*)&zero_fill_kernel,
+                         dim3((unsigned)(blocks < 1024 ? (blocks > 0 ? blocks : 1) : 1024)),
+                         dim3(256), args, 0, s);
 }
 
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,

@@ -80,5 +80,8 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, const int32_t* 
                            int head_dim, int block_shift, int elem_bytes, hipStream_t s);
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
                               size_t block_bytes, hipStream_t s);
+// Zero-fills `bytes` (a multiple of 16) at the 16-byte aligned device
+// address `p` with a kernel.
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace pagedkv

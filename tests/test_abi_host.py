@@ -292,3 +292,31 @@ def test_latent_write_rejects_bad_args(lib):
     assert lib.pa_latent_write(None, None, 0, None, ctypes.byref(d), None) == pk.PA_OK
     bad = latent_dims(block_size=32)
     assert lib.pa_latent_write(FAKE, FAKE, 3, FAKE, ctypes.byref(bad), None) == pk.PA_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------
+# allocation-free decode: its checks run before the library touches the GPU
+# --------------------------------------------------------------------------
+
+def noalloc_status(lib, d, q=FAKE, scale=0.1):
+    return lib.pa_decode_noalloc(q, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE,
+                                 ctypes.byref(d), None)
+
+
+def test_noalloc_rejects_workspaces_beyond_its_scratch(lib):
+    # fixed split at 16-token partitions: 64 x 32 x 256 partials of 128 fp32
+    big = dims(partition_tokens=16)
+    assert pk.pa_decode_workspace_bytes(big) > pk.NOALLOC_SCRATCH_BYTES
+    assert noalloc_status(lib, big) == pk.PA_ERR_UNSUPPORTED
+    # the balanced split fits at every supported head group and the largest batch
+    for g in (1, 4, 8, 16):
+        d = dims(partition_tokens=0, num_seqs=4096, num_q_heads=8 * g)
+        assert 0 < pk.pa_decode_workspace_bytes(d) <= pk.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_bad_args_like_pa_decode(lib):
+    assert noalloc_status(lib, dims(head_dim=96)) == pk.PA_ERR_UNSUPPORTED
+    assert noalloc_status(lib, dims(num_seqs=0)) == pk.PA_ERR_INVALID_ARG
+    assert noalloc_status(lib, dims(partition_tokens=0), q=None) == pk.PA_ERR_INVALID_ARG
+    assert noalloc_status(lib, dims(partition_tokens=0), scale=float("nan")) == \
+        pk.PA_ERR_INVALID_ARG
