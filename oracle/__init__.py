@@ -11,8 +11,9 @@ helpers or constants. The two meet only through the seeded inputs that
 ``workloads`` produces and that callers pass to both sides.
 
 Modules
-  attention  paged decode, chunked-prefill and latent (MLA-style) decode
-             attention, KV append (write) and block copy
+  attention  paged decode, decode over an unpaged (contiguous) cache,
+             chunked-prefill and latent (MLA-style) decode attention, KV
+             append (write) and block copy
   pages      page / block-table arithmetic of the admission ledger
 
 Every function names the passage of the pages it follows. No function here
@@ -28,6 +29,7 @@ from .attention import (  # noqa: F401
     gather_sequence,
     decode_contiguous,
     paged_decode,
+    contiguous_cache_decode,
     paged_prefill,
     latent_decode,
     brute_force_decode,

@@ -176,6 +176,33 @@ def paged_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, dtype,
     return out
 
 
+def contiguous_cache_decode(q, k_cache, v_cache, seq_lens, scale, dtype, rows=None):
+    """Decode attention over an unpaged KV cache, in float64.
+
+    Each (sequence, KV head) owns one contiguous run of capacity Lmax
+    tokens: k_cache [B, Hkv, Lmax, D] holds token t at [b, h, t];
+    v_cache [B, Hkv, Lmax // 16, D, 16] holds it at [b, h, t // 16, :, t % 16]
+    (the V layout of a paged 16-token tile, tiles laid end to end). Token t's
+    address is then base + stride * t with no table to read, the
+    contiguous cache that paging is measured against [llm-serving.xyz
+    "KV-cache systems", paragraph on the price of paging; cs2680 Lecture 10,
+    Exercise 3(a)]. Attention is the same as ``paged_decode``'s over the first
+    seq_lens[b] tokens; positions at or past seq_lens[b] are never read.
+    """
+    B, Hq, D = q.shape
+    rows = range(B) if rows is None else list(rows)
+    out = np.zeros((len(rows), Hq, D))
+    for i, b in enumerate(rows):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        K = as_f64(k_cache[b, :, :L, :], dtype)                        # [Hkv, L, D]
+        V = as_f64(v_cache[b, :, t // 16, :, t % 16], dtype).transpose(1, 0, 2)
+        out[i] = decode_contiguous(as_f64(q[b], dtype), K, V, scale)
+    return out
+
+
 def paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale,
                   dtype, block_size=BLOCK_SIZE, seqs=None):
     """Chunked-prefill paged attention for a batch, in float64.
