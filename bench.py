@@ -85,6 +85,10 @@ def parse():
                          "needs the balanced split)")
     ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
                     help="physical block placement of the 8B/70B layers")
+    ap.add_argument("--kv-layout", default="paged", choices=["paged", "contiguous"],
+                    help="8B/70B layers: the paged pool, or the same values in an unpaged "
+                         "cache decoded by pa_decode_contiguous (no table; the step is the "
+                         "decode alone)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed steps in a HIP graph (one step per input copy) "
                          "and time its replays")
@@ -163,6 +167,10 @@ def main():
             workload += f"_block{args.block_size}"
         if args.placement != "random":
             workload += f"_{args.placement}"
+        contiguous_kv = args.kv_layout == "contiguous"
+        if contiguous_kv:
+            workload += "_contiguous_kv"
+            unpaged = [wl.contiguous_cache(c) for c in copies]
         outs = [torch.empty_like(c.q) for c in copies]
         dims = pk.make_dims(B, Hq, Hkv, D, case.max_blocks_per_seq, case.num_blocks,
                             pk.PA_BF16, part, kernel, case.block_size)
@@ -172,11 +180,14 @@ def main():
 
         def decode_calls(i):
             c = copies[i % len(copies)]
+            if contiguous_kv:
+                kc, vc = unpaged[i % len(copies)]
+                return [(c.q, kc, vc, None, c.seq_lens, outs[i % len(copies)])]
             return [(c.q, c.k_pool, c.v_pool, c.block_tables, c.seq_lens, outs[i % len(copies)])]
 
         def pre(i):
             c = copies[i % len(copies)]
-            if c.slot_mapping is not None:
+            if c.slot_mapping is not None and not contiguous_kv:
                 pk.pa_write_kv(c.k_new, c.v_new, c.slot_mapping, c.k_pool, c.v_pool)
     elif args.config == 6:
         case = wl.prefill_step_8b(block_size=args.block_size)
@@ -258,7 +269,7 @@ def main():
 
     def step(i, events=None, mode=None):
         mode = mode or args.step
-        fused = mode == "fused" and args.config == 2
+        fused = mode == "fused" and args.config == 2 and args.kv_layout == "paged"
         stream = torch.cuda.current_stream()  # the capture stream inside a graph capture
         if not fused:
             pre(i)
@@ -277,6 +288,8 @@ def main():
                               stream=stream)
             elif args.config == 7:
                 pk.pa_latent_decode(q, k, tb, ln, scale, o, workspace=ws, stream=stream)
+            elif tb is None:
+                pk.pa_decode_contiguous(q, k, v, ln, scale, o, workspace=ws, stream=stream)
             else:
                 pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part, kernel=kernel,
                              workspace=ws, stream=stream)
@@ -318,7 +331,8 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = timed_steps(args.step)
     other_ms = None
-    if args.config == 2 and not args.no_other_form:  # the other form, for comparison
+    if args.config == 2 and not args.no_other_form and args.kv_layout == "paged":
+        # the other form, for comparison
         other = "separate" if args.step == "fused" else "fused"
         for i in range(args.warmup):
             step(i, mode=other)
@@ -391,13 +405,16 @@ def main():
     value = kv_bytes / sec / 1e9
     bsz = (case.block_size if args.config != 7 else wl.LATENT_BLOCK) if case is not None else 16
     table_bytes = int(sum(math.ceil(int(L) / bsz) for L in lens_host)) * 4
+    unpaged_kv = args.config in (2, 4) and args.kv_layout == "contiguous"
+    if unpaged_kv:
+        table_bytes = 0  # no table is read
     per_call_alg = (kv_bytes / layers) + 2 * B * Hq * D * 2 + table_bytes + 4 * B
     latent_flops = None
     if args.config == 7:  # q read, out written (512 of 576 elements), latents, tables
         per_call_alg = kv_bytes + B * Hq * (D + wl.LATENT_VALUE_DIM) * 2 + table_bytes + 4 * B
         # scores: 2 * 576 flops, values: 2 * 512 flops per (head, cached token)
         latent_flops = int(lens_host.sum()) * Hq * 2 * (D + wl.LATENT_VALUE_DIM)
-    fused = args.config == 2 and args.step == "fused"
+    fused = args.config == 2 and args.step == "fused" and not unpaged_kv
     if fused:  # the appended tokens: k_new/v_new read, their slots written, slot ids
         T = int((case.slot_mapping >= 0).sum())
         per_call_alg += 4 * T * Hkv * D * 2 + 4 * B
@@ -455,7 +472,8 @@ def main():
             "placement": args.placement if case is not None else "random",
             "partition_tokens": part, "kernel": kernel, "graph": args.graph,
             "kv_bytes_per_step": kv_bytes,
-            "step": ("pa_decode_append (64-token KV append fused into the decode)"
+            "step": ("pa_decode_contiguous (unpaged cache, no table; no append)" if unpaged_kv
+                     else "pa_decode_append (64-token KV append fused into the decode)"
                      if fused else "pa_write_kv(64 tokens) + pa_decode" if args.config == 2
                      else "pa_decode" if args.config == 4
                      else "pa_write_kv(4096 chunk tokens) + pa_prefill" if args.config == 6
@@ -476,6 +494,8 @@ def main():
                        "latent_decode_kernel + latent_merge_kernel (one call: the decode, then "
                        "the merge of cut rows)"
                        if args.config == 7 else
+                       f"decode_mfma_balanced_kernel<{D}, contiguous> (unpaged cache; no table)"
+                       if unpaged_kv else
                        roofline_kernel(kernel, part, D) + (" with the fused KV append"
                                                            if fused else "")),
             "bound": "mfma" if args.config == 6 else "hbm",

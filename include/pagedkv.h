@@ -126,6 +126,29 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     float scale, void* out, const pa_dims* dims,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode attention over an unpaged KV cache: the same computation as
+ * pa_decode, but each (sequence, KV head) owns one contiguous run of
+ * Lmax = 16 * max_blocks_per_seq token slots, so token t of sequence b sits
+ * at base + stride * t and no table is read. This is the contiguous cache
+ * that paging is priced against: a paged kernel reads each block's table
+ * entry and then gathers the block, a contiguous one computes the address
+ * [llm-serving.xyz "KV-cache systems", paragraph on the price of paging;
+ * cs2680 Lecture 10, Exercise 3(a)].
+ *   k_cache  [B, Hkv, Lmax, D]           token-major
+ *   v_cache  [B, Hkv, Lmax / 16, D, 16]  a dim-major 16-token tile per 16
+ *                                        slots (the paged V tile's layout)
+ * Slots at or past seq_lens[b] are never used (they may hold anything). The
+ * balanced split of the matrix-core kernel only: dims->dtype bf16,
+ * block_size 16, partition_tokens 0, kernel AUTO or MFMA (else
+ * PA_ERR_UNSUPPORTED); num_blocks is not used. Workspace as pa_decode's for
+ * the same dims (pa_decode_workspace_bytes). Results are bit-identical to
+ * pa_decode's on the same values: the work split and the arithmetic are
+ * those of the paged kernel. */
+pa_status pa_decode_contiguous(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, float scale, void* out,
+                               const pa_dims* dims, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* pa_decode without a caller workspace, for callers that cannot allocate
  * device memory (code under graph capture, serving loops and harnesses that
  * forbid allocation). Same arguments, kernels and results as pa_decode,

@@ -36,7 +36,8 @@ from .build import LIB_PATH
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_LAUNCH",
     "PaDims", "PagedKVError", "SYMBOLS", "load_library", "make_dims",
-    "pa_decode", "pa_decode_append", "pa_decode_noalloc", "pa_decode_workspace_bytes",
+    "pa_decode", "pa_decode_append", "pa_decode_noalloc", "pa_decode_contiguous",
+    "pa_decode_workspace_bytes",
     "pa_prefill", "pa_write_kv", "NOALLOC_SCRATCH_BYTES",
     "pa_copy_blocks", "PaLatentDims", "make_latent_dims", "pa_latent_decode",
     "pa_latent_write", "pa_latent_workspace_bytes",
@@ -48,7 +49,8 @@ PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 BLOCK_SIZE = 16
 
-SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_noalloc", "pa_decode_append",
+SYMBOLS = ("pa_decode_workspace_bytes", "pa_decode", "pa_decode_noalloc", "pa_decode_contiguous",
+           "pa_decode_append",
            "pa_prefill",
            "pa_write_kv", "pa_copy_blocks", "pa_latent_workspace_bytes", "pa_latent_decode",
            "pa_latent_write", "pa_status_string", "pa_version")
@@ -94,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_bytes.restype = SZ
     lib.pa_decode.argtypes = [P, P, P, P, P, F32, P, D, P, SZ, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_contiguous.argtypes = [P, P, P, P, F32, P, D, P, SZ, P]
+    lib.pa_decode_contiguous.restype = ctypes.c_int
     lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, F32, P, D, P]
     lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_append.argtypes = [P, P, P, P, P, P, P, P, F32, P, D, P, SZ, P]
@@ -243,6 +247,40 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
                                   _stream(stream))
     if st != PA_OK:
         raise PagedKVError("pa_decode", st)
+    return out
+
+
+def pa_decode_contiguous(q, k_cache, v_cache, seq_lens, scale, out=None, *, workspace=None,
+                         stream=None):
+    """Decode attention over an unpaged cache: k_cache [B, Hkv, Lmax, D],
+    v_cache [B, Hkv, Lmax // 16, D, 16]; token t of row b at slot t, no
+    table. The balanced split of the matrix-core kernel (bf16)."""
+    torch = _torch()
+    _need(k_cache.dim() == 4 and v_cache.dim() == 5, "k_cache [B, Hkv, Lmax, D], "
+          "v_cache [B, Hkv, Lmax // 16, D, 16]")
+    B, Hkv, lmax, D = k_cache.shape
+    _need(lmax % BLOCK_SIZE == 0 and tuple(v_cache.shape) == (B, Hkv, lmax // BLOCK_SIZE, D,
+                                                              BLOCK_SIZE),
+          "v_cache must be [B, Hkv, Lmax // 16, D, 16] with Lmax a multiple of 16")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (q, "q")):
+        _need(t.is_contiguous() and t.is_cuda and t.dtype == k_cache.dtype,
+              f"{n} must be a contiguous device tensor of the caches' dtype")
+    _need(q.dim() == 3 and q.shape[0] == B and q.shape[2] == D, "q must be [B, Hq, D]")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,)
+          and seq_lens.is_contiguous() and seq_lens.is_cuda,
+          "seq_lens must be int32 [B] on the device")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
+          and out.is_cuda, "out must match q")
+    dims = make_dims(B, q.shape[1], Hkv, D, lmax // BLOCK_SIZE, B, _dtype_code(q), 0, "mfma")
+    workspace, ws_bytes = _workspace(dims, workspace, q.device)
+    st = load_library().pa_decode_contiguous(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                                             ctypes.byref(dims), _ptr(workspace),
+                                             ctypes.c_size_t(ws_bytes), _stream(stream))
+    if st != PA_OK:
+        raise PagedKVError("pa_decode_contiguous", st)
     return out
 
 

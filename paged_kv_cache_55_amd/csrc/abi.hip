@@ -168,15 +168,20 @@ hipError_t lds_per_workgroup(size_t* out) {
 // pa_decode, and pa_decode_append when k_new is non-null: the balanced split
 // stores each row's new token inside the decode kernel; any other plan
 // launches the KV append kernel first.
+// With `contiguous`, k_pool / v_pool are unpaged caches (pa_decode_contiguous),
+// block_tables is unused, and only the balanced split is taken.
 pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
                       const int32_t* slot_mapping, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* seq_lens, float scale,
                       void* out, const pa_dims* dims, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, bool contiguous = false) {
   Plan plan;
   pa_status st = plan_decode(dims, &plan);
   if (st != PA_OK) return st;
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
+  if (contiguous && (!plan.balanced || dims->block_size != kBlockTokens))
+    return PA_ERR_UNSUPPORTED;
+  if (!q || !k_pool || !v_pool || (!block_tables && !contiguous) || !seq_lens || !out)
+    return PA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return PA_ERR_INVALID_ARG;
@@ -232,7 +237,7 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
       return PA_ERR_UNSUPPORTED;  // the work list and parked pieces alone do not fit
   }
   const void* fn = plan.kernel == PA_KERNEL_MFMA
-                       ? decode_mfma_fn(dims->head_dim, plan.balanced, a.block_shift)
+                       ? decode_mfma_fn(dims->head_dim, plan.balanced, a.block_shift, contiguous)
                        : decode_valu_fn(dims->dtype, dims->head_dim, a.group);
   const size_t smem = plan.kernel == PA_KERNEL_MFMA
                           ? decode_mfma_smem(dims->num_seqs, a.group, dims->head_dim,
@@ -245,7 +250,7 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
     const int grid = resident < kMaxBalancedGrid ? resident : kMaxBalancedGrid;
     a.split_waves = 4 * grid;
     a.min_seg_blocks = kMinSegBlocks;
-    e = launch_decode_mfma(a, dims->head_dim, true, grid, s);
+    e = launch_decode_mfma(a, dims->head_dim, true, grid, s, contiguous);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   }
   // never more workgroups than items can exist
@@ -392,6 +397,14 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     void* stream) {
   return decode_impl(q, nullptr, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens, scale,
                      out, dims, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_contiguous(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, float scale, void* out,
+                               const pa_dims* dims, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return decode_impl(q, nullptr, nullptr, nullptr, k_cache, v_cache, nullptr, seq_lens, scale,
+                     out, dims, workspace, workspace_bytes, stream, true);
 }
 
 pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,

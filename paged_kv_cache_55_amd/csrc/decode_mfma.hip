@@ -697,8 +697,11 @@ __device__ __forceinline__ bool append_new_tokens(const DecodeArgs& a, const int
 // tile) or blocks of 16 << k tokens (1 << k tiles each). In the latter every
 // tile is contiguous in both pools: K rows [16, D] and a dim-major V tile
 // [D, 16] (longer blocks store V as one such tile per 16 tokens), both at
-// ((block * Hkv + head) * bs + 16 * sub) * D.
-enum BlockShape { kHalfTileBlocks = 0, kTileBlocks = 1 };
+// ((block * Hkv + head) * bs + 16 * sub) * D. The third shape is no paging
+// at all: each (sequence, KV head) owns one contiguous run of
+// max_blocks 16-token tiles, tile j at ((b * Hkv + head) * max_blocks + j)
+// * 16 * D in both caches, and no table is read.
+enum BlockShape { kHalfTileBlocks = 0, kTileBlocks = 1, kContiguous = 2 };
 
 template <int D, int kShape>
 __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a) {
@@ -726,7 +729,7 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   const bf16_t* kbase = (const bf16_t*)a.k_pool;
   const bf16_t* vbase = (const bf16_t*)a.v_pool;
   // flat positions count 16-token tiles, whatever the block size
-  const int sub_shift = kShape == kHalfTileBlocks ? 0 : a.block_shift - 4;
+  const int sub_shift = kShape == kTileBlocks ? a.block_shift - 4 : 0;
   const int sub_mask = (1 << sub_shift) - 1;
   const LaneOffsets<D> lo(row, kg);
 
@@ -741,7 +744,9 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
   auto table_entry = [&](const Segment& sg) {
     const size_t rowb = (size_t)sg.b * a.max_blocks;
     Phys p;
-    if (kShape == kHalfTileBlocks) {
+    if (kShape == kContiguous) {
+      p.a = p.b = 0;  // the address is a formula of (b, kvh, j)
+    } else if (kShape == kHalfTileBlocks) {
       const int j0 = 2 * sg.j;
       p.a = uniform_load(a.block_tables, rowb + j0);
       p.b = j0 + 1 < ((sg.L + 7) >> 3) ? uniform_load(a.block_tables, rowb + j0 + 1) : p.a;
@@ -752,7 +757,11 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
     return p;
   };
   auto load_tile_at = [&](Tile<D>& dst, const Segment& sg, const Phys& p) {
-    if (kShape == kHalfTileBlocks) {
+    if (kShape == kContiguous) {
+      const size_t base =
+          (((size_t)sg.b * Hkv + sg.kvh) * (size_t)a.max_blocks + (size_t)sg.j) * kTile * D;
+      load_tile<D>(dst, kbase + base, vbase + base, lo);
+    } else if (kShape == kHalfTileBlocks) {
       load_tile_two_blocks<D>(dst, kbase, vbase, ((size_t)p.a * Hkv + sg.kvh) * (8 * D),
                               ((size_t)p.b * Hkv + sg.kvh) * (8 * D), row, kg);
     } else {
@@ -850,7 +859,10 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a)
 
 }  // namespace
 
-const void* decode_mfma_fn(int head_dim, bool balanced, int block_shift) {
+const void* decode_mfma_fn(int head_dim, bool balanced, int block_shift, bool contiguous) {
+  if (contiguous)
+    return head_dim == 64 ? (const void*)&decode_mfma_balanced_kernel<64, kContiguous>
+                          : (const void*)&decode_mfma_balanced_kernel<128, kContiguous>;
   if (balanced) {
     const bool half = block_shift == 3;
     if (head_dim == 64)
@@ -870,10 +882,11 @@ size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced, in
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, int grid,
-                              hipStream_t s) {
+                              hipStream_t s, bool contiguous) {
   DecodeArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(decode_mfma_fn(head_dim, balanced, a.block_shift), dim3(grid), dim3(256), args,
+  return hipLaunchKernel(decode_mfma_fn(head_dim, balanced, a.block_shift, contiguous), dim3(grid),
+                         dim3(256), args,
                          decode_mfma_smem(a.num_seqs, a.group, head_dim, balanced,
                                           a.stage_slots), s);
 }

@@ -13,10 +13,12 @@ namespace pagedkv {
 // of (num_seqs + 1) ints for the work list.
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int grid,
                               hipStream_t s);
+// contiguous: the balanced kernel over unpaged caches (tile j of (b, kvh)
+// at ((b * Hkv + kvh) * max_blocks + j) * 16 * D; no table)
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool balanced, int grid,
-                              hipStream_t s);
+                              hipStream_t s, bool contiguous = false);
 const void* decode_valu_fn(int dtype, int head_dim, int group);
-const void* decode_mfma_fn(int head_dim, bool balanced, int block_shift);
+const void* decode_mfma_fn(int head_dim, bool balanced, int block_shift, bool contiguous = false);
 // dynamic LDS bytes of a decode_mfma launch (stage_slots: balanced split only)
 size_t decode_mfma_smem(int num_seqs, int group, int head_dim, bool balanced, int stage_slots);
 // Balanced split: fp32 record of one piece of a (sequence, KV head) pair,

@@ -320,3 +320,21 @@ def test_noalloc_rejects_bad_args_like_pa_decode(lib):
     assert noalloc_status(lib, dims(partition_tokens=0), q=None) == pk.PA_ERR_INVALID_ARG
     assert noalloc_status(lib, dims(partition_tokens=0), scale=float("nan")) == \
         pk.PA_ERR_INVALID_ARG
+
+
+def contiguous_status(lib, d, tables_unused=None):
+    return lib.pa_decode_contiguous(FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
+                                    ctypes.byref(d), FAKE, ctypes.c_size_t(1 << 30), None)
+
+
+def test_contiguous_takes_the_balanced_split_only(lib):
+    assert contiguous_status(lib, dims(partition_tokens=512)) == pk.PA_ERR_UNSUPPORTED
+    assert contiguous_status(lib, dims(partition_tokens=0, kernel="valu")) == \
+        pk.PA_ERR_UNSUPPORTED
+    assert contiguous_status(lib, dims(partition_tokens=0, block_size=32)) == \
+        pk.PA_ERR_UNSUPPORTED
+    assert contiguous_status(lib, dims(partition_tokens=0, head_dim=96)) == \
+        pk.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode_contiguous(None, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
+                                    ctypes.byref(dims(partition_tokens=0)), FAKE,
+                                    ctypes.c_size_t(1 << 30), None) == pk.PA_ERR_INVALID_ARG

@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import workloads as wl
+from workloads import to_numpy
 
 
 def _valid_mask(case):
@@ -125,3 +126,21 @@ def test_latent_case_layout_and_poison():
     b = wl.latent_decode_batch()
     assert b.q.shape == (256, 128, 576) and b.kv_pool.dtype == torch.bfloat16
     assert np.array_equal(b.seq_lens.numpy(), wl.config4_lens())
+
+
+def test_contiguous_cache_layout():
+    """The unpaged cache holds each row's tokens in order (checked against the
+    table walk) and poison everywhere past the row's length."""
+    c = wl.random_case(77, 6, 8, 2, 32, "bf16", lens=[0, 1, 15, 16, 17, 70])
+    k, v = wl.contiguous_cache(c)
+    kp, vp = to_numpy(c.k_pool), to_numpy(c.v_pool)
+    kc, vc = to_numpy(k), to_numpy(v)
+    bt = to_numpy(c.block_tables)
+    for b, L in enumerate(c.seq_lens.tolist()):
+        for t in range(L):
+            blk = bt[b, t // 16]
+            assert np.array_equal(kc[b, :, t, :], kp[blk, :, t % 16, :])
+            assert np.array_equal(vc[b, :, t // 16, :, t % 16], vp[blk, :, :, t % 16])
+        assert np.all(kc[b, :, L:, :] == 0x7FC0)
+        tt = np.arange(L, kc.shape[2])
+        assert np.all(vc[b, :, tt // 16, :, tt % 16] == 0x7FC0)

@@ -602,3 +602,30 @@ def permute_physical(case: Case, seed: int) -> Case:
         out.k_new, out.v_new = case.k_new, case.v_new
         out.slot_mapping = ns.to(torch.int32)
     return out
+
+
+def contiguous_cache(case: Case):
+    """The same K/V values as a paged case (16-token blocks), laid out as an
+    unpaged cache: k [B, Hkv, Lmax, D] with token t of row b at [b, :, t],
+    v [B, Hkv, Lmax // 16, D, 16] with it at [b, :, t // 16, :, t % 16],
+    Lmax = 16 * max_blocks_per_seq. Each row's blocks are copied whole
+    (through its table), so slots past its length keep the pool's poison,
+    and slots past its last block hold poison too. Works on the case's
+    device; a layout change only."""
+    if case.block_size != BLOCK:
+        raise ValueError("contiguous_cache takes 16-token blocks")
+    B, Hkv, D = case.num_seqs, case.num_kv_heads, case.head_dim
+    mb = case.max_blocks_per_seq
+    dev, dt = case.k_pool.device, case.k_pool.dtype
+    nan = float("nan")
+    k = torch.full((B, Hkv, mb * BLOCK, D), nan, dtype=dt, device=dev)
+    v = torch.full((B, Hkv, mb, D, BLOCK), nan, dtype=dt, device=dev)
+    lens = case.seq_lens.cpu().numpy()
+    for b in range(B):
+        nb = math.ceil(int(lens[b]) / BLOCK)
+        if nb == 0:
+            continue
+        blk = case.block_tables[b, :nb].long()
+        k[b, :, :nb * BLOCK, :] = case.k_pool[blk].permute(1, 0, 2, 3).reshape(Hkv, nb * BLOCK, D)
+        v[b, :, :nb] = case.v_pool[blk].permute(1, 0, 2, 3)
+    return k, v
