@@ -76,8 +76,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=5, choices=[2, 4, 5, 6, 7])
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
-    ap.add_argument("--partition", type=int, default=0,
-                    help="split-K partition tokens; 0 = balanced split (the default)")
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="split-K partition tokens; 0 = balanced split; -1 = the library's "
+                         "choice from the dims (the default: fixed 512-token partitions for "
+                         "batches of at most 8 rows, the balanced split above)")
     ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--block-size", type=int, default=16,
@@ -149,7 +151,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     kernel = args.kernel if args.kernel != "auto" else "mfma"
-    part = args.partition
+    part = part_call = args.partition  # part: as reported; part_call: what the calls pass
+    split_policy = "library choice (PA_PARTITION_AUTO)" if part == pk.PARTITION_AUTO else "explicit"
 
     # ---------------- inputs ----------------
     if args.config in (2, 4):
@@ -263,6 +266,11 @@ def main():
         def pre(i):
             pass
 
+    if part == pk.PARTITION_AUTO:  # the library's rule, which only the dims decide
+        fixed = kernel != "mfma" or (
+            B <= 8 and (case is None or case.block_size == 16)
+            and not (args.config in (2, 4) and args.kv_layout == "contiguous"))
+        part = 512 if fixed and args.config not in (6, 7) else 0
     if part > 0:
         workload += f"_split{part}"
     stream = torch.cuda.current_stream()
@@ -281,7 +289,7 @@ def main():
             if fused:
                 c = copies[i % len(copies)]
                 pk.pa_decode_append(q, c.k_new, c.v_new, c.slot_mapping, k, v, tb, ln, scale, o,
-                                    partition_tokens=part, kernel=kernel, workspace=ws,
+                                    partition_tokens=part_call, kernel=kernel, workspace=ws,
                                     stream=stream)
             elif args.config == 6:
                 pk.pa_prefill(q, k, v, tb, ln, copies[i % len(copies)].query_start, scale, o,
@@ -291,7 +299,7 @@ def main():
             elif tb is None:
                 pk.pa_decode_contiguous(q, k, v, ln, scale, o, workspace=ws, stream=stream)
             else:
-                pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part, kernel=kernel,
+                pk.pa_decode(q, k, v, tb, ln, scale, o, partition_tokens=part_call, kernel=kernel,
                              workspace=ws, stream=stream)
             if events is not None:
                 e1.record(stream)
@@ -470,7 +478,8 @@ def main():
             "head_dim": D, "layers": layers,
             "block_size": bsz,
             "placement": args.placement if case is not None else "random",
-            "partition_tokens": part, "kernel": kernel, "graph": args.graph,
+            "partition_tokens": part, "split_policy": split_policy, "kernel": kernel,
+            "graph": args.graph,
             "kv_bytes_per_step": kv_bytes,
             "step": ("pa_decode_contiguous (unpaged cache, no table; no append)" if unpaged_kv
                      else "pa_decode_append (64-token KV append fused into the decode)"

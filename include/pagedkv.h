@@ -77,6 +77,14 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
  * the vector-ALU kernel for f32. */
 typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_kernel;
 
+/* partition_tokens value for the library's choice, made from the dims alone
+ * (so a captured launch stays valid for any lengths): with the matrix-core
+ * kernel and 16-token blocks, batches of at most 8 rows take fixed
+ * 512-token partitions (every (row, partition, KV head) its own workgroup,
+ * merged by a separate pass) and larger batches the balanced split; the
+ * vector-ALU kernel takes 512-token partitions. */
+#define PA_PARTITION_AUTO (-1)
+
 /* Host-side dimensions; all fields are fixed for a given captured shape. */
 typedef struct {
   int32_t num_seqs;           /* B   (1 .. 4096) */
@@ -87,8 +95,11 @@ typedef struct {
                                  are taken by the balanced split only */
   int32_t max_blocks_per_seq; /* MB: row stride of block_tables (>= 1) */
   int32_t num_blocks;         /* NB: pool capacity in blocks (>= 1) */
-  int32_t partition_tokens;   /* split-K partition length: a multiple of 16,
-                                 or 0 for one partition per sequence */
+  int32_t partition_tokens;   /* split-K partition length: a multiple of 16;
+                                 0 for the balanced split (matrix-core kernel)
+                                 or one partition per sequence (vector-ALU
+                                 kernel); PA_PARTITION_AUTO for the library's
+                                 choice by dims (below) */
   int32_t dtype;              /* pa_dtype of q, pools, k_new/v_new and out */
   int32_t kernel;             /* pa_kernel */
 } pa_dims;
@@ -139,7 +150,7 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
  *                                        slots (the paged V tile's layout)
  * Slots at or past seq_lens[b] are never used (they may hold anything). The
  * balanced split of the matrix-core kernel only: dims->dtype bf16,
- * block_size 16, partition_tokens 0, kernel AUTO or MFMA (else
+ * block_size 16, partition_tokens 0 or PA_PARTITION_AUTO, kernel AUTO or MFMA (else
  * PA_ERR_UNSUPPORTED); num_blocks is not used. Workspace as pa_decode's for
  * the same dims (pa_decode_workspace_bytes). Results are bit-identical to
  * pa_decode's on the same values: the work split and the arithmetic are

@@ -36,7 +36,7 @@ from .build import LIB_PATH
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_LAUNCH",
     "PaDims", "PagedKVError", "SYMBOLS", "load_library", "make_dims",
-    "pa_decode", "pa_decode_append", "pa_decode_noalloc", "pa_decode_contiguous",
+    "PARTITION_AUTO", "pa_decode", "pa_decode_append", "pa_decode_noalloc", "pa_decode_contiguous",
     "pa_decode_workspace_bytes",
     "pa_prefill", "pa_write_kv", "NOALLOC_SCRATCH_BYTES",
     "pa_copy_blocks", "PaLatentDims", "make_latent_dims", "pa_latent_decode",
@@ -46,6 +46,7 @@ __all__ = [
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
 PA_F32, PA_BF16 = 0, 1
+PARTITION_AUTO = -1  # PA_PARTITION_AUTO: the library's split, chosen from the dims
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 BLOCK_SIZE = 16
 
@@ -227,12 +228,13 @@ def _workspace(dims, workspace, device):
 
 
 def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
-              partition_tokens=512, kernel="auto", workspace=None, stream=None):
+              partition_tokens=PARTITION_AUTO, kernel="auto", workspace=None, stream=None):
     """out[b, h] = softmax(scale * q[b, h] K_b^T) V_b over the paged K/V.
 
     ``partition_tokens`` > 0 splits each sequence into partitions of that
     many tokens; 0 asks for the balanced split (matrix-core kernel) or one
-    partition per sequence (vector-ALU kernel). A caller-provided
+    partition per sequence (vector-ALU kernel); PARTITION_AUTO (the
+    default) lets the library choose from the dims. A caller-provided
     ``workspace`` (uint8 device tensor of at least
     pa_decode_workspace_bytes bytes) must be zero-filled before its first
     use; calls leave it reusable. One workspace must not serve two calls that
@@ -285,7 +287,7 @@ def pa_decode_contiguous(q, k_cache, v_cache, seq_lens, scale, out=None, *, work
 
 
 def pa_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
-                      partition_tokens=0, kernel="auto", stream=None):
+                      partition_tokens=PARTITION_AUTO, kernel="auto", stream=None):
     """pa_decode with the library's own per-GPU scratch array as workspace:
     the library call allocates nothing (pass ``out`` to allocate nothing
     here either). Calls that may overlap in time on one GPU race."""
@@ -301,7 +303,8 @@ def pa_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None
 
 
 def pa_decode_append(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_tables, seq_lens,
-                     scale, out=None, *, partition_tokens=0, kernel="auto", workspace=None,
+                     scale, out=None, *, partition_tokens=PARTITION_AUTO, kernel="auto",
+                     workspace=None,
                      stream=None):
     """One decode step: row b's new token (k_new/v_new[b], [B, Hkv, D]) is
     stored at slot_mapping[b] (negative = none), which must be the slot of

@@ -338,3 +338,29 @@ def test_contiguous_takes_the_balanced_split_only(lib):
     assert lib.pa_decode_contiguous(None, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
                                     ctypes.byref(dims(partition_tokens=0)), FAKE,
                                     ctypes.c_size_t(1 << 30), None) == pk.PA_ERR_INVALID_ARG
+
+
+def test_auto_partition_follows_the_dims(lib):
+    """PA_PARTITION_AUTO: batches of at most 8 rows take 512-token fixed
+    partitions, larger batches (and any block size but 16) the balanced
+    split; the vector-ALU kernel takes 512-token partitions."""
+    ws = pk.pa_decode_workspace_bytes
+    for B in (1, 8, 9, 256):
+        auto = ws(dims(num_seqs=B, partition_tokens=pk.PARTITION_AUTO))
+        expect = ws(dims(num_seqs=B, partition_tokens=512 if B <= 8 else 0))
+        assert auto == expect, B
+    assert ws(dims(num_seqs=4, block_size=32, partition_tokens=pk.PARTITION_AUTO)) == \
+        ws(dims(num_seqs=4, block_size=32, partition_tokens=0))
+    assert ws(dims(num_seqs=64, kernel="valu", partition_tokens=pk.PARTITION_AUTO)) == \
+        ws(dims(num_seqs=64, kernel="valu", partition_tokens=512))
+    assert ws(dims(partition_tokens=-2)) == 0  # invalid
+
+
+def test_contiguous_auto_is_the_balanced_split(lib):
+    # small batch: AUTO would pick the fixed split for the paged call, but the
+    # unpaged cache has the balanced split only; still accepted (the call
+    # fails only at the fake pointers' launch, which a host test never reaches)
+    d = dims(num_seqs=4, partition_tokens=pk.PARTITION_AUTO)
+    assert lib.pa_decode_contiguous(None, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
+                                    ctypes.byref(d), FAKE, ctypes.c_size_t(1 << 30),
+                                    None) == pk.PA_ERR_INVALID_ARG

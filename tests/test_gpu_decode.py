@@ -276,3 +276,16 @@ def test_abi_error_reaches_python():
                      workspace=torch.empty(8, dtype=torch.uint8, device="cuda"))
     with pytest.raises(ValueError):
         pk.pa_decode(c.q.float(), c.k_pool, c.v_pool, c.block_tables, c.seq_lens, c.scale)
+
+
+@pytest.mark.parametrize("B", [1, 8, 9, 40])
+def test_auto_split_is_the_documented_choice(B):
+    """PA_PARTITION_AUTO gives bit for bit the split it documents: fixed
+    512-token partitions up to 8 rows, the balanced split above; and meets
+    the oracle's bar."""
+    c = wl.random_case(470 + B, B, 32, 8, 128, "bf16", max_len=3000)
+    ref, _, _ = oracle_step(c)
+    auto, _, _ = run_step(c, kernel="mfma", partition_tokens=pk.PARTITION_AUTO)
+    chosen, _, _ = run_step(c, kernel="mfma", partition_tokens=512 if B <= 8 else 0)
+    assert torch.equal(auto.view(torch.int16), chosen.view(torch.int16))
+    compare(gpu_out_f64(auto), ref, c.seq_lens.numpy(), "bf16")
