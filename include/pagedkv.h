@@ -285,8 +285,9 @@ typedef struct {
 
 /* Bytes of device workspace pa_latent_decode needs: per row a description
  * of its pieces, then partial
- * records (each piece's output normalised by its own sum, and its max and
- * sum, all fp32, for 128 heads) for two pieces per workgroup of a grid
+ * records (each piece's output normalised by its own sum and scaled per
+ * head by a power of two, as fp16, then its max, sum and inverse scale as
+ * fp32, for 128 heads) for two pieces per workgroup of a grid
  * of at most 256. Every call writes what it reads back (no zero-fill
  * needed). Calls that may overlap in time need separate workspaces.
  * Returns 0 for invalid dims (pa_latent_decode reports those). */

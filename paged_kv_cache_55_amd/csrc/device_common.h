@@ -185,8 +185,9 @@ struct LatentArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;                   // [B, H, 512]
-  // cut rows: records of two piece slots per workgroup (fp32 O[h][d]
-  // normalised by the piece's sum, then fp32 m[H] and l[H]) and per row a
+  // cut rows: records of two piece slots per workgroup (fp16 O[h][d]
+  // normalised by the piece's sum and scaled per head by a power of two,
+  // then fp32 m[H], l[H] and the inverse scales s[H]) and per row a
   // description of its pieces (first slot, count), written by every call
   // for the rows with tokens
   void* ws_rec;

@@ -34,8 +34,9 @@
 // unit), equal in cost: a row's tiles plus kFinishSlots tiles' worth for
 // writing it, so that workgroups with many short rows take fewer tiles. A
 // row cut by range boundaries leaves one record per piece (its output
-// normalised by the piece's sum, its max and its sum, all fp32: 257 KiB, as
-// much as 228 tokens of latent cache) and a description of its pieces; a
+// normalised by the piece's sum, scaled per head by a power of two and
+// stored as fp16, then its max, sum and scale in fp32: 129.5 KiB, as
+// much as 115 tokens of latent cache) and a description of its pieces; a
 // second kernel merges each cut row in parallel over its heads. No
 // workgroup waits for another, and no merge sits at the end of a range.
 #include <type_traits>
@@ -432,32 +433,58 @@ __device__ __forceinline__ void store_scaled(const LatentArgs& a, const float4_t
   }
 }
 
-// Record of a piece: x[h][d] = O / l, then m[H], then l[H], all fp32 (a bf16
-// x added its rounding to the output's in rows merged from partly
-// cancelling pieces).
+// Record of a piece: y[h][d] = (O / l) 2^k_h as fp16, then m[H], l[H] and
+// s[H] = 2^-k_h as fp32. k_h puts the head's largest |O / l| in
+// [2^14, 2^15): the scaling is exact, no finite value overflows fp16, and
+// each element keeps fp16's 2^-11 relative rounding, a quarter of bf16's
+// (bf16 records added their rounding to the output's in rows merged from
+// partly cancelling pieces).
 __device__ __forceinline__ int record_base(int slot) { return slot * kRecordBytes; }
 __device__ __forceinline__ int record_x(int slot, int h, int d) {
-  return record_base(slot) + (h * kValue + d) * 4;
+  return record_base(slot) + (h * kValue + d) * 2;
 }
 __device__ __forceinline__ int record_m(int slot, int h) {
-  return record_base(slot) + kHeads * kValue * 4 + h * 4;
+  return record_base(slot) + kHeads * kValue * 2 + h * 4;
 }
 __device__ __forceinline__ int record_l(int slot, int h) {
-  return record_base(slot) + kHeads * kValue * 4 + kHeads * 4 + h * 4;
+  return record_base(slot) + kHeads * kValue * 2 + kHeads * 4 + h * 4;
+}
+__device__ __forceinline__ int record_s(int slot, int h) {
+  return record_base(slot) + kHeads * kValue * 2 + 2 * kHeads * 4 + h * 4;
 }
 
-__device__ __forceinline__ void store_rec16(__amdgpu_buffer_rsrc_t rec, int off, float4_t v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rec, off, 0, 0);
+__device__ __forceinline__ void store_rec8(__amdgpu_buffer_rsrc_t rec, int off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rec, off, 0, 0);
 }
 __device__ __forceinline__ void store_rec(__amdgpu_buffer_rsrc_t rec, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rec, off, 0, 0);
 }
 
-// A piece's normalised output chunk (4 dims of one head): what its record
-// holds.
-__device__ __forceinline__ float4_t normalised_chunk(float4_t o, float inv) { return o * inv; }
+// k with max_abs 2^k in [2^14, 2^15), as the fp32 power 2^k; 1 for a zero
+// or non-finite max_abs. Clamped to fp32's normal powers.
+__device__ __forceinline__ float record_scale(float max_abs) {
+  const uint32_t e = (__builtin_bit_cast(uint32_t, max_abs) >> 23) & 0xffu;  // biased exponent
+  if (!(max_abs > 0.f) || e == 0xffu) return 1.f;
+  // max_abs in [2^(e - 127), 2^(e - 126)) for e >= 1 (below for subnormals)
+  const int k = min(127, max(-126, 14 - ((int)e - 127)));
+  return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
 
 __device__ __forceinline__ float4_t zero4() { return (float4_t){0.f, 0.f, 0.f, 0.f}; }
+
+// Four fp16 (two packed pairs, low half first) as fp32, exactly.
+__device__ __forceinline__ float4_t f16x4_to_f32(uint32_t lo, uint32_t hi) {
+  return (float4_t){(float)__builtin_bit_cast(_Float16, (uint16_t)(lo & 0xffffu)),
+                    (float)__builtin_bit_cast(_Float16, (uint16_t)(lo >> 16)),
+                    (float)__builtin_bit_cast(_Float16, (uint16_t)(hi & 0xffffu)),
+                    (float)__builtin_bit_cast(_Float16, (uint16_t)(hi >> 16))};
+}
 
 // x * w + acc elementwise, one rounding each (the merge's only operation,
 // so that its result depends on the pieces' order alone)
@@ -473,13 +500,26 @@ __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slo
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int h = h0 + 16 * ht + col;
-    const float inv = 1.f / ltot[ht];
+    // the head's largest |O|: this lane's 4 dims of every dim tile, then
+    // the four lanes of the head's column
+    float amax = 0.f;
 #pragma unroll
     for (int n = 0; n < kDimTiles; ++n)
-      store_rec16(rec, record_x(slot, h, 16 * n + 4 * kg), normalised_chunk(st.o[ht][n], inv));
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(st.o[ht][n][0]), fabsf(st.o[ht][n][1])),
+                               fmaxf(fabsf(st.o[ht][n][2]), fabsf(st.o[ht][n][3]))));
+    const float inv = 1.f / ltot[ht];
+    const float up = record_scale(max_over_kg(amax) * inv);
+    const float mul = inv * up;
+#pragma unroll
+    for (int n = 0; n < kDimTiles; ++n) {
+      const float4_t v = st.o[ht][n] * mul;
+      store_rec8(rec, record_x(slot, h, 16 * n + 4 * kg),
+                 make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])));
+    }
     if (kg == 0) {
       store_rec(rec, record_m(slot, h), st.m[ht]);
       store_rec(rec, record_l(slot, h), ltot[ht]);
+      store_rec(rec, record_s(slot, h), 1.f / up);
     }
   }
 }
@@ -780,9 +820,10 @@ __global__ __launch_bounds__(256) void latent_decode_kernel(LatentArgs a) {
 // ---- merging cut rows -----------------------------------------------------------
 //
 // Workgroup (b, q) writes heads 32 q .. 32 q + 31 of cut row b: out = sum_i
-// w_i x_i over the row's pieces in piece order, x_i a piece's normalised
-// output as its record holds it (fp32), w_i = l_i 2^(m_i - M) / L
-// (log-sum-exp merge), one fused multiply-add per piece and element. Thread
+// w_i y_i over the row's pieces in piece order, y_i a piece's scaled
+// normalised output as its record holds it (fp16), w_i = s_i l_i
+// 2^(m_i - M) / L (log-sum-exp merge, with the piece's inverse scale), one
+// fused multiply-add per piece and element. Thread
 // t takes head 32 q + t / 8 and 8 chunks of 8 dims (dims 64 j + 8 (t % 8)
 // .. + 7, j = 0..7); the record loads of kMergePieces pieces go out
 // together. Rows that are whole or empty are left as the decode kernel
@@ -805,13 +846,14 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   // merged max and sum of the head, in piece order: every (m, l) in one
   // round trip when the row has at most kFewPieces pieces
   float M = -INFINITY, Lsum = 0.f;
-  float mv[kFewPieces], lv[kFewPieces];
+  float mv[kFewPieces], lv[kFewPieces], sv[kFewPieces];
   if (n <= kFewPieces) {
 #pragma unroll
     for (int k = 0; k < kFewPieces; ++k) {
       const bool in = k < n;
       mv[k] = in ? load_f(record_m(slot_of(k), h)) : -INFINITY;
       lv[k] = in ? load_f(record_l(slot_of(k), h)) : 0.f;
+      sv[k] = in ? load_f(record_s(slot_of(k), h)) : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < kFewPieces; ++k) M = fmaxf(M, mv[k]);
@@ -831,35 +873,32 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   for (int j = 0; j < 8; ++j) acc[j][0] = acc[j][1] = zero4();
   for (int i0 = 0; i0 < n; i0 += kMergePieces) {
     float w[kMergePieces];
-    float4_t x[kMergePieces][8][2];
+    u32x4_t x[kMergePieces][8];
 #pragma unroll
     for (int k = 0; k < kMergePieces; ++k) {
       if (i0 + k >= n) break;
       const int sl = slot_of(i0 + k);
       if (n <= kFewPieces) {  // weights from the registers (i0 + k < kFewPieces)
-        float mk = mv[0], lk = lv[0];
+        float mk = mv[0], lk = lv[0], sk = sv[0];
 #pragma unroll
         for (int u = 1; u < kFewPieces; ++u)
-          if (u == i0 + k) mk = mv[u], lk = lv[u];
-        w[k] = lk * fast_exp2(mk - M) * invL;
+          if (u == i0 + k) mk = mv[u], lk = lv[u], sk = sv[u];
+        w[k] = sk * (lk * fast_exp2(mk - M) * invL);
       } else {
-        w[k] = load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M) * invL;
+        w[k] = load_f(record_s(sl, h)) *
+               (load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M) * invL);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          x[k][j][e] = __builtin_bit_cast(
-              float4_t,
-              __builtin_amdgcn_raw_buffer_load_b128(rec, record_x(sl, h, 64 * j + d0 + 4 * e), 0, 0));
+        x[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rec, record_x(sl, h, 64 * j + d0), 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < kMergePieces; ++k) {
       if (i0 + k >= n) break;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        acc[j][0] = fma4(x[k][j][0], w[k], acc[j][0]);
-        acc[j][1] = fma4(x[k][j][1], w[k], acc[j][1]);
+        acc[j][0] = fma4(f16x4_to_f32(x[k][j][0], x[k][j][1]), w[k], acc[j][0]);
+        acc[j][1] = fma4(f16x4_to_f32(x[k][j][2], x[k][j][3]), w[k], acc[j][1]);
       }
     }
   }

@@ -67,9 +67,10 @@ constexpr int kLatentBlockTokens = 64;
 constexpr int kLatentTileTokens = 32;
 constexpr int kLatentStageBytes = 39 * 1024;
 constexpr int kLatentStages = 3;
-// record of one piece of a cut row: its output normalised by its own sum,
-// fp32 [H][512], then fp32 max m[H] and sum l[H] (257 KiB)
-constexpr int kLatentRecordBytes = kLatentHeads * kLatentValueDim * 4 + 2 * kLatentHeads * 4;
+// record of one piece of a cut row: its output normalised by its own sum
+// and scaled per head by a power of two, fp16 [H][512], then fp32 max m[H],
+// sum l[H] and inverse scale s[H] (129.5 KiB)
+constexpr int kLatentRecordBytes = kLatentHeads * kLatentValueDim * 2 + 3 * kLatentHeads * 4;
 const void* latent_decode_fn();
 size_t latent_decode_smem(int num_seqs);
 hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t s);

@@ -243,7 +243,7 @@ def latent_dims(**kw):
 def test_latent_workspace_size(lib):
     align = lambda x: (x + 255) // 256 * 256
     B = 256
-    rec = 128 * 512 * 4 + 2 * 128 * 4  # normalised output, max and sum, all fp32
+    rec = 128 * 512 * 2 + 3 * 128 * 4  # scaled output (fp16), then max, sum, scale (fp32)
     off_rec = align(2 * B * 4)  # piece descriptors [B][2], then the records
     assert pk.pa_latent_workspace_bytes(latent_dims()) == off_rec + 2 * 256 * rec
     assert pk.pa_latent_workspace_bytes(latent_dims(num_heads=64)) == 0
