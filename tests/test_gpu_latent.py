@@ -54,6 +54,20 @@ def test_latent_many_cuts():
     check(wl.latent_case(1002, rng.integers(1, 3000, size=40)))
 
 
+@pytest.mark.parametrize("shift", [20, -40])
+def test_latent_records_out_of_fp16_range(shift):
+    """Latents 2^20 times larger (values past fp16's largest, 65504) or
+    2^-40 times smaller (past its smallest normal) in rows cut into many
+    pieces: the pieces' records are fp16 scaled per head by a power of two,
+    so neither overflows nor flushes. The queries take the inverse factor,
+    so every score is the same (both factors are exact in bf16)."""
+    c = wl.latent_case(1010 + abs(shift), [5000, 3000, 40, 6000])
+    c.kv_pool = c.kv_pool * (2.0 ** shift)
+    c.q = c.q * (2.0 ** -shift)
+    assert c.kv_pool.dtype == torch.bfloat16 and c.q.dtype == torch.bfloat16
+    check(c)
+
+
 @pytest.mark.parametrize("lens", [[20000], [20000, 5, 7000, 0]])
 def test_latent_long_rows_over_many_workgroups(lens):
     """A 20,000-token row is 625 tiles, spread over dozens of workgroups."""
