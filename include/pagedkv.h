@@ -106,7 +106,8 @@ typedef struct {
 
 /* Bytes of device workspace pa_decode needs for these dims.
  *   Fixed split (partition_tokens > 0, or the vector-ALU kernel): 0 when
- *   every sequence fits one partition, else fp32 partial results (max, sum,
+ *   every sequence fits one partition, else int32 partition counters for
+ *   every (sequence, KV head), then fp32 partial results (max, sum,
  *   unnormalised output) of every (sequence, query head, partition).
  *   Balanced split (matrix-core kernel, partition_tokens == 0): int32 piece
  *   counters for every (sequence, KV head), then fp32 partials for two
@@ -122,10 +123,13 @@ size_t pa_decode_workspace_bytes(const pa_dims* dims);
  * over t < seq_lens[b], with K_b/V_b gathered through block_tables[b]
  * (naive softmax over the whole row; computed with an online softmax per
  * piece of the sequence and a log-sum-exp merge across pieces, fp32
- * accumulation). Pieces are fixed partitions of partition_tokens tokens,
- * or, with partition_tokens == 0 and the matrix-core kernel, the balanced
- * split: every wave of a persistent grid streams an equal share of all
- * blocks and the last wave to finish a cut sequence merges its pieces.
+ * accumulation). Pieces are fixed partitions of partition_tokens tokens
+ * (with the matrix-core kernel the last partition of a sequence to finish
+ * merges them in the same kernel; the vector-ALU kernel merges in a second
+ * kernel), or, with partition_tokens == 0 and the matrix-core kernel, the
+ * balanced split: every wave of a persistent grid streams an equal share
+ * of all blocks and the last wave to finish a cut sequence merges its
+ * pieces.
  * Results do not depend on timing: pieces merge in a fixed order.
  * Rows with seq_lens[b] == 0 get zeros. Slots at or past seq_lens[b] never
  * reach the result (they are masked, so they may hold anything, NaN

@@ -124,10 +124,13 @@ pa_status plan_decode(const pa_dims* d, Plan* p, bool balanced_only = false) {
     p->ws_bytes = p->off_m = p->off_l = p->off_o = 0;
     return PA_OK;
   }
+  // partition counters per (sequence, KV head) (the matrix-core kernel
+  // merges in place; the vector-ALU kernel leaves them to the reduce
+  // kernel), then the partials: m, l, unnormalised output
   const size_t rows = (size_t)d->num_seqs * d->num_q_heads * p->num_parts;
-  p->off_m = 0;
-  p->off_l = align_up(rows * sizeof(float));
-  p->off_o = 2 * p->off_l;
+  p->off_m = align_up((size_t)d->num_seqs * d->num_kv_heads * sizeof(int));
+  p->off_l = p->off_m + align_up(rows * sizeof(float));
+  p->off_o = p->off_l + align_up(rows * sizeof(float));
   p->ws_bytes = p->off_o + rows * (size_t)d->head_dim * sizeof(float);
   return PA_OK;
 }
@@ -215,7 +218,7 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
   a.ws_m = plan.ws_bytes && !plan.balanced ? (float*)(ws + plan.off_m) : nullptr;
   a.ws_l = plan.ws_bytes && !plan.balanced ? (float*)(ws + plan.off_l) : nullptr;
   a.ws_o = plan.ws_bytes ? (float*)(ws + plan.off_o) : nullptr;
-  a.ws_cnt = plan.balanced ? (int*)(ws + plan.off_cnt) : nullptr;
+  a.ws_cnt = plan.ws_bytes ? (int*)(ws + plan.off_cnt) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = dims->num_seqs;
   a.num_q_heads = dims->num_q_heads;
@@ -279,7 +282,7 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
   else
     e = launch_decode_valu(a, dims->dtype, dims->head_dim, grid, s);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
-  if (plan.num_parts > 1) {
+  if (plan.num_parts > 1 && plan.kernel != PA_KERNEL_MFMA) {
     e = launch_decode_reduce(a, dims->dtype, dims->head_dim, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
@@ -436,11 +439,13 @@ pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_poo
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
   void* ws = nullptr;
   if (scratch_address(&ws) != hipSuccess) return PA_ERR_LAUNCH;
-  if (plan.balanced) {
-    // the piece counters must start at zero; the previous call on this GPU
-    // left them so unless it failed, and the fill makes it certain
-    const hipError_t e = launch_zero_fill((char*)ws + plan.off_cnt, plan.off_o - plan.off_cnt,
-                                          (hipStream_t)stream);
+  if (plan.ws_bytes > 0) {
+    // the piece or partition counters must start at zero; the previous call
+    // on this GPU left them so unless it failed or had other dims, and the
+    // fill makes it certain
+    const size_t end = plan.balanced ? plan.off_o : plan.off_m;
+    const hipError_t e =
+        launch_zero_fill((char*)ws + plan.off_cnt, end - plan.off_cnt, (hipStream_t)stream);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   return decode_impl(q, nullptr, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens, scale,

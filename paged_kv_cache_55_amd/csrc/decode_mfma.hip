@@ -29,7 +29,10 @@
 // holds at once):
 //   fixed     (partition_tokens > 0): items are (sequence, partition,
 //             KV head); a workgroup's 4 waves share an item, take its blocks
-//             round robin and merge through LDS (worklist.h);
+//             round robin and merge through LDS (worklist.h). A sequence
+//             over several partitions leaves one fp32 partial per
+//             partition, and the item that completes a pair's count (an
+//             atomic per pair) merges them: one kernel, no reduce pass;
 //   balanced  (partition_tokens == 0): the blocks of all (sequence, KV head)
 //             pairs are laid end to end and every wave streams an equal
 //             contiguous range of them, prefetching across pair boundaries.
@@ -220,10 +223,63 @@ __device__ __forceinline__ void zero_padded_rows(const DecodeArgs& a, const int*
 // fixed partitions
 // ===========================================================================
 
+// Partials of the fixed split cross workgroups on different XCDs, whose L2
+// caches are not coherent with each other: they are stored and loaded as
+// agent-scope relaxed atomics, which the L2 keeps coherent at the device
+// level (sc1) without flushing or invalidating it.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merges the nparts partitions of (sequence b, the G heads from h0) into
+// the bf16 output, in partition order, kB at a time: a batch's loads go
+// out together and fold into a running max, sum and output rescaled as in
+// the online softmax.
+template <int D, int kB>
+__device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int b, int h0, int nparts,
+                                                 int tid) {
+  const int G = a.group;
+  bf16_t* out = (bf16_t*)a.out;
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    const size_t r0 = ((size_t)b * a.num_q_heads + h0 + g) * a.num_parts;
+    float M = -INFINITY, lsum = 0.f, o = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += kB) {
+      float mv[kB], lv[kB], ov[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const bool in = p0 + k < nparts;
+        const size_t r = r0 + (in ? p0 + k : 0);
+        mv[k] = in ? load_partial(a.ws_m + r) : -INFINITY;
+        lv[k] = in ? load_partial(a.ws_l + r) : 0.f;
+        ov[k] = in ? load_partial(a.ws_o + r * D + d) : 0.f;
+      }
+      float Mb = M;
+#pragma unroll
+      for (int k = 0; k < kB; ++k) Mb = fmaxf(Mb, mv[k]);
+      const float f = fast_exp2(M - Mb);  // 0 before the first batch
+      lsum *= f;
+      o *= f;
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const float e = fast_exp2(mv[k] - Mb);  // 0 past the last partition
+        lsum = fmaf(lv[k], e, lsum);
+        o = fmaf(ov[k], e, o);
+      }
+      M = Mb;
+    }
+    out[((size_t)b * a.num_q_heads + h0 + g) * D + d].bits = f32_to_bf16_bits(o / lsum);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, int part, int L,
                                            float (*red_m)[kTile], float (*red_l)[kTile],
-                                           float (*red_o)[kTile][D + 1]) {
+                                           float (*red_o)[kTile][D + 1], int* last) {
   constexpr int NDT = Tile<D>::kDimTiles;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,14 +362,41 @@ __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, 
       out[((size_t)b * Hq + h0 + g) * D + d].bits = f32_to_bf16_bits(o / lsum);
     } else {
       const size_t r = ((size_t)b * Hq + h0 + g) * a.num_parts + part;
-      a.ws_o[r * D + d] = o;
+      store_partial(a.ws_o + r * D + d, o);
       if (d == 0) {
-        a.ws_m[r] = M;
-        a.ws_l[r] = lsum;
+        store_partial(a.ws_m + r, M);
+        store_partial(a.ws_l + r, lsum);
       }
     }
   }
-  __syncthreads();  // the LDS merge buffers are reused by the next item
+  if (nparts == 1) {
+    __syncthreads();  // the LDS merge buffers are reused by the next item
+    return;
+  }
+  // Count this partition once every thread's partials are stored; the item
+  // that completes the count merges the pair's partitions (in a batch as
+  // large as their number, up to 16) and rearms the counter for the next
+  // call. No workgroup waits for another.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    int* cnt = a.ws_cnt + (size_t)b * a.num_kv_heads + kvh;
+    *last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            nparts - 1;
+  }
+  __syncthreads();
+  if (*last) {
+    if (nparts <= 4)
+      merge_partitions<D, 4>(a, b, h0, nparts, tid);
+    else if (nparts <= 8)
+      merge_partitions<D, 8>(a, b, h0, nparts, tid);
+    else
+      merge_partitions<D, 16>(a, b, h0, nparts, tid);
+    if (tid == 0)
+      __hip_atomic_store(a.ws_cnt + (size_t)b * a.num_kv_heads + kvh, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();  // the LDS merge buffers and `last` are reused by the next item
 }
 
 template <int D>
@@ -323,6 +406,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ float red_m[kWaves][kTile];
   __shared__ float red_l[kWaves][kTile];
   __shared__ float red_o[kWaves][kTile][D + 1];
+  __shared__ int last;
 
   const int B = a.num_seqs;
   build_partition_prefix(a.seq_lens, B, a.part_tokens, prefix, scan_scratch);
@@ -335,7 +419,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int kvh = item - j * Hkv;
     const int b = find_sequence(prefix, B, j);
     const int bu = __builtin_amdgcn_readfirstlane(b);
-    fixed_item<D>(a, bu, kvh, j - prefix[bu], uniform_load(a.seq_lens, bu), red_m, red_l, red_o);
+    fixed_item<D>(a, bu, kvh, j - prefix[bu], uniform_load(a.seq_lens, bu), red_m, red_l, red_o,
+                  &last);
   }
 }
 

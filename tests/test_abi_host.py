@@ -66,7 +66,12 @@ def test_workspace_size(lib):
     nparts = 4096 // 512
     rows = 64 * 32 * nparts
     align = lambda x: (x + 255) // 256 * 256
-    assert pk.pa_decode_workspace_bytes(d) == 2 * align(rows * 4) + rows * 128 * 4
+    # fixed split: int32 partition counters per (sequence, KV head), then
+    # fp32 m, l and unnormalised outputs per (sequence, query head, partition)
+    assert pk.pa_decode_workspace_bytes(d) == \
+        align(64 * 8 * 4) + 2 * align(rows * 4) + rows * 128 * 4
+    assert pk.pa_decode_workspace_bytes(dims(kernel="valu")) == \
+        align(64 * 8 * 4) + 2 * align(rows * 4) + rows * 128 * 4
     # balanced split (matrix-core kernel, partition_tokens = 0): int32
     # counters per (sequence, KV head), then one fp32 record (G x D outputs,
     # G maxima, G sums, padded to 4 floats) per piece slot, two slots per

@@ -251,21 +251,38 @@ def test_balanced_many_pieces(lens, hq, hkv):
     compare(gpu_out_f64(out), ref, lens, "bf16")
 
 
-def test_workspace_reuse_across_calls():
-    """The balanced split's counters return to zero: one workspace serves a
-    sequence of different batches."""
+@pytest.mark.parametrize("lens", [[70000], [70000, 3, 0, 2000]])
+def test_fixed_many_partitions(lens):
+    """512-token partitions: a 70,000-token row is 137 partitions, merged in
+    the decode kernel by the last one to finish, 16 at a time."""
+    c = wl.random_case(455 + len(lens), len(lens), 32, 8, 128, "bf16", lens=lens)
+    ref, _, _ = oracle_step(c)
+    out, _, _ = run_step(c, kernel="mfma", partition_tokens=512)
+    compare(gpu_out_f64(out), ref, lens, "bf16")
+
+
+@pytest.mark.parametrize("partition", [0, 512, 64])
+def test_workspace_reuse_across_calls(partition):
+    """The piece counters of the balanced split and the partition counters
+    of the fixed split return to zero: one workspace serves a sequence of
+    different batches, each repeated bit for bit."""
     cases = [wl.random_case(500 + i, 7, 32, 8, 128, "bf16", max_len=3000) for i in range(3)]
     refs = [oracle_step(c)[0] for c in cases]
     dims = pk.make_dims(7, 32, 8, 128, max(c.max_blocks_per_seq for c in cases),
-                        max(c.num_blocks for c in cases), pk.PA_BF16, 0, "mfma")
+                        max(c.num_blocks for c in cases), pk.PA_BF16, partition, "mfma")
     ws = torch.zeros(pk.pa_decode_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    first = {}
     for rep in range(3):
-        for c, ref in zip(cases, refs):
+        for i, (c, ref) in enumerate(zip(cases, refs)):
             d = c.to("cuda")
             out = pk.pa_decode(d.q, d.k_pool, d.v_pool, d.block_tables, d.seq_lens, c.scale,
-                               partition_tokens=0, kernel="mfma", workspace=ws)
+                               partition_tokens=partition, kernel="mfma", workspace=ws)
             torch.cuda.synchronize()
             compare(gpu_out_f64(out), ref, c.seq_lens.numpy(), "bf16")
+            if rep == 0:
+                first[i] = out.clone()
+            else:
+                assert torch.equal(out.view(torch.int16), first[i].view(torch.int16))
 
 
 def test_abi_error_reaches_python():
