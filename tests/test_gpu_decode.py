@@ -261,6 +261,17 @@ def test_fixed_many_partitions(lens):
     compare(gpu_out_f64(out), ref, lens, "bf16")
 
 
+def test_fixed_merge_batch_boundaries():
+    """Rows of 4, 5, 8, 9, 16, 17 and 33 partitions of 64 tokens, exact and
+    one token past: each merge batch size (4, 8, 16) at its edges, and
+    several rounds of 16."""
+    lens = [p * 64 + e for p in (4, 5, 8, 9, 16, 17, 33) for e in (0, 1)]
+    c = wl.random_case(457, len(lens), 32, 8, 128, "bf16", lens=lens)
+    ref, _, _ = oracle_step(c)
+    out, _, _ = run_step(c, kernel="mfma", partition_tokens=64)
+    compare(gpu_out_f64(out), ref, lens, "bf16")
+
+
 @pytest.mark.parametrize("partition", [0, 512, 64])
 def test_workspace_reuse_across_calls(partition):
     """The piece counters of the balanced split and the partition counters
