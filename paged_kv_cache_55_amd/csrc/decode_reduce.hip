@@ -6,6 +6,8 @@
 //   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
 // taken in partition order, so reruns are bit-identical. Sequences with at
 // most one partition were finished by the partition kernel and are skipped.
+// The vector-ALU kernel's fixed split uses this pass; the matrix-core
+// kernel merges its partitions in place.
 #include "launch.h"
 
 namespace pagedkv {
