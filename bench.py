@@ -60,7 +60,7 @@ MFMA_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s per layer"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
-    "mfma": ["decode_mfma.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
+    "mfma": ["decode_mfma.hip", "device_common.h", "worklist.h", "launch.h"],
     "valu": ["decode_valu.hip", "decode_reduce.hip", "device_common.h", "worklist.h", "launch.h"],
     "latent": ["latent_mfma.hip", "lds_stream.h", "mfma_tile.h", "device_common.h", "worklist.h",
                "launch.h"],
