@@ -150,7 +150,8 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   float* ws_o;
-  int* ws_cnt;   // balanced split: pieces finished per (b, kvh); zero between calls
+  int* ws_cnt;   // pieces (balanced) or partitions (fixed, matrix-core kernel) finished
+                 // per (b, kvh); zero between calls
   float scale_log2;  // scale * log2(e)
   int num_seqs, num_q_heads, num_kv_heads, group, max_blocks, part_tokens, num_parts;
   int split_waves;     // balanced split: waves of the decode grid (4 per workgroup)
