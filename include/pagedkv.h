@@ -113,9 +113,12 @@ typedef struct {
  *   counters for every (sequence, KV head), then fp32 partials for two
  *   pieces per wave of the decode grid (at most 1024 waves).
  * The workspace must be zero-filled before its first use; every pa_decode
- * call leaves it zero where it must be (the counters), so it can be reused
- * without clearing. Calls that may overlap in time need separate
- * workspaces. Returns 0 for invalid dims as well; pa_decode reports those. */
+ * call leaves its counters at zero, so it can be reused without clearing by
+ * calls with the same dims. A call with other dims (another batch size, KV
+ * head count, partition size or split) may find its counters where the
+ * previous layout kept partials: zero-fill the workspace again before it.
+ * Calls that may overlap in time need separate workspaces. Returns 0 for
+ * invalid dims as well; pa_decode reports those. */
 size_t pa_decode_workspace_bytes(const pa_dims* dims);
 
 /* Paged decode attention: for every sequence b and query head h,

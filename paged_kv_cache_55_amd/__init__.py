@@ -237,8 +237,9 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out=None, *,
     default) lets the library choose from the dims. A caller-provided
     ``workspace`` (uint8 device tensor of at least
     pa_decode_workspace_bytes bytes) must be zero-filled before its first
-    use; calls leave it reusable. One workspace must not serve two calls that
-    can run at the same time.
+    use; calls with the same dims leave it reusable (zero-fill it again
+    before a call with other dims or another split). One workspace must not
+    serve two calls that can run at the same time.
     """
     dims, out = _decode_dims(q, k_pool, v_pool, block_tables, seq_lens, out,
                              partition_tokens, kernel)
