@@ -59,3 +59,33 @@ def test_latent_streaming_loop_has_no_scratch_reloads(tmp_path):
     assert len(steps) >= 10, "the score steps with a tile refill were not found"
     bad = [i for i, b in enumerate(steps) if any(x.startswith("scratch_load") for x in b)]
     assert not bad, f"{len(bad)} of {len(steps)} score steps reload from scratch"
+
+
+def kernel_metadata(asm):
+    """Per kernel: the scratch bytes per lane and the VGPRs spilled, from the
+    code object's metadata."""
+    meta = {}
+    for chunk in asm.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", chunk).group(1)
+        scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", chunk).group(1))
+        spills = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", chunk).group(1))
+        meta[name] = (scratch, spills)
+    return meta
+
+
+@pytest.mark.parametrize("src,prefix,count", [
+    ("decode_mfma.hip", "_ZN7pagedkv12_GLOBAL__N_127decode_mfma_balanced_kernel", 6),
+    ("decode_mfma.hip", "_ZN7pagedkv12_GLOBAL__N_118decode_mfma_kernel", 2),
+    ("prefill_mfma.hip", "_ZN7pagedkv12_GLOBAL__N_119prefill_mfma_kernel", 2),
+    ("latent_mfma.hip", "_ZN7pagedkv12_GLOBAL__N_119latent_merge_kernel", 1),
+])
+def test_streaming_kernels_use_no_scratch(tmp_path, src, prefix, count):
+    """The paged decode and prefill kernels keep every value in registers: a
+    scratch spill inside their tile loops would put a scratch round trip and
+    a full memory wait between tile loads, the stall the latent test above
+    guards against."""
+    meta = kernel_metadata(device_asm(src, tmp_path))
+    found = {n: v for n, v in meta.items() if n.startswith(prefix)}
+    assert len(found) == count, sorted(meta)
+    bad = {n: v for n, v in found.items() if v != (0, 0)}
+    assert not bad, f"kernels with scratch bytes or VGPR spills: {bad}"
