@@ -270,7 +270,8 @@ def main():
         fixed = kernel != "mfma" or (
             B <= 8 and (case is None or case.block_size == 16)
             and not (args.config in (2, 4) and args.kv_layout == "contiguous"))
-        part = 512 if fixed and args.config not in (6, 7) else 0
+        part = (256 if kernel == "mfma" and B <= 2 else 512) if fixed and args.config not in (6, 7) \
+            else 0
     if part > 0:
         workload += f"_split{part}"
     stream = torch.cuda.current_stream()

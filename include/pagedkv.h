@@ -80,9 +80,11 @@ typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_k
 /* partition_tokens value for the library's choice, made from the dims alone
  * (so a captured launch stays valid for any lengths): with the matrix-core
  * kernel and 16-token blocks, batches of at most 8 rows take fixed
- * 512-token partitions (every (row, partition, KV head) its own workgroup,
- * merged by a separate pass) and larger batches the balanced split; the
- * vector-ALU kernel takes 512-token partitions. */
+ * partitions (every (row, partition, KV head) its own workgroup, merged in
+ * the same kernel by the last partition of a row and KV head to finish):
+ * 256 tokens for one or two rows, 512 for three to eight; larger batches
+ * take the balanced split. The vector-ALU kernel takes 512-token
+ * partitions. */
 #define PA_PARTITION_AUTO (-1)
 
 /* Host-side dimensions; all fields are fixed for a given captured shape. */

@@ -55,15 +55,21 @@ constexpr int kMinSegBlocks = 16;
 // Chunked prefill: at most this many persistent workgroups.
 constexpr int kMaxPrefillGrid = 1024;
 
-// PA_PARTITION_AUTO: batches of at most this many rows take the fixed split
-// of kAutoPartition tokens, larger ones the balanced split. A small batch
-// leaves most of the balanced split's waves idle (each streams at least
-// kMinSegBlocks tiles) and one wave merges each long row's many pieces,
-// while the fixed split gives every (row, partition, KV head) its own
-// workgroup and merges in a separate parallel pass: on the 32-layer 8B step
-// it measured 20 us per layer at buckets 1-8 against 25-31 us balanced, and
-// 12% slower at 32 rows.
+// PA_PARTITION_AUTO: batches of at most kAutoFixedRows rows take the fixed
+// split, larger ones the balanced split. A small batch leaves most of the
+// balanced split's waves idle (each streams at least kMinSegBlocks tiles)
+// and one wave merges each long row's many pieces, while the fixed split
+// gives every (row, partition, KV head) its own workgroup: on the 32-layer
+// 8B step it measured 20 us per layer at buckets 1-8 against 25-31 us
+// balanced, and 12% slower at 32 rows. One compute unit streams a
+// partition at about 30 GB/s, so a batch of one or two rows spreads over
+// more of them with 256-token partitions (bucket 1: 16.2 against 17.2 us
+// per layer; bucket 2: 12.4 against 15.6); from three rows on, 512-token
+// partitions keep the merge, which one workgroup reads at that same rate,
+// shorter (bucket 4: 17.9 against 19.1 us).
 constexpr int kAutoFixedRows = 8;
+constexpr int kAutoFewRows = 2;
+constexpr int kAutoPartitionFew = 256;
 constexpr int kAutoPartition = 512;
 
 struct Plan {
@@ -97,7 +103,9 @@ pa_status plan_decode(const pa_dims* d, Plan* p, bool balanced_only = false) {
     const bool fixed = p->kernel != PA_KERNEL_MFMA ||
                        (!balanced_only && d->block_size == kBlockTokens &&
                         d->num_seqs <= kAutoFixedRows);
-    p->partition = fixed ? kAutoPartition : 0;
+    p->partition = !fixed ? 0
+                   : p->kernel == PA_KERNEL_MFMA && d->num_seqs <= kAutoFewRows ? kAutoPartitionFew
+                                                                                 : kAutoPartition;
   }
   if (p->partition < 0 || p->partition % kBlockTokens != 0) return PA_ERR_INVALID_ARG;
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -159,6 +167,26 @@ hipError_t resident_workgroups(const void* fn, size_t smem, int* out, int thread
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, smem);
   if (e != hipSuccess) return e;
   *out = cache[key] = (ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
+  return hipSuccess;
+}
+
+// Compute units of the current device, cached per device.
+hipError_t compute_units(int* out) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  int ncu = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  *out = cache[dev] = ncu > 0 ? ncu : 1;
   return hipSuccess;
 }
 
@@ -230,6 +258,7 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
   a.split_waves = 0;
   a.min_seg_blocks = 0;
   a.stage_slots = 0;
+  a.slot_grid = 0;
   a.block_shift = block_shift(dims->block_size);
   a.k_new = nullptr;
   a.v_new = nullptr;
@@ -276,9 +305,23 @@ pa_status decode_impl(const void* q, const void* k_new, const void* v_new,
   }
   // never more workgroups than items can exist
   const long long max_items = (long long)dims->num_seqs * dims->num_kv_heads * plan.num_parts;
-  const int grid = (int)(max_items < resident ? max_items : resident);
-  if (plan.kernel == PA_KERNEL_MFMA)
+  int grid = (int)(max_items < resident ? max_items : resident);
+  if (plan.kernel == PA_KERNEL_MFMA) {
+    // When every (row, partition, KV head) slot fits on a compute unit of
+    // its own, each slot gets a workgroup and no work list is built: the
+    // row length, queries and first table entries load together. A
+    // compute unit streams at a fixed rate, so with more slots than compute
+    // units the work list's packing of the real items onto distinct
+    // compute units is worth its cost.
+    int ncu = 0;
+    e = compute_units(&ncu);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+    if (max_items <= ncu && max_items <= resident) {
+      a.slot_grid = 1;
+      grid = (int)max_items;
+    }
     e = launch_decode_mfma(a, dims->head_dim, false, grid, s);
+  }
   else
     e = launch_decode_valu(a, dims->dtype, dims->head_dim, grid, s);
   if (e != hipSuccess) return PA_ERR_LAUNCH;

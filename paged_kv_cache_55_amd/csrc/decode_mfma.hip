@@ -234,29 +234,57 @@ __device__ __forceinline__ float load_partial(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Four consecutive partial outputs, as two 8-byte loads with the same
+// coherence as load_partial.
+__device__ __forceinline__ float4_t load_partial4(const float* p) {
+  typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
+  const u64x2_t v = {
+      __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+      __hip_atomic_load((uint64_t*)(p + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+  return __builtin_bit_cast(float4_t, v);
+}
+
 // Merges the nparts partitions of (sequence b, the G heads from h0) into
-// the bf16 output, in partition order, kB at a time: a batch's loads go
-// out together and fold into a running max, sum and output rescaled as in
-// the online softmax.
+// the bf16 output. Work unit: 4 consecutive dims of one head. The T threads
+// of a unit split its partitions (thread s takes p = s, s + T, ...), load up
+// to kB of them in one memory round trip and fold them into a running max,
+// sum and output rescaled as in the online softmax; the T results are then
+// combined through LDS (`lds`: 6 floats per thread) in thread order. Every
+// partition's loads go out at once for nparts <= kB T, and the result does
+// not depend on timing.
 template <int D, int kB>
 __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int b, int h0, int nparts,
-                                                 int tid) {
+                                                 int tid, float* lds) {
+  constexpr int kQuads = D / 4;
   const int G = a.group;
-  bf16_t* out = (bf16_t*)a.out;
-  for (int idx = tid; idx < G * D; idx += blockDim.x) {
-    const int g = idx / D;
-    const int d = idx - g * D;
+  const int units = G * kQuads;
+  const int nt = blockDim.x;
+  const int T = units >= nt ? 1 : nt / units;  // threads per unit
+  const int per_pass = nt / T;                 // units per pass
+  const int s = tid % T;
+  bf16_t* out = (bf16_t*)a.out + ((size_t)b * a.num_q_heads + h0) * D;
+  for (int u0 = 0; u0 < units; u0 += per_pass) {
+    const int u = u0 + tid / T;
+    const bool on = u < units && tid < per_pass * T;
+    const int uc = min(u, units - 1);
+    const int g = uc / kQuads;
+    const int q = uc - g * kQuads;
     const size_t r0 = ((size_t)b * a.num_q_heads + h0 + g) * a.num_parts;
-    float M = -INFINITY, lsum = 0.f, o = 0.f;
-    for (int p0 = 0; p0 < nparts; p0 += kB) {
-      float mv[kB], lv[kB], ov[kB];
+    float M = -INFINITY, lsum = 0.f;
+    float4_t o = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int p0 = s; p0 < nparts; p0 += kB * T) {
+      float mv[kB], lv[kB];
+      float4_t ov[kB];
 #pragma unroll
       for (int k = 0; k < kB; ++k) {
-        const bool in = p0 + k < nparts;
-        const size_t r = r0 + (in ? p0 + k : 0);
-        mv[k] = in ? load_partial(a.ws_m + r) : -INFINITY;
-        lv[k] = in ? load_partial(a.ws_l + r) : 0.f;
-        ov[k] = in ? load_partial(a.ws_o + r * D + d) : 0.f;
+        const int p = p0 + k * T;
+        const size_t r = r0 + min(p, nparts - 1);
+        const float m = load_partial(a.ws_m + r);
+        const float l = load_partial(a.ws_l + r);
+        const float4_t v = load_partial4(a.ws_o + r * D + 4 * q);
+        mv[k] = p < nparts ? m : -INFINITY;
+        lv[k] = p < nparts ? l : 0.f;
+        ov[k] = p < nparts ? v : (float4_t){0.f, 0.f, 0.f, 0.f};
       }
       float Mb = M;
 #pragma unroll
@@ -268,18 +296,58 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int b, int
       for (int k = 0; k < kB; ++k) {
         const float e = fast_exp2(mv[k] - Mb);  // 0 past the last partition
         lsum = fmaf(lv[k], e, lsum);
-        o = fmaf(ov[k], e, o);
+        o += ov[k] * e;
       }
       M = Mb;
     }
-    out[((size_t)b * a.num_q_heads + h0 + g) * D + d].bits = f32_to_bf16_bits(o / lsum);
+    float* mine = lds + 6 * tid;
+    mine[0] = M;
+    mine[1] = lsum;
+    mine[2] = o[0];
+    mine[3] = o[1];
+    mine[4] = o[2];
+    mine[5] = o[3];
+    __syncthreads();
+    if (on && s == 0) {
+      float Mt = M;
+      for (int t = 1; t < T; ++t) Mt = fmaxf(Mt, mine[6 * t]);
+      float lt = 0.f;
+      float4_t ot = (float4_t){0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < T; ++t) {
+        const float* th = mine + 6 * t;
+        const float e = fast_exp2(th[0] - Mt);  // a thread with no partition has M = -inf
+        lt = fmaf(th[1], e, lt);
+        ot += (float4_t){th[2], th[3], th[4], th[5]} * e;
+      }
+      const float inv = 1.f / lt;
+      *(uint2*)(out + (size_t)uc * 4) =
+          make_uint2(pack_bf16x2(f32_to_bf16_bits(ot[0] * inv), f32_to_bf16_bits(ot[1] * inv)),
+                     pack_bf16x2(f32_to_bf16_bits(ot[2] * inv), f32_to_bf16_bits(ot[3] * inv)));
+    }
+    __syncthreads();
   }
 }
 
+// Table entry of the first block wave w folds in partition `part` of row b.
+// It is read before the row's length is known, so the index is kept inside
+// the row's table (a partition past the row's end reads an entry it never
+// uses).
+__device__ __forceinline__ int32_t first_entry(const DecodeArgs& a, int b, int part, int w) {
+  const int blk = part * (a.part_tokens / kBlockTokens) + w;
+  return uniform_load(a.block_tables,
+                      (size_t)b * a.max_blocks + max(0, min(blk, a.max_blocks - 1)));
+}
+
+// Partition `part` of (row b, KV head kvh), L tokens in the row; qb holds
+// the G queries (load_q) and e_first the table entry of this wave's first
+// block (first_entry), both read by the caller so that their loads overlap
+// the row length's.
 template <int D>
 __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, int part, int L,
-                                           float (*red_m)[kTile], float (*red_l)[kTile],
-                                           float (*red_o)[kTile][D + 1], int* last) {
+                                           const bf16x8_t (&qb)[Tile<D>::kQkSteps],
+                                           int32_t e_first, float (*red_m)[kTile],
+                                           float (*red_l)[kTile], float (*red_o)[kTile][D + 1],
+                                           int* last) {
   constexpr int NDT = Tile<D>::kDimTiles;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -296,8 +364,6 @@ __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, 
   const int nblk = (tok_end - tok0 + kBlockTokens - 1) / kBlockTokens;
   const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
 
-  bf16x8_t qb[Tile<D>::kQkSteps];
-  load_q<D>(qb, a, b, kvh, row, kg);
   WaveState<D> st;
   st.reset();
 
@@ -309,20 +375,23 @@ __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, 
   const size_t head_off = (size_t)kvh * tile_elems;
 
   // ping-pong over two register tiles: the loads of block i + 4 are in
-  // flight while block i is computed
+  // flight while block i is computed; each block's table entry is read a
+  // step before its loads
   const LaneOffsets<D> lo(row, kg);
   Tile<D> ta, tb;
   int i = w;
+  int32_t e_next = 0;
   if (i < nblk) {
-    const size_t base = (size_t)uniform_load(a.block_tables, bt_row + i) * block_stride + head_off;
+    const size_t base = (size_t)e_first * block_stride + head_off;
     load_tile<D>(ta, kbase + base, vbase + base, lo);
+    if (i + kWaves < nblk) e_next = uniform_load(a.block_tables, bt_row + i + kWaves);
   }
   auto step = [&](Tile<D>& cur, Tile<D>& nxt) {
     const int inext = i + kWaves;
     if (inext < nblk) {
-      const size_t base =
-          (size_t)uniform_load(a.block_tables, bt_row + inext) * block_stride + head_off;
+      const size_t base = (size_t)e_next * block_stride + head_off;
       load_tile<D>(nxt, kbase + base, vbase + base, lo);
+      if (inext + kWaves < nblk) e_next = uniform_load(a.block_tables, bt_row + inext + kWaves);
     }
     st.block(cur, qb, min(kBlockTokens, tok_end - (tok0 + i * kBlockTokens)), a.scale_log2, kg);
     i = inext;
@@ -386,12 +455,17 @@ __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, 
   }
   __syncthreads();
   if (*last) {
-    if (nparts <= 4)
-      merge_partitions<D, 4>(a, b, h0, nparts, tid);
-    else if (nparts <= 8)
-      merge_partitions<D, 8>(a, b, h0, nparts, tid);
+    // partitions per thread of a work unit (4 dims of one head)
+    const int units = G * (D / 4);
+    const int T = units >= (int)blockDim.x ? 1 : blockDim.x / units;
+    const int per_thread = (nparts + T - 1) / T;
+    float* lds = &red_o[0][0][0];
+    if (per_thread <= 4)
+      merge_partitions<D, 4>(a, b, h0, nparts, tid, lds);
+    else if (per_thread <= 8)
+      merge_partitions<D, 8>(a, b, h0, nparts, tid, lds);
     else
-      merge_partitions<D, 16>(a, b, h0, nparts, tid);
+      merge_partitions<D, 16>(a, b, h0, nparts, tid, lds);
     if (tid == 0)
       __hip_atomic_store(a.ws_cnt + (size_t)b * a.num_kv_heads + kvh, 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -409,17 +483,45 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ int last;
 
   const int B = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  bf16x8_t qb[Tile<D>::kQkSteps];
+
+  if (a.slot_grid) {
+    // A workgroup for every (row, partition, KV head) slot, empty ones
+    // included: no work list, and the row's length, the queries and the
+    // first table entries load together.
+    const int kvh = blockIdx.x % Hkv;
+    const int j = blockIdx.x / Hkv;
+    const int part = j % a.num_parts;
+    const int b = j / a.num_parts;
+    const int32_t e_first = first_entry(a, b, part, w);
+    load_q<D>(qb, a, b, kvh, lane & 15, lane >> 4);
+    const int L = uniform_load(a.seq_lens, b);
+    if (part * a.part_tokens >= L) {
+      if (part == 0) {  // a padded row (L = 0): its outputs are zero
+        bf16_t* o = (bf16_t*)a.out + ((size_t)b * a.num_q_heads + (size_t)kvh * a.group) * D;
+        for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) o[i].bits = 0;
+      }
+      return;
+    }
+    fixed_item<D>(a, b, kvh, part, L, qb, e_first, red_m, red_l, red_o, &last);
+    return;
+  }
+
   build_partition_prefix(a.seq_lens, B, a.part_tokens, prefix, scan_scratch);
   zero_padded_rows<bf16_t>(a, prefix, a.num_q_heads * D);
 
-  const int Hkv = a.num_kv_heads;
   const int nitems = prefix[B] * Hkv;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int j = item / Hkv;
     const int kvh = item - j * Hkv;
-    const int b = find_sequence(prefix, B, j);
-    const int bu = __builtin_amdgcn_readfirstlane(b);
-    fixed_item<D>(a, bu, kvh, j - prefix[bu], uniform_load(a.seq_lens, bu), red_m, red_l, red_o,
+    const int b = __builtin_amdgcn_readfirstlane(find_sequence(prefix, B, j));
+    const int part = __builtin_amdgcn_readfirstlane(j - prefix[b]);
+    const int32_t e_first = first_entry(a, b, part, w);
+    load_q<D>(qb, a, b, kvh, lane & 15, lane >> 4);
+    fixed_item<D>(a, b, kvh, part, uniform_load(a.seq_lens, b), qb, e_first, red_m, red_l, red_o,
                   &last);
   }
 }

@@ -157,6 +157,8 @@ struct DecodeArgs {
   int split_waves;     // balanced split: waves of the decode grid (4 per workgroup)
   int min_seg_blocks;  // balanced split: least blocks per wave range
   int stage_slots;     // balanced split: complete outputs a wave stages in LDS (0 = none)
+  int slot_grid;       // fixed split (matrix-core kernel): 1 when the grid has one workgroup
+                       // per (row, partition, KV head) slot, in that order, empty ones included
   int block_shift;     // log2 of the tokens per KV block (4 = 16 tokens)
   // fused KV append (balanced split): row b's new token k_new/v_new[b] is
   // stored at slot_mapping[b] (skipped when negative) before it is read;

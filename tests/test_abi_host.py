@@ -346,18 +346,23 @@ def test_contiguous_takes_the_balanced_split_only(lib):
 
 
 def test_auto_partition_follows_the_dims(lib):
-    """PA_PARTITION_AUTO: batches of at most 8 rows take 512-token fixed
-    partitions, larger batches (and any block size but 16) the balanced
-    split; the vector-ALU kernel takes 512-token partitions."""
+    """PA_PARTITION_AUTO: batches of one or two rows take 256-token fixed
+    partitions, of three to eight rows 512-token ones, larger batches (and
+    any block size but 16) the balanced split; the vector-ALU kernel takes
+    512-token partitions."""
     ws = pk.pa_decode_workspace_bytes
-    for B in (1, 8, 9, 256):
+    for B in (1, 2, 3, 8, 9, 256):
         auto = ws(dims(num_seqs=B, partition_tokens=pk.PARTITION_AUTO))
-        expect = ws(dims(num_seqs=B, partition_tokens=512 if B <= 8 else 0))
+        expect = ws(dims(num_seqs=B, partition_tokens=256 if B <= 2 else 512 if B <= 8 else 0))
         assert auto == expect, B
+    for B in (1, 2):  # the workspace sizes tell 256-token partitions from 512-token ones
+        assert ws(dims(num_seqs=B, partition_tokens=256)) != \
+            ws(dims(num_seqs=B, partition_tokens=512))
     assert ws(dims(num_seqs=4, block_size=32, partition_tokens=pk.PARTITION_AUTO)) == \
         ws(dims(num_seqs=4, block_size=32, partition_tokens=0))
-    assert ws(dims(num_seqs=64, kernel="valu", partition_tokens=pk.PARTITION_AUTO)) == \
-        ws(dims(num_seqs=64, kernel="valu", partition_tokens=512))
+    for B in (1, 64):
+        assert ws(dims(num_seqs=B, kernel="valu", partition_tokens=pk.PARTITION_AUTO)) == \
+            ws(dims(num_seqs=B, kernel="valu", partition_tokens=512))
     assert ws(dims(partition_tokens=-2)) == 0  # invalid
 
 

@@ -254,22 +254,60 @@ def test_balanced_many_pieces(lens, hq, hkv):
 @pytest.mark.parametrize("lens", [[70000], [70000, 3, 0, 2000]])
 def test_fixed_many_partitions(lens):
     """512-token partitions: a 70,000-token row is 137 partitions, merged in
-    the decode kernel by the last one to finish, 16 at a time."""
+    the decode kernel by the last one to finish over several rounds of
+    loads (each thread of a 4-dim unit takes up to 16 partitions a round)."""
     c = wl.random_case(455 + len(lens), len(lens), 32, 8, 128, "bf16", lens=lens)
     ref, _, _ = oracle_step(c)
     out, _, _ = run_step(c, kernel="mfma", partition_tokens=512)
     compare(gpu_out_f64(out), ref, lens, "bf16")
 
 
-def test_fixed_merge_batch_boundaries():
-    """Rows of 4, 5, 8, 9, 16, 17 and 33 partitions of 64 tokens, exact and
-    one token past: each merge batch size (4, 8, 16) at its edges, and
-    several rounds of 16."""
-    lens = [p * 64 + e for p in (4, 5, 8, 9, 16, 17, 33) for e in (0, 1)]
-    c = wl.random_case(457, len(lens), 32, 8, 128, "bf16", lens=lens)
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 128), (16, 1, 128), (32, 8, 64)])
+def test_fixed_merge_batch_boundaries(hq, hkv, d):
+    """The merge of a row's partitions gives each unit (4 dims of one head)
+    T = 256 / units threads (at least 1; units = G D / 4), each loading up to
+    4, 8 or 16 partitions a round. Rows of 64-token partitions at the edges
+    of each batch size and of the first round, exact and one token past
+    (one partition more), for T = 1 (two passes over the units), 2, 4 and 8."""
+    units = hq // hkv * d // 4
+    T = 1 if units >= 256 else 256 // units
+    parts = sorted({2, 4 * T, 4 * T + 1, 8 * T, 8 * T + 1, 16 * T, 16 * T + 1, 32 * T + 1})
+    lens = [p * 64 + e for p in parts for e in (0, 1)]
+    c = wl.random_case(457 + T, len(lens), hq, hkv, d, "bf16", lens=lens)
     ref, _, _ = oracle_step(c)
     out, _, _ = run_step(c, kernel="mfma", partition_tokens=64)
     compare(gpu_out_f64(out), ref, lens, "bf16")
+
+
+@pytest.mark.parametrize("lens,partition", [
+    ([5000], 256),              # one row, 20 slots per KV head, the last partition partial
+    ([0, 1000, 4096, 1], 512),  # a padded row, a partition end at a row end, a one-token row
+    ([512, 0, 3000], 512),
+])
+def test_fixed_slot_grid(lens, partition):
+    """While every (row, partition, KV head) slot fits on a compute unit of
+    its own, the fixed split gives each slot a workgroup and builds no work
+    list: slots past a row's end exit, and slot 0 of a padded row writes its
+    zeros. The same call with a block table wide enough to need the work
+    list (columns past every row's end, never read) gives the same bits,
+    and both meet the oracle's bar."""
+    c = wl.random_case(480 + len(lens), len(lens), 32, 8, 128, "bf16", lens=lens)
+    ref, _, _ = oracle_step(c)
+    d = c.to("cuda")
+    wide = torch.cat([d.block_tables, torch.zeros((len(lens), 2000), dtype=torch.int32,
+                                                  device="cuda")], dim=1).contiguous()
+    outs = []
+    for bt in (d.block_tables, wide):
+        out = torch.full_like(d.q, float("nan"))
+        pk.pa_decode(d.q, d.k_pool, d.v_pool, bt, d.seq_lens, c.scale, out,
+                     partition_tokens=partition, kernel="mfma")
+        torch.cuda.synchronize()
+        compare(gpu_out_f64(out), ref, np.asarray(lens), "bf16")
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert torch.count_nonzero(out[b].view(torch.int16)) == 0
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
 @pytest.mark.parametrize("partition", [0, 512, 64])
@@ -306,14 +344,15 @@ def test_abi_error_reaches_python():
         pk.pa_decode(c.q.float(), c.k_pool, c.v_pool, c.block_tables, c.seq_lens, c.scale)
 
 
-@pytest.mark.parametrize("B", [1, 8, 9, 40])
+@pytest.mark.parametrize("B", [1, 2, 3, 8, 9, 40])
 def test_auto_split_is_the_documented_choice(B):
     """PA_PARTITION_AUTO gives bit for bit the split it documents: fixed
-    512-token partitions up to 8 rows, the balanced split above; and meets
-    the oracle's bar."""
+    256-token partitions for one or two rows, 512-token ones up to 8 rows,
+    the balanced split above; and meets the oracle's bar."""
     c = wl.random_case(470 + B, B, 32, 8, 128, "bf16", max_len=3000)
     ref, _, _ = oracle_step(c)
     auto, _, _ = run_step(c, kernel="mfma", partition_tokens=pk.PARTITION_AUTO)
-    chosen, _, _ = run_step(c, kernel="mfma", partition_tokens=512 if B <= 8 else 0)
+    chosen, _, _ = run_step(c, kernel="mfma",
+                            partition_tokens=256 if B <= 2 else 512 if B <= 8 else 0)
     assert torch.equal(auto.view(torch.int16), chosen.view(torch.int16))
     compare(gpu_out_f64(auto), ref, c.seq_lens.numpy(), "bf16")
