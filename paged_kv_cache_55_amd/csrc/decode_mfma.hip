@@ -632,11 +632,10 @@ __device__ __forceinline__ float load_coherent_f32(__amdgpu_buffer_rsrc_t r, int
 // a time, the pieces' (m, l) and outputs are loaded in one round and folded
 // into a running (M, L, O) with the same rescaling as the online softmax,
 // so a merge of up to kBatch pieces costs one memory round trip.
-template <int D>
+template <int D, int kBatch>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, __amdgpu_buffer_rsrc_t rec,
                                              int pf, int b, int kvh, const Pieces& pc,
                                              int lane) {
-  constexpr int kBatch = 4;
   constexpr int kUnits = 2;
   const int G = a.group;
   const int n = pc.v1 - pc.v0 + 1;
@@ -831,7 +830,13 @@ __device__ __forceinline__ void publish_pieces(const DecodeArgs& a, const Pendin
     const PendingPiece& pp = k == 0 ? p0 : p1;
     const Pieces pc(pp.ps, pp.nb, chunk);
     if ((k == 0 ? old0 : old1) == pc.v1 - pc.v0) {
-      merge_pieces<D>(a, rec, pf, pp.b, pp.kvh, pc, lane);
+      const int n = pc.v1 - pc.v0 + 1;  // pieces; the batch follows their number
+      if (n <= 4)
+        merge_pieces<D, 4>(a, rec, pf, pp.b, pp.kvh, pc, lane);
+      else if (n <= 8)
+        merge_pieces<D, 8>(a, rec, pf, pp.b, pp.kvh, pc, lane);
+      else
+        merge_pieces<D, 16>(a, rec, pf, pp.b, pp.kvh, pc, lane);
       if (lane == 0)
         __hip_atomic_store(k == 0 ? cnt0 : cnt1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
