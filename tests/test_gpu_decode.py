@@ -279,6 +279,30 @@ def test_fixed_merge_batch_boundaries(hq, hkv, d):
     compare(gpu_out_f64(out), ref, lens, "bf16")
 
 
+@pytest.fixture(scope="module")
+def max_batch():
+    """4,096 rows (the most a call takes) of 0-90 tokens, a quarter empty."""
+    rng = np.random.default_rng(1101)
+    lens = rng.integers(0, 91, size=4096)
+    lens[rng.choice(4096, 1024, replace=False)] = 0
+    c = wl.random_case(1101, 4096, 32, 8, 128, "bf16", lens=lens.tolist())
+    return c, oracle_step(c)[0], lens
+
+
+@pytest.mark.parametrize("kernel,partition", [("mfma", 0), ("mfma", 512), ("valu", 512),
+                                              ("auto", pk.PARTITION_AUTO)])
+def test_max_batch_4096_rows(max_batch, kernel, partition):
+    """The most rows a call takes: the work lists' prefixes over 4,096 rows
+    fill their LDS share and each balanced range holds many whole rows.
+    Every row is compared with the oracle, and the empty rows are exactly
+    zero."""
+    c, ref, lens = max_batch
+    out, _, _ = run_step(c, kernel=kernel, partition_tokens=partition)
+    compare(gpu_out_f64(out), ref, lens, "bf16")
+    empty = torch.from_numpy(lens == 0).to(out.device)
+    assert torch.count_nonzero(out[empty].view(torch.int16)) == 0
+
+
 @pytest.mark.parametrize("lens,partition", [
     ([5000], 256),              # one row, 20 slots per KV head, the last partition partial
     ([0, 1000, 4096, 1], 512),  # a padded row, a partition end at a row end, a one-token row

@@ -82,6 +82,18 @@ def test_one_token_chunks_match_the_decode_kernel():
     compare(gpu_out_f64(out_d), ref, np.ones(24), "bf16")
 
 
+def test_prefill_4096_sequences():
+    """The most sequences a call takes: 4,096 rows with 0-90 cached tokens,
+    most appending one token (decode rows), 512 idle and 256 appending
+    seven; every query row is compared with the oracle."""
+    rng = np.random.default_rng(1102)
+    contexts = rng.integers(0, 91, size=4096)
+    chunks = np.ones(4096, dtype=np.int64)
+    chunks[rng.choice(4096, 512, replace=False)] = 0
+    chunks[rng.choice(4096, 256, replace=False)] = 7
+    check(wl.prefill_case(1102, chunks.tolist(), contexts.tolist(), 32, 8, 128))
+
+
 def test_prefill_rejects_unsupported():
     c = wl.prefill_case(971, [4], [4], 8, 2, 64, block_size=8).to("cuda")
     with pytest.raises(pk.PagedKVError):
