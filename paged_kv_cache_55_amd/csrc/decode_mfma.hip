@@ -29,10 +29,13 @@
 // holds at once):
 //   fixed     (partition_tokens > 0): items are (sequence, partition,
 //             KV head); a workgroup's 4 waves share an item, take its blocks
-//             round robin and merge through LDS (worklist.h). A sequence
-//             over several partitions leaves one fp32 partial per
-//             partition, and the item that completes a pair's count (an
-//             atomic per pair) merges them: one kernel, no reduce pass;
+//             round robin and merge through LDS. Items come from a work
+//             list (worklist.h), or, when every (sequence, partition, KV
+//             head) slot fits on a compute unit of its own, each slot gets a
+//             workgroup and no list is built. A sequence over several
+//             partitions leaves one fp32 partial per partition, and the
+//             item that completes a pair's count (an atomic per pair) merges
+//             them: one kernel, no reduce pass;
 //   balanced  (partition_tokens == 0): the blocks of all (sequence, KV head)
 //             pairs are laid end to end and every wave streams an equal
 //             contiguous range of them, prefetching across pair boundaries.

@@ -262,6 +262,21 @@ def test_fixed_many_partitions(lens):
     compare(gpu_out_f64(out), ref, lens, "bf16")
 
 
+@pytest.mark.parametrize("partition", [256, 64])
+def test_fixed_partials_at_extreme_magnitudes(partition):
+    """The fixed split at outputs far from 1: V scaled by 1e-6 .. 3e4 per
+    KV head, so that heads of one row differ by ten orders of magnitude
+    through the partials and their merge; every row meets the oracle's
+    bar."""
+    lens = [3000, 700, 1, 1800, 0, 257]
+    c = wl.random_case(492, len(lens), 32, 8, 128, "bf16", lens=lens)
+    gains = torch.tensor([1e-6, 1e-3, 1.0, 30.0, 1e3, 3e4, 1.0, 0.5]).view(1, 8, 1, 1)
+    c.v_pool = (c.v_pool.float() * gains).to(c.v_pool.dtype)  # NaN poison stays NaN
+    ref, _, _ = oracle_step(c)
+    out, _, _ = run_step(c, kernel="mfma", partition_tokens=partition)
+    compare(gpu_out_f64(out), ref, np.asarray(lens), "bf16")
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 128), (16, 1, 128), (32, 8, 64)])
 def test_fixed_merge_batch_boundaries(hq, hkv, d):
     """The merge of a row's partitions gives each unit (4 dims of one head)
