@@ -446,8 +446,8 @@ __device__ __forceinline__ void fixed_item(const DecodeArgs& a, int b, int kvh, 
     return;
   }
   // Count this partition once every thread's partials are stored; the item
-  // that completes the count merges the pair's partitions (in a batch as
-  // large as their number, up to 16) and rearms the counter for the next
+  // that completes the count merges the pair's partitions (merge_partitions:
+  // one load round for up to 16 per thread) and rearms the counter for the next
   // call. No workgroup waits for another.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
