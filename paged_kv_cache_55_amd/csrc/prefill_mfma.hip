@@ -423,44 +423,93 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const TileLoa
   // wholly at or before this wave's first position need no masks; they run
   // in a loop of their own, so that it keeps its accumulators in place (one
   // loop that branches between the forms copies them).
+  // The two waves of a SIMD (w and w + 4) run half an iteration apart: the
+  // second half of the waves opens iteration p with the softmax of pair
+  // p - 1 (its scores held across the barrier), then the scores of pair p
+  // and the value product of pair p - 1. Its vector work then meets the
+  // first half's score product instead of its own, and the barrier no
+  // longer lines the two waves up on the same phase. Both orders fold the
+  // pairs in the same order, so the result is the same bit for bit.
   const int clear = active ? (pos_min + 1) / (2 * kTile) : 0;
-  bf16x8_t pf[kColTiles];  // probabilities of the pair whose value product is pending
-  int pending = -1;        // that pair, or -1
-  int p = 0;
-  if (clear > 0) {
-    advance(0);
-    float4_t s0[kColTiles], s1[kColTiles];
-    pair_scores<D, false>(stage(0), stage(1), qb, pos, 0, row, kg, s0, s1);
-    pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
-    for (p = 1; p < clear; ++p) {
+  if (wave < kWaves / 2) {
+    bf16x8_t pf[kColTiles];  // probabilities of the pair whose value product is pending
+    int pending = -1;        // that pair, or -1
+    int p = 0;
+    if (clear > 0) {
+      advance(0);
+      float4_t s0[kColTiles], s1[kColTiles];
+      pair_scores<D, false>(stage(0), stage(1), qb, pos, 0, row, kg, s0, s1);
+      pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+      for (p = 1; p < clear; ++p) {
+        advance(p);
+        pair_scores<D, false>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
+                              s1);
+        pair_values<D, false>(stage(2 * p - 2), stage(2 * p - 1), pf, st, (2 * p - 2) * kTile, vlimit,
+                              row, kg);
+        pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+      }
+      pending = clear - 1;
+    }
+    for (; p < pairs; ++p) {
       advance(p);
-      pair_scores<D, false>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
-                            s1);
-      pair_values<D, false>(stage(2 * p - 2), stage(2 * p - 1), pf, st, (2 * p - 2) * kTile, vlimit,
-                            row, kg);
-      pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+      const bool fold = active && 2 * p < wave_tiles;
+      float4_t s0[kColTiles], s1[kColTiles];
+      if (fold)
+        pair_scores<D, true>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
+                             s1);
+      if (pending >= 0)
+        pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st,
+                             2 * pending * kTile, vlimit, row, kg);
+      pending = -1;
+      if (fold) {
+        pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+        pending = p;
+      }
     }
-    pending = clear - 1;
-  }
-  for (; p < pairs; ++p) {
-    advance(p);
-    const bool fold = active && 2 * p < wave_tiles;
-    float4_t s0[kColTiles], s1[kColTiles];
-    if (fold)
-      pair_scores<D, true>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
-                           s1);
     if (pending >= 0)
-      pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st,
-                           2 * pending * kTile, vlimit, row, kg);
-    pending = -1;
-    if (fold) {
+      pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st, 2 * pending * kTile,
+                           vlimit, row, kg);
+  } else {
+    float4_t s0[kColTiles], s1[kColTiles];
+    int held = -1;  // the pair whose scores are held for its softmax, or -1
+    int p = 0;
+    if (clear > 0) {
+      advance(0);
+      pair_scores<D, false>(stage(0), stage(1), qb, pos, 0, row, kg, s0, s1);
+      for (p = 1; p < clear; ++p) {
+        advance(p);
+        bf16x8_t pf[kColTiles];
+        pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+        pair_scores<D, false>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg,
+                              s0, s1);
+        pair_values<D, false>(stage(2 * p - 2), stage(2 * p - 1), pf, st, (2 * p - 2) * kTile,
+                              vlimit, row, kg);
+      }
+      held = clear - 1;
+    }
+    for (; p < pairs; ++p) {
+      advance(p);
+      const bool fold = active && 2 * p < wave_tiles;
+      if (held >= 0) {
+        bf16x8_t pf[kColTiles];
+        pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
+        pair_values<D, true>(stage(2 * held), stage(2 * held + 1), pf, st, 2 * held * kTile,
+                             vlimit, row, kg);
+      }
+      held = -1;
+      if (fold) {
+        pair_scores<D, true>(stage(2 * p), stage(2 * p + 1), qb, pos, 2 * p * kTile, row, kg, s0,
+                             s1);
+        held = p;
+      }
+    }
+    if (held >= 0) {
+      bf16x8_t pf[kColTiles];
       pair_softmax<D>(s0, s1, st, a.scale_log2, pf);
-      pending = p;
+      pair_values<D, true>(stage(2 * held), stage(2 * held + 1), pf, st, 2 * held * kTile, vlimit,
+                           row, kg);
     }
   }
-  if (pending >= 0)
-    pair_values<D, true>(stage(2 * pending), stage(2 * pending + 1), pf, st, 2 * pending * kTile,
-                         vlimit, row, kg);
   lds_barrier();  // every wave is done with the stages before the next item
 
   if (!active) return;
