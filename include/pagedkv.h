@@ -178,10 +178,12 @@ pa_status pa_decode_contiguous(const void* q, const void* k_cache, const void* v
  * pa_decode_workspace_bytes() exceeds PA_NOALLOC_SCRATCH_BYTES return
  * PA_ERR_UNSUPPORTED before anything runs (the balanced split at the
  * supported head groups needs at most about 17 MiB; the fixed split's
- * partials grow with B * Hq * partitions). With the balanced split a zero
- * fill of its piece counters runs on `stream` before the decode. Every call
- * on one GPU shares that GPU's array: calls that may overlap in time on one
- * GPU (other streams, other threads) race and give undefined results. */
+ * partials grow with B * Hq * partitions). When the dims need a workspace,
+ * a zero fill of its counters (the balanced split's piece counters or the
+ * fixed split's partition counters) runs on `stream` before the decode.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (other streams, other threads) race and give undefined
+ * results. */
 #define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
                             const int32_t* block_tables, const int32_t* seq_lens,
