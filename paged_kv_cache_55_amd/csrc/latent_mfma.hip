@@ -843,6 +843,20 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   auto load_f = [&](int off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rec, off, 0, 0));
   };
+  // the first kMergePieces records' outputs go out with the (m, l, s) loads
+  // below: they do not depend on the merged max
+  u32x4_t x[kMergePieces][8];
+  auto load_batch = [&](int i0) {
+#pragma unroll
+    for (int k = 0; k < kMergePieces; ++k) {
+      if (i0 + k >= n) break;
+      const int sl = slot_of(i0 + k);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rec, record_x(sl, h, 64 * j + d0), 0, 0);
+    }
+  };
+  load_batch(0);
   // merged max and sum of the head, in piece order: every (m, l) in one
   // round trip when the row has at most kFewPieces pieces
   float M = -INFINITY, Lsum = 0.f;
@@ -872,8 +886,8 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j][0] = acc[j][1] = zero4();
   for (int i0 = 0; i0 < n; i0 += kMergePieces) {
+    if (i0 > 0) load_batch(i0);
     float w[kMergePieces];
-    u32x4_t x[kMergePieces][8];
 #pragma unroll
     for (int k = 0; k < kMergePieces; ++k) {
       if (i0 + k >= n) break;
@@ -888,9 +902,6 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
         w[k] = load_f(record_s(sl, h)) *
                (load_f(record_l(sl, h)) * fast_exp2(load_f(record_m(sl, h)) - M) * invL);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        x[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rec, record_x(sl, h, 64 * j + d0), 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < kMergePieces; ++k) {
