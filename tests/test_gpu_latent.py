@@ -77,13 +77,14 @@ def test_latent_long_rows_over_many_workgroups(lens):
 def test_latent_4096_short_rows_sampled():
     """The most rows a call takes: 4,096 rows of 0-90 tokens (a quarter of
     them empty), so the work list's two prefixes fill their LDS share and
-    every workgroup range holds dozens of whole rows; 24 rows are checked,
-    empty ones among them."""
+    every workgroup range holds dozens of whole rows; 404 rows are checked
+    (the float64 oracle takes about 8 ms a row here), empty ones among
+    them."""
     rng = np.random.default_rng(1013)
     lens = rng.integers(0, 91, size=4096)
     lens[rng.choice(4096, 1024, replace=False)] = 0
     c = wl.latent_case(1013, lens.tolist())
-    rows = sorted(set(rng.choice(4096, 20, replace=False).tolist() + [0, 1, 4094, 4095]))
+    rows = sorted(set(rng.choice(4096, 400, replace=False).tolist() + [0, 1, 4094, 4095]))
     worst = check(c, rows)
     print(f"latent 4096 rows worst ratio {worst:.3f}")
 
@@ -106,16 +107,10 @@ def test_latent_tiny_batch():
     check(wl.latent_case(1015, [1, 3, 33]))
 
 
-def test_latent_decode_batch_full_size_sampled():
-    """The measured workload (B = 256, the 70B serving batch's length mix):
-    the kernel runs over the whole batch; the oracle checks 16 rows, the
-    longest and shortest among them."""
-    c = wl.latent_decode_batch()
-    lens = c.seq_lens.numpy()
-    order = np.argsort(lens)
-    rows = sorted(set(order[:4].tolist() + order[-4:].tolist() +
-                      np.random.default_rng(7).choice(len(lens), 8, replace=False).tolist()))
-    worst = check(c, rows)
+def test_latent_decode_batch_full_size():
+    """The measured workload (B = 256, the 70B serving batch's length mix),
+    every row against the oracle."""
+    worst = check(wl.latent_decode_batch())
     print(f"latent full-size worst ratio {worst:.3f}")
 
 
