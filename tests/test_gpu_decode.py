@@ -144,7 +144,7 @@ def test_config3_sharing_is_exact():
 
 
 # --------------------------------------------------------------------------
-# configuration 4: 70B-shaped layer, full size, sampled rows
+# configuration 4: 70B-shaped layer, full size, every row
 # --------------------------------------------------------------------------
 
 @pytest.fixture(scope="module")
