@@ -89,3 +89,40 @@ def test_streaming_kernels_use_no_scratch(tmp_path, src, prefix, count):
     assert len(found) == count, sorted(meta)
     bad = {n: v for n, v in found.items() if v != (0, 0)}
     assert not bad, f"kernels with scratch bytes or VGPR spills: {bad}"
+
+
+# instructions that read M0 without naming it on gfx950 (relative moves, messages, the
+# global data share and ordered counts, interpolation, and every load into LDS)
+M0_READERS = ("s_movrel", "v_movrel", "s_sendmsg", "ds_gws", "ds_append", "ds_consume",
+              "ds_ordered_count", "v_interp", "global_load_lds", "scratch_load_lds")
+
+
+def reads_m0(line):
+    return line.startswith(M0_READERS) or (line.startswith("buffer_") and line.endswith(" lds"))
+
+
+def test_prefill_m0_holds_only_the_tile_load_destination(tmp_path):
+    """The chunked-prefill kernel's direct-to-LDS tile loads set M0 to their
+    LDS destination and leave it there (the compiler keeps M0 reserved and
+    does not honour it as an asm clobber). That is correct only while
+    nothing else in the kernel reads M0: every M0 write is one of those
+    loads' and is followed by its load, and no other instruction that reads
+    M0 appears."""
+    asm = device_asm("prefill_mfma.hip", tmp_path)
+    for prefix in ("_ZN7pagedkv12_GLOBAL__N_119prefill_mfma_kernelILi128",
+                   "_ZN7pagedkv12_GLOBAL__N_119prefill_mfma_kernelILi64"):
+        start = asm.index("\n" + prefix)
+        body = [l.strip() for l in asm[start:asm.index("s_endpgm", start)].splitlines()]
+        code = [l for l in body if l and not l.startswith((";", "."))]
+        writes = [i for i, l in enumerate(code) if re.match(r"s_\w+ m0,", l)]
+        assert writes, "no tile loads found"
+        for i in writes:
+            assert code[i].startswith("s_mov_b32 m0,"), code[i]
+            nxt = [l for l in code[i + 1:i + 4] if not l.startswith("s_nop")]
+            assert nxt and nxt[0].startswith("global_load_lds_dwordx4"), code[i:i + 4]
+        loads = {i + 1 + k for i in writes for k in range(3)}
+        readers = [l for i, l in enumerate(code) if reads_m0(l) and
+                   not (i in loads and l.startswith("global_load_lds_dwordx4"))]
+        assert not readers, readers[:5]
+        other = [l for l in code if re.search(r"\bm0\b", l) and not re.match(r"s_mov_b32 m0,", l)]
+        assert not other, other[:5]
