@@ -29,17 +29,23 @@ __device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
 // assembly so that the compiler does not track these LDS writes: it cannot
 // tell the stages apart and would otherwise make every later LDS read wait
 // for all of them, the prefetch included. Completion is awaited explicitly
-// (tile_barrier). M0 belongs to the compiler, so the sequence restores it.
+// (tile_barrier).
+//
+// Both load forms leave M0 holding `dst`. The compiler keeps M0 reserved
+// and would not honour it as an asm clobber, so they are only for kernels
+// in which nothing else reads M0 (no relative moves, messages or other
+// M0-addressed instructions): the chunked-prefill and latent-decode
+// kernels, whose generated code a test checks for exactly that. Dropping
+// the save and restore measured 1.2% on prefill (its loader waves share
+// the scalar unit with the waves beside them) and 2.1% on latent decode
+// (one wave per SIMD: the refill's scalar instructions sit on its path).
 __device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
+      :
       : "s"(m0), "v"(off), "s"(rsrc)
       : "memory");
 }
@@ -47,14 +53,8 @@ __device__ __forceinline__ void load_to_lds(u32x4_t rsrc, lds_char* dst, int off
 // 16 bytes per lane from the global address `src` (one per lane) into LDS
 // at `dst` + 16 * lane (global_load_lds_dwordx4), default cache policy: the
 // lines stay in L2 for other workgroups that read the same tile. Untracked
-// by the compiler like load_to_lds, and awaited with wait_loads. M0 is
-// left holding `dst`: the compiler treats M0 as reserved and would not
-// honour it as a clobber, so this form is only for kernels in which
-// nothing else reads M0 (no relative moves, messages or other
-// M0-addressed instructions; the chunked-prefill kernel, whose generated
-// code a test checks for exactly that). Dropping the save and restore
-// measured 1.2% on that kernel: its loader waves share the scalar unit
-// with the waves beside them.
+// by the compiler like load_to_lds, awaited with wait_loads, and leaving
+// M0 holding `dst` as load_to_lds does.
 __device__ __forceinline__ void global_load_to_lds(const void* src, lds_char* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   asm volatile(

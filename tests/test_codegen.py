@@ -101,16 +101,21 @@ def reads_m0(line):
     return line.startswith(M0_READERS) or (line.startswith("buffer_") and line.endswith(" lds"))
 
 
-def test_prefill_m0_holds_only_the_tile_load_destination(tmp_path):
-    """The chunked-prefill kernel's direct-to-LDS tile loads set M0 to their
-    LDS destination and leave it there (the compiler keeps M0 reserved and
-    does not honour it as an asm clobber). That is correct only while
-    nothing else in the kernel reads M0: every M0 write is one of those
-    loads' and is followed by its load, and no other instruction that reads
-    M0 appears."""
-    asm = device_asm("prefill_mfma.hip", tmp_path)
-    for prefix in ("_ZN7pagedkv12_GLOBAL__N_119prefill_mfma_kernelILi128",
-                   "_ZN7pagedkv12_GLOBAL__N_119prefill_mfma_kernelILi64"):
+@pytest.mark.parametrize("src,prefixes,load", [
+    ("prefill_mfma.hip", ("_ZN7pagedkv12_GLOBAL__N_119prefill_mfma_kernelILi128",
+                          "_ZN7pagedkv12_GLOBAL__N_119prefill_mfma_kernelILi64"),
+     "global_load_lds_dwordx4"),
+    ("latent_mfma.hip", ("_ZN7pagedkv12_GLOBAL__N_120latent_decode_kernel",), "buffer_load_dwordx4"),
+])
+def test_m0_holds_only_the_tile_load_destination(tmp_path, src, prefixes, load):
+    """The direct-to-LDS tile loads of the chunked-prefill and latent-decode
+    kernels set M0 to their LDS destination and leave it there (the
+    compiler keeps M0 reserved and does not honour it as an asm clobber).
+    That is correct only while nothing else in these kernels reads M0:
+    every M0 write is one of those loads' and is followed by its load, and
+    no other instruction that reads M0 appears."""
+    asm = device_asm(src, tmp_path)
+    for prefix in prefixes:
         start = asm.index("\n" + prefix)
         body = [l.strip() for l in asm[start:asm.index("s_endpgm", start)].splitlines()]
         code = [l for l in body if l and not l.startswith((";", "."))]
@@ -119,10 +124,10 @@ def test_prefill_m0_holds_only_the_tile_load_destination(tmp_path):
         for i in writes:
             assert code[i].startswith("s_mov_b32 m0,"), code[i]
             nxt = [l for l in code[i + 1:i + 4] if not l.startswith("s_nop")]
-            assert nxt and nxt[0].startswith("global_load_lds_dwordx4"), code[i:i + 4]
+            assert nxt and nxt[0].startswith(load) and reads_m0(nxt[0]), code[i:i + 4]
         loads = {i + 1 + k for i in writes for k in range(3)}
         readers = [l for i, l in enumerate(code) if reads_m0(l) and
-                   not (i in loads and l.startswith("global_load_lds_dwordx4"))]
+                   not (i in loads and l.startswith(load))]
         assert not readers, readers[:5]
         other = [l for l in code if re.search(r"\bm0\b", l) and not re.match(r"s_mov_b32 m0,", l)]
         assert not other, other[:5]
