@@ -58,7 +58,6 @@ using lds_stream::load_to_lds;
 using lds_stream::raw_rsrc;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
@@ -416,19 +415,40 @@ __device__ __forceinline__ void fold_tile(const lds_char* tile, const bf16x8_t (
 //
 // Every use of the accumulator here only reads it.
 
+// Lane 16 kg + col holds dims 4 kg .. 4 kg + 3 of its head in every 16-dim
+// tile, as two packed dwords per tile. Given those of tiles 2 p (a) and
+// 2 p + 1 (b), a swap between the wave's halves and one between its 16-lane
+// rows (two dwords each) leave lane kg with dims 32 p + 8 kg .. + 7, in
+// order: one 16-byte store per lane and tile pair where two 8-byte stores
+// would be needed. (Vector memory operations retire in order and stores
+// count with the tile loads, so every store instruction a row finish saves
+// is one fewer that the next tile waits behind.)
+__device__ __forceinline__ uint4 dims8_of_pair(uint2 a, uint2 b) {
+  // row r then holds a of rows r and r + 2 (r < 2), or b of rows r - 2 and r
+  const auto x32 = __builtin_amdgcn_permlane32_swap(a.x, b.x, false, false);
+  const auto y32 = __builtin_amdgcn_permlane32_swap(a.y, b.y, false, false);
+  // row r: a (r < 2) or b (r >= 2) of rows 2 (r & 1) and 2 (r & 1) + 1
+  const auto x16 = __builtin_amdgcn_permlane16_swap(x32[0], x32[1], false, false);
+  const auto y16 = __builtin_amdgcn_permlane16_swap(y32[0], y32[1], false, false);
+  return make_uint4(x16[0], y16[0], x16[1], y16[1]);
+}
+
 // Row b's outputs of this wave's heads: O^T scaled per head, as bf16.
 __device__ __forceinline__ void store_scaled(const LatentArgs& a, const float4_t (&o)[2][kDimTiles],
                                              const float (&mul)[2], int b, int h0, int col,
                                              int kg) {
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    bf16_t* out =
-        (bf16_t*)a.out + ((size_t)b * kHeads + h0 + 16 * ht + col) * kValue + 4 * kg;
+    bf16_t* out = (bf16_t*)a.out + ((size_t)b * kHeads + h0 + 16 * ht + col) * kValue + 8 * kg;
 #pragma unroll
-    for (int n = 0; n < kDimTiles; ++n) {
-      const float4_t v = o[ht][n] * mul[ht];
-      *(uint2*)(out + 16 * n) = make_uint2(pack_bf16x2(bf16_rne(v[0]), bf16_rne(v[1])),
-                                           pack_bf16x2(bf16_rne(v[2]), bf16_rne(v[3])));
+    for (int p = 0; p < kDimTiles / 2; ++p) {
+      const float4_t v = o[ht][2 * p] * mul[ht];
+      const float4_t u = o[ht][2 * p + 1] * mul[ht];
+      *(uint4*)(out + 32 * p) = dims8_of_pair(
+          make_uint2(pack_bf16x2(bf16_rne(v[0]), bf16_rne(v[1])),
+                     pack_bf16x2(bf16_rne(v[2]), bf16_rne(v[3]))),
+          make_uint2(pack_bf16x2(bf16_rne(u[0]), bf16_rne(u[1])),
+                     pack_bf16x2(bf16_rne(u[2]), bf16_rne(u[3]))));
     }
   }
 }
@@ -453,8 +473,8 @@ __device__ __forceinline__ int record_s(int slot, int h) {
   return record_base(slot) + kHeads * kValue * 2 + 2 * kHeads * 4 + h * 4;
 }
 
-__device__ __forceinline__ void store_rec8(__amdgpu_buffer_rsrc_t rec, int off, uint2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rec, off, 0, 0);
+__device__ __forceinline__ void store_rec16(__amdgpu_buffer_rsrc_t rec, int off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rec, off, 0, 0);
 }
 __device__ __forceinline__ void store_rec(__amdgpu_buffer_rsrc_t rec, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rec, off, 0, 0);
@@ -497,6 +517,7 @@ __device__ __forceinline__ float4_t fma4(float4_t x, float w, float4_t acc) {
 __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slot,
                                              const RowState& st, const float (&ltot)[2], int h0,
                                              int col, int kg) {
+  float up[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int h = h0 + 16 * ht + col;
@@ -508,20 +529,28 @@ __device__ __forceinline__ void write_record(__amdgpu_buffer_rsrc_t rec, int slo
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(st.o[ht][n][0]), fabsf(st.o[ht][n][1])),
                                fmaxf(fabsf(st.o[ht][n][2]), fabsf(st.o[ht][n][3]))));
     const float inv = 1.f / ltot[ht];
-    const float up = record_scale(max_over_kg(amax) * inv);
-    const float mul = inv * up;
+    up[ht] = record_scale(max_over_kg(amax) * inv);
+    const float mul = inv * up[ht];
 #pragma unroll
-    for (int n = 0; n < kDimTiles; ++n) {
-      const float4_t v = st.o[ht][n] * mul;
-      store_rec8(rec, record_x(slot, h, 16 * n + 4 * kg),
-                 make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])));
-    }
-    if (kg == 0) {
-      store_rec(rec, record_m(slot, h), st.m[ht]);
-      store_rec(rec, record_l(slot, h), ltot[ht]);
-      store_rec(rec, record_s(slot, h), 1.f / up);
+    for (int p = 0; p < kDimTiles / 2; ++p) {
+      const float4_t v = st.o[ht][2 * p] * mul;
+      const float4_t u = st.o[ht][2 * p + 1] * mul;
+      store_rec16(rec, record_x(slot, h, 32 * p + 8 * kg),
+                  dims8_of_pair(make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])),
+                                make_uint2(pack_f16x2(u[0], u[1]), pack_f16x2(u[2], u[3]))));
     }
   }
+  // m, l and s are the same in a head's four lanes: lane rows 0 and 1 store
+  // m of head tiles 0 and 1 and rows 2 and 3 their l, in one instruction;
+  // rows 0 and 1 then store s
+  // (selects, not indexing: an index that varies by lane would move the
+  // row state out of registers)
+  const bool t1 = kg & 1;
+  const int h = h0 + 16 * (kg & 1) + col;
+  const float m = t1 ? st.m[1] : st.m[0];
+  const float l = t1 ? ltot[1] : ltot[0];
+  store_rec(rec, kg < 2 ? record_m(slot, h) : record_l(slot, h), kg < 2 ? m : l);
+  if (kg < 2) store_rec(rec, record_s(slot, h), 1.f / (t1 ? up[1] : up[0]));
 }
 
 // Writes a finished segment (flat tiles seg0 .. seg1 - 1 of row c.b): a
