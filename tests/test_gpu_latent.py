@@ -74,6 +74,13 @@ def test_latent_long_rows_over_many_workgroups(lens):
     check(wl.latent_case(1003 + len(lens), lens))
 
 
+def test_latent_one_row_over_every_workgroup():
+    """One 65,280-token row: 2,040 tiles, which the smallest range (8 tiles)
+    spreads over 255 workgroups, so the merge folds about 255 records of one
+    row, in piece order, in its many-piece loop."""
+    check(wl.latent_case(1016, [65280]))
+
+
 def test_latent_4096_short_rows_sampled():
     """The most rows a call takes: 4,096 rows of 0-90 tokens (a quarter of
     them empty), so the work list's two prefixes fill their LDS share and
