@@ -78,8 +78,8 @@ def parse():
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--partition", type=int, default=-1,
                     help="split-K partition tokens; 0 = balanced split; -1 = the library's "
-                         "choice from the dims (the default: fixed 512-token partitions for "
-                         "batches of at most 8 rows, the balanced split above)")
+                         "choice from the dims (the default: fixed 256-token partitions for "
+                         "one or two rows, 512 for three to eight, the balanced split above)")
     ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--block-size", type=int, default=16,
@@ -528,8 +528,10 @@ def roofline_kernel(kernel: str, part: int, head_dim: int) -> str:
     if kernel == "mfma" and part == 0:
         return (f"decode_mfma_balanced_kernel<{head_dim}> (one launch per call; "
                 "cut pairs are merged inside it)")
-    name = "decode_mfma_kernel" if kernel == "mfma" else "decode_valu_kernel"
-    return f"{name}<{head_dim}> + decode_reduce_kernel when a row spans several partitions"
+    if kernel == "mfma":
+        return (f"decode_mfma_kernel<{head_dim}> (one launch per call; a row's partitions "
+                "are merged inside it by the last one to finish)")
+    return f"decode_valu_kernel<{head_dim}> + decode_reduce_kernel when a row spans several partitions"
 
 
 def host_threads():
