@@ -78,8 +78,9 @@ def parse():
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--partition", type=int, default=-1,
                     help="split-K partition tokens; 0 = balanced split; -1 = the library's "
-                         "choice from the dims (the default: fixed 256-token partitions for "
-                         "one or two rows, 512 for three to eight, the balanced split above)")
+                         "choice from the dims (the default: fixed partitions of 256 tokens "
+                         "for one row, 192 for two, 320 for three or four, 384 for five to "
+                         "eight; the balanced split above)")
     ap.add_argument("--bucket", type=int, default=256, help="config 5 batch bucket")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--block-size", type=int, default=16,
@@ -270,7 +271,8 @@ def main():
         fixed = kernel != "mfma" or (
             B <= 8 and (case is None or case.block_size == 16)
             and not (args.config in (2, 4) and args.kv_layout == "contiguous"))
-        part = (256 if kernel == "mfma" and B <= 2 else 512) if fixed and args.config not in (6, 7) \
+        mfma_part = 256 if B <= 1 else 192 if B == 2 else 320 if B <= 4 else 384
+        part = (mfma_part if kernel == "mfma" else 512) if fixed and args.config not in (6, 7) \
             else 0
     if part > 0:
         workload += f"_split{part}"

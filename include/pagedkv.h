@@ -82,9 +82,9 @@ typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_k
  * kernel and 16-token blocks, batches of at most 8 rows take fixed
  * partitions (every (row, partition, KV head) its own workgroup, merged in
  * the same kernel by the last partition of a row and KV head to finish):
- * 256 tokens for one or two rows, 512 for three to eight; larger batches
- * take the balanced split. The vector-ALU kernel takes 512-token
- * partitions. */
+ * 256 tokens for one row, 192 for two, 320 for three or four and 384 for
+ * five to eight; larger batches take the balanced split. The vector-ALU
+ * kernel takes 512-token partitions. */
 #define PA_PARTITION_AUTO (-1)
 
 /* Host-side dimensions; all fields are fixed for a given captured shape. */

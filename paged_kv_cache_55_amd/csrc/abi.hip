@@ -61,16 +61,22 @@ constexpr int kMaxPrefillGrid = 1024;
 // and one wave merges each long row's many pieces, while the fixed split
 // gives every (row, partition, KV head) its own workgroup: on the 32-layer
 // 8B step it measured 20 us per layer at buckets 1-8 against 25-31 us
-// balanced, and 12% slower at 32 rows. One compute unit streams a
-// partition at about 30 GB/s, so a batch of one or two rows spreads over
-// more of them with 256-token partitions (bucket 1: 16.2 against 17.2 us
-// per layer; bucket 2: 12.4 against 15.6); from three rows on, 512-token
-// partitions keep the merge, which one workgroup reads at that same rate,
-// shorter (bucket 4: 17.9 against 19.1 us).
+// balanced, and 12% slower at 32 rows.
 constexpr int kAutoFixedRows = 8;
-constexpr int kAutoFewRows = 2;
-constexpr int kAutoPartitionFew = 256;
-constexpr int kAutoPartition = 512;
+// The fixed split's partition length for B rows. Shorter partitions spread
+// a row over more compute units (one streams a partition at about 30 GB/s);
+// longer ones leave fewer partials for the merge, which one workgroup reads
+// at that same rate. Measured on the 32-layer 8B step (bucket: real rows,
+// us per layer for partitions of 192 / 256 / 320 / 384 / 512 tokens;
+// two boxes agreed within 1%): bucket 1: 18.8 / 14.6 / 14.4 / 15.2 / 15.7;
+// bucket 2: 10.8 / 11.9 / 12.5 / 13.6 / 13.9; bucket 4 (3 rows): 19.0 /
+// 19.0 / 16.4 / 17.0 / 17.7; bucket 8 (5 rows): 18.0 / 17.5 / 16.6 / 16.3 /
+// 17.6. A single row keeps 256 tokens, whose slots (rows x partitions x KV
+// heads) fit the compute units at 8,192 tokens and 8 KV heads.
+constexpr int auto_partition(int rows) {
+  return rows <= 1 ? 256 : rows == 2 ? 192 : rows <= 4 ? 320 : 384;
+}
+constexpr int kAutoPartitionValu = 512;  // the vector-ALU kernel, any batch
 
 struct Plan {
   int kernel;       // PA_KERNEL_VALU or PA_KERNEL_MFMA
@@ -104,8 +110,8 @@ pa_status plan_decode(const pa_dims* d, Plan* p, bool balanced_only = false) {
                        (!balanced_only && d->block_size == kBlockTokens &&
                         d->num_seqs <= kAutoFixedRows);
     p->partition = !fixed ? 0
-                   : p->kernel == PA_KERNEL_MFMA && d->num_seqs <= kAutoFewRows ? kAutoPartitionFew
-                                                                                 : kAutoPartition;
+                   : p->kernel == PA_KERNEL_MFMA ? auto_partition(d->num_seqs)
+                                                 : kAutoPartitionValu;
   }
   if (p->partition < 0 || p->partition % kBlockTokens != 0) return PA_ERR_INVALID_ARG;
   const int G = d->num_q_heads / d->num_kv_heads;

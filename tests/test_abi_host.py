@@ -345,19 +345,24 @@ def test_contiguous_takes_the_balanced_split_only(lib):
                                     ctypes.c_size_t(1 << 30), None) == pk.PA_ERR_INVALID_ARG
 
 
+# the fixed partition PA_PARTITION_AUTO documents for 1 .. 8 rows
+AUTO_PARTITION = {1: 256, 2: 192, 3: 320, 4: 320, 5: 384, 6: 384, 7: 384, 8: 384}
+
+
 def test_auto_partition_follows_the_dims(lib):
-    """PA_PARTITION_AUTO: batches of one or two rows take 256-token fixed
-    partitions, of three to eight rows 512-token ones, larger batches (and
-    any block size but 16) the balanced split; the vector-ALU kernel takes
-    512-token partitions."""
+    """PA_PARTITION_AUTO: fixed partitions of 256 tokens for one row, 192
+    for two, 320 for three or four and 384 for five to eight; larger batches
+    (and any block size but 16) the balanced split; the vector-ALU kernel
+    takes 512-token partitions."""
     ws = pk.pa_decode_workspace_bytes
-    for B in (1, 2, 3, 8, 9, 256):
+    for B in (1, 2, 3, 4, 5, 8, 9, 256):
         auto = ws(dims(num_seqs=B, partition_tokens=pk.PARTITION_AUTO))
-        expect = ws(dims(num_seqs=B, partition_tokens=256 if B <= 2 else 512 if B <= 8 else 0))
+        expect = ws(dims(num_seqs=B, partition_tokens=AUTO_PARTITION.get(B, 0)))
         assert auto == expect, B
-    for B in (1, 2):  # the workspace sizes tell 256-token partitions from 512-token ones
-        assert ws(dims(num_seqs=B, partition_tokens=256)) != \
-            ws(dims(num_seqs=B, partition_tokens=512))
+        if B <= 8:  # the workspace size tells the chosen partition from its neighbours
+            for other in (192, 256, 320, 384, 512):
+                if other != AUTO_PARTITION[B]:
+                    assert ws(dims(num_seqs=B, partition_tokens=other)) != auto, (B, other)
     assert ws(dims(num_seqs=4, block_size=32, partition_tokens=pk.PARTITION_AUTO)) == \
         ws(dims(num_seqs=4, block_size=32, partition_tokens=0))
     for B in (1, 64):

@@ -138,7 +138,8 @@ def test_config3_sharing_is_exact():
     k2 = torch.cat([k, extra_k]).contiguous()
     v2 = torch.cat([v, extra_v]).contiguous()
     d = c.to("cuda")
-    out_private = pk.pa_decode(d.q, k2, v2, tables.cuda(), d.seq_lens, c.scale)
+    out_private = pk.pa_decode(d.q, k2, v2, tables.cuda(), d.seq_lens, c.scale,
+                               partition_tokens=c.partition_tokens)
     torch.cuda.synchronize()
     assert torch.equal(out_shared.view(torch.int16), out_private.view(torch.int16))
 
@@ -383,15 +384,17 @@ def test_abi_error_reaches_python():
         pk.pa_decode(c.q.float(), c.k_pool, c.v_pool, c.block_tables, c.seq_lens, c.scale)
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 8, 9, 40])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 9, 40])
 def test_auto_split_is_the_documented_choice(B):
     """PA_PARTITION_AUTO gives bit for bit the split it documents: fixed
-    256-token partitions for one or two rows, 512-token ones up to 8 rows,
-    the balanced split above; and meets the oracle's bar."""
+    partitions of 256 tokens for one row, 192 for two, 320 for three or
+    four, 384 for five to eight, the balanced split above; and meets the
+    oracle's bar."""
     c = wl.random_case(470 + B, B, 32, 8, 128, "bf16", max_len=3000)
     ref, _, _ = oracle_step(c)
     auto, _, _ = run_step(c, kernel="mfma", partition_tokens=pk.PARTITION_AUTO)
     chosen, _, _ = run_step(c, kernel="mfma",
-                            partition_tokens=256 if B <= 2 else 512 if B <= 8 else 0)
+                            partition_tokens={1: 256, 2: 192, 3: 320, 4: 320}.get(
+                                B, 384 if B <= 8 else 0))
     assert torch.equal(auto.view(torch.int16), chosen.view(torch.int16))
     compare(gpu_out_f64(auto), ref, c.seq_lens.numpy(), "bf16")
